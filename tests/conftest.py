@@ -1,0 +1,16 @@
+"""pytest configuration: the `gpu` marker and import paths.
+
+Tests marked `gpu` need an MI355X (gfx950) and the built HIP library; the
+rest run on any CPU.
+"""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+for p in (ROOT, os.path.join(ROOT, "tests")):
+    if p not in sys.path:
+        sys.path.insert(0, p)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")

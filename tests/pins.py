@@ -1,0 +1,535 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with an independent fact:
+
+* library routines: torch / numpy dtype casts, ``torch.nn.functional.rms_norm``,
+  ``silu`` and ``gelu(approximate="tanh")``, complex multiplication, eager add;
+* closed forms: a power-of-two constant row normalises to exactly +-R(w + delta),
+  a zero row to zero; a (cos, sin) = (0, 1) cache swaps each pair with one sign
+  flip, (-1, 0) negates it, position 0 is the identity;
+* invariants: scale invariance at eps = 0, rotation preserves pair norms and
+  composes additively in the angle, the fused ops equal the composition of the
+  separately written row primitives;
+* brute force against exact (mpmath) arithmetic on tiny heads and over every
+  bf16 input of the activations.
+
+The same functions run against deliberately mutated builds of the oracle
+(tests/test_oracle_strength.py) to show that each plausible mistake is caught.
+"""
+import math
+
+import mpmath
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import workloads as W
+
+F32, F16, BF16 = W.F32, W.F16, W.BF16
+U32 = 2.0 ** -24  # unit roundoff of binary32
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def _ord16(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def ulp16(a_bits, b_bits):
+    """ulp distance of two bf16 / fp16 arrays (sign-magnitude order, +0 == -0)."""
+    return np.abs(_ord16(a_bits) - _ord16(b_bits))
+
+
+def same_bits(a, b, dtype):
+    """Bitwise equality, treating +0 / -0 as equal and NaN == NaN."""
+    if dtype == F32:
+        a = np.asarray(a, np.float32)
+        b = np.asarray(b, np.float32)
+        return np.all((a == b) | (np.isnan(a) & np.isnan(b)))
+    return np.all(ulp16(a, b) == 0)
+
+
+def f32(bits, dtype):
+    return W.bits_to_f32(bits, dtype)
+
+
+def round_exact(v, dtype):
+    """Round an exact real (float64 or mpmath value) to `dtype`, nearest-even,
+    from its float64 value.  Returns (rounded float64 value, ambiguous flag):
+    ambiguous when v lies within 1e-6 relative of a midpoint, where an fp32
+    computation may legitimately land on either side."""
+    v = float(v)
+    if v == 0.0 or not math.isfinite(v):
+        return v, False
+    p = {BF16: 8, F16: 11, F32: 24}[dtype]
+    m, e = math.frexp(abs(v))                    # |v| = m 2^e, m in [0.5, 1)
+    if dtype == F16:
+        e = max(e, -13)                          # subnormal grid 2^-24
+    elif dtype == BF16:
+        e = max(e, -125)
+    q = math.ldexp(1.0, e - p)
+    lo = math.floor(abs(v) / q) * q
+    hi = lo + q
+    mid = lo + q / 2
+    amb = abs(abs(v) - mid) <= 1e-6 * abs(v)
+    if abs(v) < mid:
+        r = lo
+    elif abs(v) > mid:
+        r = hi
+    else:
+        r = lo if (lo / q) % 2 == 0 else hi
+    return math.copysign(r, v), amb
+
+
+# ---------------------------------------------------------------------------
+# converters (IEEE 754 / OCP OFP8 vs torch and numpy casts)
+# ---------------------------------------------------------------------------
+
+def _fp32_sweep(n=400_000, seed=7):
+    g = np.random.default_rng(seed)
+    rand = g.integers(0, 2 ** 32, size=n, dtype=np.uint64).astype(np.uint32)
+    hi = np.arange(65536, dtype=np.uint32) << 16
+    near_mid = np.concatenate([hi | 0x7FFF, hi | 0x8000, hi | 0x8001, hi, hi | 0xFFFF])
+    return np.concatenate([rand, near_mid]).view(np.float32)
+
+
+def pin_bf16_converter(orc):
+    bits = np.arange(65536, dtype=np.uint16)
+    dec = orc.decode(bits, BF16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert same_bits(dec, ref, F32), "bf16 decode differs from torch"
+    vals = _fp32_sweep()
+    enc = orc.encode(vals, BF16)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(vals)
+    assert np.array_equal(enc[~nan], ref[~nan]), "bf16 RNE encode differs from torch"
+    assert np.all((enc[nan] & 0x7F80) == 0x7F80) and np.all(enc[nan] & 0x7F), "NaN lost"
+
+
+def pin_f16_converter(orc):
+    bits = np.arange(65536, dtype=np.uint16)
+    dec = orc.decode(bits, F16)
+    ref = bits.view(np.float16).astype(np.float32)
+    assert same_bits(dec, ref, F32), "fp16 decode differs from numpy"
+    # every fp16 value, its midpoints to the next value and one fp32 ulp around
+    finite = bits[(bits & 0x7C00) != 0x7C00]
+    v = finite.view(np.float16).astype(np.float64)
+    with np.errstate(over="ignore"):
+        nxt = np.nextafter(finite.view(np.float16), np.float16(np.inf)).astype(np.float64)
+    mid = ((v + nxt) / 2).astype(np.float32)
+    extra = np.concatenate([mid, np.nextafter(mid, np.float32(np.inf)),
+                            np.nextafter(mid, np.float32(-np.inf)),
+                            np.float32([65504, 65519.99, 65520, 1e5, 2 ** -25, 2 ** -26,
+                                        3 * 2 ** -26, 2 ** -24 * 1.5])])
+    vals = np.concatenate([_fp32_sweep(seed=8), extra]).astype(np.float32)
+    enc = orc.encode(vals, F16)
+    with np.errstate(over="ignore", invalid="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    nan = np.isnan(vals)
+    assert np.array_equal(enc[~nan], ref[~nan]), "fp16 RNE encode differs from numpy"
+
+
+def e4m3fn_closed_form(code):
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    if e == 0:
+        return s * m / 8.0 * 2.0 ** -6
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def pin_e4m3fn_converter(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    dec = orc.decode_e4m3fn(codes)
+    closed = np.array([e4m3fn_closed_form(int(c)) for c in codes], dtype=np.float32)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    assert same_bits(dec, closed, F32) and same_bits(dec, lib, F32), "e4m3fn decode"
+    # every code value, midpoints between neighbours and one fp32 ulp around them
+    fin = np.sort(np.unique(closed[np.isfinite(closed)].astype(np.float64)))
+    mids = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)
+    g = np.random.default_rng(3)
+    rnd = (g.standard_normal(200_000) * np.exp2(g.integers(-12, 9, 200_000))).astype(np.float32)
+    vals = np.concatenate([fin.astype(np.float32), mids, np.nextafter(mids, np.float32(np.inf)),
+                           np.nextafter(mids, np.float32(-np.inf)), rnd])
+    inr = np.abs(vals) <= 464.0
+    enc = orc.encode_e4m3fn(vals[inr])
+    ref = torch.from_numpy(vals[inr]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # torch keeps the sign of zero; e4m3fn has both zeros, so compare bitwise
+    assert np.array_equal(enc, ref), "e4m3fn RNE encode differs from torch"
+    sat = orc.encode_e4m3fn(np.float32([448.5, 470, 1e6, np.inf, -500, -np.inf]))
+    assert list(sat) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE], "e4m3fn saturation"
+    nan = orc.encode_e4m3fn(np.float32([np.nan]))
+    assert (nan[0] & 0x7F) == 0x7F, "e4m3fn NaN"
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+
+def pin_rmsnorm_vs_torch(orc):
+    """fp32 rows against torch.nn.functional.rms_norm in float64.  Bound from
+    the recursive-summation error of sum(x^2) ((D-1) u relative), halved by
+    the square root, plus the divide, the sqrt and two products."""
+    g = np.random.default_rng(11)
+    for D in (7, 64, 128, 256, 2560):
+        for eps in (1e-6, 0.5):
+            for delta in (0, 1):
+                x = g.standard_normal((16, D)).astype(np.float32) * 1.7
+                w = (g.standard_normal(D) * 0.05 + (1 - delta)).astype(np.float32)
+                y = orc.rmsnorm_rows(x, w, eps, delta, F32).astype(np.float64)
+                ref = F.rms_norm(torch.from_numpy(x.astype(np.float64)), (D,),
+                                 weight=torch.from_numpy(w.astype(np.float64) + delta),
+                                 eps=float(np.float32(eps))).numpy()
+                tol = ((D + 8) / 2.0) * U32 * np.abs(ref) + 1e-30
+                assert np.all(np.abs(y - ref) <= tol), f"rmsnorm vs torch D={D} eps={eps}"
+
+
+def pin_rmsnorm_closed_forms(orc):
+    g = np.random.default_rng(12)
+    for dtype in (BF16, F16, F32):
+        for D in (4, 64, 256):
+            for delta in (0, 1):
+                w = W.to_bits(g.standard_normal(D) * 0.05 + (1 - delta), dtype)
+                wd = f32(w, dtype).astype(np.float64) + delta
+                # power-of-two constant rows: x * inv is exactly +-1 at eps = 0
+                for c in (1.0, -4.0, 0.25, 64.0):
+                    x = W.to_bits(np.full((1, D), c), dtype)
+                    y = orc.rmsnorm_rows(x, w, 0.0, delta, dtype)
+                    ref = W.to_bits(np.sign(c) * wd, dtype)
+                    assert same_bits(y[0], ref, dtype), f"constant row c={c}"
+                # zero row with eps > 0: exactly zero
+                z = W.to_bits(np.zeros((1, D)), dtype)
+                y = orc.rmsnorm_rows(z, w, 1e-6, delta, dtype)
+                assert np.all(f32(y, dtype) == 0.0), "zero row"
+                # scale invariance at eps = 0: x * 2^k gives the same bits
+                x = W.to_bits(g.standard_normal((4, D)), dtype)
+                y0 = orc.rmsnorm_rows(x, w, 0.0, delta, dtype)
+                for k in (-3, 2):
+                    xs = W.to_bits(f32(x, dtype).astype(np.float64) * 2.0 ** k, dtype)
+                    # only where the scaled row is itself exact (no fp16 subnormals)
+                    if not np.array_equal(f32(xs, dtype), f32(x, dtype) * np.float32(2.0 ** k)):
+                        continue
+                    yk = orc.rmsnorm_rows(xs, w, 0.0, delta, dtype)
+                    assert same_bits(y0, yk, dtype), "scale invariance"
+
+
+_GRID = [0.5, -1.0, 1.5, -3.0, 0.1015625, -2.75, 7.0, 0.0, -0.03125, 12.5]
+
+
+def pin_rmsnorm_bruteforce(orc):
+    """All rows of D = 2 and D = 4 drawn from a small bf16 grid, against the
+    exact value (mpmath, 40 digits) rounded once to bf16."""
+    mpmath.mp.dps = 40
+    eps = float(np.float32(1e-6))
+    for D, delta in ((2, 0), (4, 1), (4, 0)):
+        rows = np.array(np.meshgrid(*([_GRID] * D), indexing="ij")).reshape(D, -1).T
+        w = np.array([0.75, -0.5, 1.25, 0.0625][:D]) - (0.0 if delta == 0 else 1.0)
+        xb = W.to_bits(rows, BF16)
+        wb = W.to_bits(w, BF16)
+        y = f32(orc.rmsnorm_rows(xb, wb, eps, delta, BF16), BF16)
+        xv = f32(xb, BF16).astype(np.float64)
+        wv = f32(wb, BF16).astype(np.float64) + delta
+        amb = bad = 0
+        for r in range(rows.shape[0]):
+            ms = mpmath.fsum(mpmath.mpf(v) ** 2 for v in xv[r]) / D
+            inv = 1 / mpmath.sqrt(ms + mpmath.mpf(eps))
+            for i in range(D):
+                exact, a = round_exact(mpmath.mpf(xv[r, i]) * inv * mpmath.mpf(wv[i]), BF16)
+                if y[r, i] != exact:
+                    if a:
+                        amb += 1
+                    else:
+                        bad += 1
+        assert bad == 0, f"brute force D={D}: {bad} wrong roundings"
+        assert amb <= rows.size // 200, f"brute force D={D}: {amb} midpoint cases"
+
+
+# ---------------------------------------------------------------------------
+# rotary embedding
+# ---------------------------------------------------------------------------
+
+def _complex_pairs(x, rot, layout):
+    if layout == W.ROTATE_HALF:
+        a, b = np.arange(rot // 2), np.arange(rot // 2) + rot // 2
+    else:
+        a, b = np.arange(0, rot, 2), np.arange(1, rot, 2)
+    return a, b
+
+
+def pin_rope_complex(orc):
+    """fp32 rotation against complex multiplication by cos + i sin (numpy
+    complex128, with the cache's own fp32 values as the exact angle): bound
+    3u |z| per component (two rounded products and one rounded sum)."""
+    g = np.random.default_rng(21)
+    for layout in (W.ROTATE_HALF, W.INTERLEAVED):
+        for D, rot in ((128, 128), (256, 64), (64, 32), (8, 4)):
+            cs = W.rope_cache(512, rot, 1e4)
+            T, H = 9, 3
+            x = g.standard_normal((T, H, D)).astype(np.float32)
+            pos = g.integers(0, 512, T).astype(np.int64)
+            y = orc.rope(x, cs, pos, rot, layout, F32)
+            a, b = _complex_pairs(x, rot, layout)
+            c = cs[pos][:, None, : rot // 2].astype(np.float64)
+            s = cs[pos][:, None, rot // 2:].astype(np.float64)
+            z = x[..., a].astype(np.float64) + 1j * x[..., b].astype(np.float64)
+            o = z * (c + 1j * s)
+            tol = 3 * U32 * np.abs(z) + 1e-30
+            assert np.all(np.abs(y[..., a] - o.real) <= tol), "rope real part"
+            assert np.all(np.abs(y[..., b] - o.imag) <= tol), "rope imaginary part"
+            assert np.array_equal(y[..., rot:], x[..., rot:]), "channels past rot changed"
+
+
+def pin_rope_closed_forms(orc):
+    g = np.random.default_rng(22)
+    for dtype in (BF16, F16, F32):
+        for layout in (W.ROTATE_HALF, W.INTERLEAVED):
+            D, rot = 32, 16
+            x = W.to_bits(g.standard_normal((5, 2, D)), dtype)
+            a, b = _complex_pairs(None, rot, layout)
+            # quarter turn: (c, s) = (0, 1) maps (a, b) -> (-b, a) exactly
+            cs = np.zeros((3, rot), np.float32)
+            cs[0, :rot // 2] = 1.0                      # row 0: identity
+            cs[1, rot // 2:] = 1.0                      # row 1: quarter turn
+            cs[2, :rot // 2] = -1.0                     # row 2: half turn
+            xv = f32(x, dtype)
+            for p, want_a, want_b in ((0, xv[..., a], xv[..., b]),
+                                      (1, -xv[..., b], xv[..., a]),
+                                      (2, -xv[..., a], -xv[..., b])):
+                y = f32(orc.rope(x, cs, np.full(5, p), rot, layout, dtype), dtype)
+                assert np.array_equal(y[..., a], want_a) and np.array_equal(y[..., b], want_b), \
+                    f"rope closed form p={p} layout={layout}"
+                assert np.array_equal(y[..., rot:], xv[..., rot:]), "tail channels"
+            # outside the cache: untouched (p = max_pos, p < 0)
+            y = orc.rope(x, cs, np.array([3, -1, 1 << 40, 3, -7]), rot, layout, dtype)
+            assert same_bits(y, x, dtype), "out-of-range position must leave the token untouched"
+
+
+def pin_rope_invariants(orc):
+    """Pair norm preserved and angles additive (fp32 I/O, real cache)."""
+    g = np.random.default_rng(23)
+    D, rot = 64, 64
+    cs = W.rope_cache(4096, rot, 1e6)
+    x = g.standard_normal((6, 4, D)).astype(np.float32)
+    for layout in (W.ROTATE_HALF, W.INTERLEAVED):
+        a, b = _complex_pairs(None, rot, layout)
+        p1 = g.integers(0, 2048, 6)
+        p2 = g.integers(0, 2048, 6)
+        y1 = orc.rope(x, cs, p1, rot, layout, F32)
+        n0 = x[..., a].astype(np.float64) ** 2 + x[..., b].astype(np.float64) ** 2
+        n1 = y1[..., a].astype(np.float64) ** 2 + y1[..., b].astype(np.float64) ** 2
+        assert np.all(np.abs(n1 - n0) <= 12 * U32 * n0 + 1e-30), "pair norm"
+        y12 = orc.rope(y1, cs, p2, rot, layout, F32)
+        y3 = orc.rope(x, cs, p1 + p2, rot, layout, F32)
+        scale = np.sqrt(n0)
+        # the cache rows themselves carry fp32 rounding: allow a few u |z|
+        assert np.all(np.abs(y12[..., a] - y3[..., a]) <= 16 * U32 * scale + 1e-30) and \
+            np.all(np.abs(y12[..., b] - y3[..., b]) <= 16 * U32 * scale + 1e-30), "additivity"
+
+
+# ---------------------------------------------------------------------------
+# fused QK-norm + RoPE prologue
+# ---------------------------------------------------------------------------
+
+def pin_prologue_composition(orc):
+    """The fused prologue equals rmsnorm_rows (w_q on query heads, w_k on key
+    heads) -> round -> rope, bit for bit, for every dtype, both layouts,
+    partial rotation and positions inside and outside the cache."""
+    g = np.random.default_rng(31)
+    for dtype in (BF16, F16, F32):
+        for layout in (W.ROTATE_HALF, W.INTERLEAVED):
+            for (Q, K, D, rot, delta) in ((4, 2, 64, 64, 0), (3, 1, 256, 64, 1),
+                                          (2, 2, 128, 32, 1), (1, 0, 16, 0, 0)):
+                T = 5
+                q = W.to_bits(g.standard_normal((T, Q, D)) * 2, dtype)
+                k = W.to_bits(g.standard_normal((T, K, D)) * 2, dtype)
+                wq = W.to_bits(g.standard_normal(D) * 0.05 + (1 - delta), dtype)
+                wk = W.to_bits(g.standard_normal(D) * 0.05 + (1 - delta), dtype)
+                cs = W.rope_cache(64, rot, 1e7)
+                pos = np.array([0, 63, 64, -1, 17])[:T]
+                qo, ko = orc.qknorm_rope(q, k, wq, wk, cs, pos, rot, 1e-6, delta, layout, dtype)
+                qn = orc.rmsnorm_rows(q, wq, 1e-6, delta, dtype)
+                kn = orc.rmsnorm_rows(k, wk, 1e-6, delta, dtype)
+                qr = orc.rope(qn, cs, pos, rot, layout, dtype)
+                kr = orc.rope(kn, cs, pos, rot, layout, dtype) if K else kn
+                assert same_bits(qo, qr, dtype), f"prologue q composition {dtype} {layout}"
+                assert same_bits(ko, kr, dtype), f"prologue k composition {dtype} {layout}"
+
+
+def pin_prologue_constant_head(orc):
+    """A power-of-two constant head at position 0 comes out as +-R(w + delta)
+    exactly, whatever the rotated width (the mean is over head_dim)."""
+    for dtype in (BF16, F32):
+        for (D, rot) in ((256, 64), (128, 128), (64, 16)):
+            for delta in (0, 1):
+                w = W.to_bits(np.linspace(-0.1, 0.1, D) + (1 - delta), dtype)
+                q = W.to_bits(np.full((1, 2, D), -2.0), dtype)
+                k = W.to_bits(np.full((1, 1, D), 0.5), dtype)
+                cs = W.rope_cache(8, rot, 1e6)
+                qo, ko = orc.qknorm_rope(q, k, w, w, cs, np.array([0]), rot, 0.0, delta,
+                                         W.ROTATE_HALF, dtype)
+                wd = W.to_bits(f32(w, dtype).astype(np.float64) + delta, dtype)
+                assert same_bits(qo[0, 0], W.to_bits(-f32(wd, dtype), dtype), dtype), "q head"
+                assert same_bits(ko[0, 0], wd, dtype), "k head"
+
+
+# ---------------------------------------------------------------------------
+# fused residual-add RMSNorm and its FP8 variant
+# ---------------------------------------------------------------------------
+
+def pin_residual_add(orc):
+    """Residual stream equals torch's eager add (bf16 / fp16) or numpy's
+    (fp32) bit for bit, and the normalised output equals rmsnorm_rows of the
+    rounded sum."""
+    g = np.random.default_rng(41)
+    for dtype in (BF16, F16, F32):
+        for H in (37, 1024):
+            x = W.to_bits(g.standard_normal((6, H)), dtype)
+            r = W.to_bits(g.standard_normal((6, H)) * 3, dtype)
+            w = W.to_bits(g.standard_normal(H) * 0.05 + 1, dtype)
+            xo, ro = orc.fused_add_rmsnorm(x, r, w, 1e-6, 0, dtype)
+            if dtype == F32:
+                eager = (x + r).astype(np.float32)
+            else:
+                tx, tr = W.to_torch(x, dtype), W.to_torch(r, dtype)
+                eager = W.from_torch(tx + tr, dtype)
+            assert same_bits(ro, eager, dtype), f"residual != eager add ({dtype})"
+            assert same_bits(xo, orc.rmsnorm_rows(ro, w, 1e-6, 0, dtype), dtype), \
+                "normalised output != rmsnorm(rounded sum)"
+            xo2, ro2 = orc.fused_add_rmsnorm(x, None, w, 1e-6, 1, dtype)
+            assert ro2 is None and same_bits(xo2, orc.rmsnorm_rows(x, w, 1e-6, 1, dtype), dtype)
+
+
+def pin_norm_fp8(orc):
+    """FP8 variant == quantize_fp8 of the fp32 output of the plain op (fp32
+    I/O: that output is the unrounded value), and the calibration amax is the
+    largest magnitude of that same output."""
+    g = np.random.default_rng(42)
+    H = 2048
+    x = g.standard_normal((8, H)).astype(np.float32)
+    r = g.standard_normal((8, H)).astype(np.float32)
+    w = (g.standard_normal(H) * 0.05 + 1).astype(np.float32)
+    for delta in (0, 1):
+        xo, ro = orc.fused_add_rmsnorm(x, r, w, 1e-6, delta, F32)
+        amax = orc.fused_add_rmsnorm_amax(x, r, w, 1e-6, delta, F32)
+        assert amax == float(np.max(np.abs(xo))), "norm amax"
+        for inv_scale in (448.0 / amax, 200.0 / amax, 1000.0 / amax):
+            y, ro8 = orc.fused_add_rmsnorm_fp8(x, r, w, np.float32(inv_scale), 1e-6, delta, F32)
+            assert np.array_equal(ro8, ro)
+            assert np.array_equal(y, orc.quantize_fp8(xo, np.float32(inv_scale))), "norm fp8"
+
+
+def pin_quantize_vs_torch(orc):
+    g = np.random.default_rng(43)
+    x = (g.standard_normal(100_000) * 3).astype(np.float32)
+    for inv_scale in (1.0, 37.5, 0.01):
+        y = orc.quantize_fp8(x, np.float32(inv_scale))
+        v = (x * np.float32(inv_scale)).astype(np.float32)
+        inr = np.abs(v) <= 464
+        ref = torch.from_numpy(v[inr]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(y[inr], ref), "quantize vs torch"
+        assert np.all((y[~inr] & 0x7F) == 0x7E), "quantize saturation"
+
+
+# ---------------------------------------------------------------------------
+# gated activations
+# ---------------------------------------------------------------------------
+
+def pin_act_vs_torch(orc):
+    """fp32 against torch silu / gelu(tanh) in float64 on g in [-4, 6], where
+    torch's float64 tanh form is accurate.  Bound: a few u plus 2|z| times the
+    rounding of z, as e^{-2z} magnifies it."""
+    g = np.random.default_rng(51)
+    d = 4096
+    gv = g.uniform(-4, 6, (3, d)).astype(np.float32)
+    uv = g.standard_normal((3, d)).astype(np.float32)
+    gu = np.concatenate([gv, uv], axis=1)
+    gt, ut = torch.from_numpy(gv.astype(np.float64)), torch.from_numpy(uv.astype(np.float64))
+    for act, ref in ((W.SILU, F.silu(gt) * ut),
+                     (W.GELU_TANH, F.gelu(gt, approximate="tanh") * ut)):
+        out = orc.gated_act(gu, act, F32).astype(np.float64)
+        ref = ref.numpy()
+        z = np.abs(gv.astype(np.float64)) * (1 + 0.045 * gv.astype(np.float64) ** 2)
+        tol = (16 + 8 * z) * U32 * np.abs(ref) + 1e-35
+        assert np.all(np.abs(out - ref) <= tol), f"act {act} vs torch"
+
+
+def pin_act_exhaustive_bf16(orc):
+    """Every finite bf16 gate value with up = 1, against the exact activation
+    (mpmath, 60 digits: 1 + tanh(z) needs ~40 of them before bf16 underflows)
+    rounded once to bf16."""
+    mpmath.mp.dps = 60
+    bits = np.arange(65536, dtype=np.uint16)
+    gv = f32(bits, BF16)
+    keep = np.isfinite(gv)
+    bits, gv = bits[keep], gv[keep].astype(np.float64)
+    one = W.to_bits(np.ones(bits.size), BF16)
+    gu = np.concatenate([bits, one])[None, :]
+    c = mpmath.sqrt(2 / mpmath.pi)
+    for act in (W.SILU, W.GELU_TANH):
+        out = f32(orc.gated_act(gu, act, BF16)[0], BF16)
+        bad = amb = 0
+        for i in range(bits.size):
+            x = mpmath.mpf(gv[i])
+            if act == W.SILU:
+                ex = x / (1 + mpmath.exp(-x))
+            else:
+                ex = x / 2 * (1 + mpmath.tanh(c * (x + mpmath.mpf("0.044715") * x ** 3)))
+            r, a = round_exact(ex, BF16)
+            if out[i] != r:
+                if a:
+                    amb += 1
+                else:
+                    bad += 1
+        assert bad == 0, f"act {act}: {bad} bf16 inputs round wrongly"
+        assert amb <= 64, f"act {act}: {amb} midpoint cases"
+
+
+def pin_act_identities(orc):
+    """act(g) - act(-g) = g for SiLU and GELU-tanh; act(0) = 0; for large g
+    the gate is exactly g, so out = R(g u)."""
+    g = np.random.default_rng(52)
+    d = 2048
+    gv = g.uniform(-5, 5, (1, d)).astype(np.float32)
+    one = np.ones((1, d), np.float32)
+    for act in (W.SILU, W.GELU_TANH):
+        pos = orc.gated_act(np.concatenate([gv, one], 1), act, F32).astype(np.float64)
+        neg = orc.gated_act(np.concatenate([-gv, one], 1), act, F32).astype(np.float64)
+        assert np.all(np.abs((pos - neg) - gv) <= 8 * U32 * np.abs(gv) + 1e-30), "odd part"
+        zero = orc.gated_act(np.zeros((1, 2 * d), np.float32), act, F32)
+        assert np.all(zero == 0)
+        big = g.uniform(30, 1000, (1, d)).astype(np.float32)
+        u = g.standard_normal((1, d)).astype(np.float32)
+        for dtype in (BF16, F32):
+            gu = W.to_bits(np.concatenate([big, u], 1), dtype)
+            out = orc.gated_act(gu, act, dtype)
+            ref = W.to_bits(f32(gu[:, :d], dtype).astype(np.float64)
+                            * f32(gu[:, d:], dtype).astype(np.float64), dtype)
+            assert same_bits(out, ref, dtype), "large-g limit"
+
+
+def pin_act_fp8(orc):
+    g = np.random.default_rng(53)
+    gu = (g.standard_normal((4, 2 * 1024)) * 1.5).astype(np.float32)
+    for act in (W.SILU, W.GELU_TANH):
+        out = orc.gated_act(gu, act, F32)
+        amax = orc.gated_act_amax(gu, act, F32)
+        assert amax == float(np.max(np.abs(out))), "act amax"
+        for inv_scale in (448.0 / amax, 100.0 / amax):
+            y = orc.gated_act_fp8(gu, np.float32(inv_scale), act, F32)
+            assert np.array_equal(y, orc.quantize_fp8(out, np.float32(inv_scale))), "act fp8"
+
+
+ALL_PINS = [
+    pin_bf16_converter, pin_f16_converter, pin_e4m3fn_converter,
+    pin_rmsnorm_vs_torch, pin_rmsnorm_closed_forms, pin_rmsnorm_bruteforce,
+    pin_rope_complex, pin_rope_closed_forms, pin_rope_invariants,
+    pin_prologue_composition, pin_prologue_constant_head,
+    pin_residual_add, pin_norm_fp8, pin_quantize_vs_torch,
+    pin_act_vs_torch, pin_act_exhaustive_bf16, pin_act_identities, pin_act_fp8,
+]

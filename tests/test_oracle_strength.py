@@ -1,0 +1,58 @@
+"""Strength control of the oracle's pins.
+
+In the spirit of the strength control in ninfer PR #273 ("Verification":
+scaling the rotation by 1.000001 must make the exact comparisons fail), each
+case below builds a copy of the oracle with one planted mistake (compiled in
+through MBT_ORACLE_MUTATION, on the CPU) and requires that at least one pin
+rejects it.  The unmutated build must pass every pin (test_oracle_pins.py).
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+import pins
+
+MUTATIONS = {
+    1: "rotation scaled by 1.000001 (the PR's strength control)",
+    2: "eps dropped from the mean square",
+    3: "prologue mean taken over rot_dim instead of head_dim",
+    4: "sin sign flipped",
+    5: "rotate-half partner off by one",
+    6: "weight offset (1 + w) ignored",
+    7: "GELU cubic coefficient 0.0447 instead of 0.044715",
+    8: "e4m3fn rounding truncates",
+    9: "bf16 rounding truncates",
+    10: "residual sum normalised before rounding",
+    11: "key heads normalised with the query weight",
+    12: "positions past the cache clamped to its last row",
+}
+
+# fast pins first: most mutations are caught within a second
+ORDER = sorted(pins.ALL_PINS, key=lambda f: f in (pins.pin_act_exhaustive_bf16,
+                                                  pins.pin_rmsnorm_bruteforce))
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS), ids=lambda m: f"m{m}")
+def test_planted_mistake_is_caught(tmp_path, mutation):
+    lib = obuild.build(out=str(tmp_path / f"liboracle_m{mutation}.so"), mutation=mutation)
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in ORDER:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin catches mutation {mutation}: {MUTATIONS[mutation]}"
+
+
+def test_rotation_nudge_fails_exact_checks(tmp_path):
+    """The 1e-6 nudge is far below one bf16 ulp; only exact comparisons see
+    it.  It must fail the bitwise closed forms and the fp32 complex pin."""
+    orc = oracle.Oracle(obuild.build(out=str(tmp_path / "m1.so"), mutation=1))
+    for pin in (pins.pin_rope_closed_forms, pins.pin_rope_complex):
+        with pytest.raises(AssertionError):
+            pin(orc)
+    assert os.path.exists(oracle.DEFAULT_LIB)
