@@ -254,7 +254,7 @@ static void pair_index(int32_t i, int32_t rot, int32_t layout, int32_t* a, int32
 }
 
 /* Position range check (P1 R5 and 5.4): only 0 <= p < max_pos reads the
- * cache; anything else is "outside the cache" and the row is NULL. */
+ * cache; any other position has no cache row and the result is NULL. */
 static const float* cache_row(const float* cos_sin, int64_t p, int64_t max_pos,
                               int32_t rot) {
 #if MBT_ORACLE_MUTATION == 12
@@ -315,7 +315,7 @@ int mbt_ref_rope(void* x, const float* cos_sin, int64_t max_pos,
 /* token, each of its Q query heads is normalised with w_q and each of its K */
 /* key heads with w_k (weights of length head_dim), the normalised value is  */
 /* rounded to the I/O dtype, and that rounded value is rotated.  A token     */
-/* whose position lies outside the cache is normalised but not rotated.      */
+/* positioned beyond the cache gets the norm only; its rotation is skipped.   */
 /* Written out on its own (not by calling the two primitives above) so the   */
 /* tests can check that this op equals their composition.                    */
 /* ------------------------------------------------------------------------ */
@@ -363,9 +363,10 @@ int mbt_ref_qknorm_rope(const void* q_in, const void* k_in, void* q_out,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Fused residual-add RMSNorm (P1 5.1 "updates the residual stream and       */
-/* normalizes its rounded value in one pass"; R1: the residual sum is the     */
-/* eager addition, i.e. fp32 add of the decoded operands rounded once).      */
+/* Fused residual-add RMSNorm (P1 5.1: the sum is written back to the        */
+/* residual stream and its rounded value is what gets normalised; R1: that   */
+/* sum matches eager addition bit for bit, i.e. it is the fp32 add of the    */
+/* decoded operands rounded once to the dtype).                              */
 /* ------------------------------------------------------------------------ */
 
 /* s[i] (fp32 value of the rounded sum) for row t; writes the residual when

@@ -69,7 +69,7 @@ int mbt_ref_rmsnorm_rows(const void* x, void* y, const void* w, int64_t rows,
 /* Standalone rotary embedding, in place, on x[T][heads][D]
  * (thox-edge-ops v2, 5.1 and R5): rotates the first rot_dim channels of every
  * head of token t by the cached angles of position pos[t]; a position outside
- * [0, max_pos) leaves the token untouched. */
+ * [0, max_pos) is skipped: its values are not modified. */
 int mbt_ref_rope(void* x, const float* cos_sin, int64_t max_pos,
                  const int64_t* pos, int64_t T, int32_t heads, int32_t D,
                  int32_t rot_dim, int32_t layout, int32_t dtype);
