@@ -1,0 +1,221 @@
+"""Python binding of libmbt: fused memory-bound decoder ops on MI355X.
+
+Argument marshalling only.  Every operation runs in the HIP kernels of
+libmbt.so (built in-tree by ``python -m memory_bound_transformer_amd.build``);
+PyTorch supplies device memory and the current stream.  There is no CPU or
+eager fallback: if the library is missing, importing this package fails.
+
+The entry points mirror include/mbt.h:
+
+    qknorm_rope            fused per-head QK-RMSNorm + RoPE prologue
+    fused_add_rmsnorm      residual add + RMSNorm, in place
+    fused_add_rmsnorm_fp8  the same with static-scale e4m3fn output
+    fused_add_rmsnorm_amax calibration pass (amax of the FP8 input)
+    gated_act              SiLU / GELU-tanh gated activation
+    gated_act_fp8          the same with static-scale e4m3fn output
+    gated_act_amax         calibration pass
+    quantize_fp8           standalone static e4m3fn quantization
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "qknorm_rope", "fused_add_rmsnorm", "fused_add_rmsnorm_fp8", "fused_add_rmsnorm_amax",
+    "gated_act", "gated_act_fp8", "gated_act_amax", "quantize_fp8", "MbtError",
+    "ROTATE_HALF", "INTERLEAVED", "SILU", "GELU_TANH", "LIB_PATH", "abi_version",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmbt.so")
+
+ROTATE_HALF, INTERLEAVED = 0, 1
+SILU, GELU_TANH = 0, 1
+_DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libmbt.so is not built ({LIB_PATH}); run: python -m memory_bound_transformer_amd.build")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+_SIGS = {
+    "mbt_qknorm_rope": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i64, _i32,
+                        _i32, _f32, _i32, _i32, _i32, _vp],
+    "mbt_fused_add_rmsnorm": [_vp, _vp, _vp, _i64, _i32, _f32, _i32, _i32, _vp],
+    "mbt_fused_add_rmsnorm_fp8": [_vp, _vp, _vp, _vp, _f32, _i64, _i32, _f32, _i32, _i32, _vp],
+    "mbt_fused_add_rmsnorm_amax": [_vp, _vp, _vp, _vp, _i64, _i32, _f32, _i32, _i32, _vp],
+    "mbt_gated_act": [_vp, _vp, _i64, _i32, _i32, _i32, _vp],
+    "mbt_gated_act_fp8": [_vp, _vp, _f32, _i64, _i32, _i32, _i32, _vp],
+    "mbt_gated_act_amax": [_vp, _vp, _i64, _i32, _i32, _i32, _vp],
+    "mbt_quantize_fp8": [_vp, _vp, _i64, _f32, _vp],
+}
+for _name, _args in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = ctypes.c_int
+_lib.mbt_status_string.argtypes = [ctypes.c_int]
+_lib.mbt_status_string.restype = ctypes.c_char_p
+_lib.mbt_last_error.argtypes = []
+_lib.mbt_last_error.restype = ctypes.c_char_p
+_lib.mbt_abi_version.argtypes = []
+_lib.mbt_abi_version.restype = ctypes.c_int32
+
+
+class MbtError(RuntimeError):
+    """A libmbt call returned a non-OK status."""
+
+    def __init__(self, status, detail):
+        self.status = status
+        name = _lib.mbt_status_string(status).decode()
+        super().__init__(f"{name}: {detail}")
+
+
+def abi_version():
+    return int(_lib.mbt_abi_version())
+
+
+def _check(status):
+    if status != 0:
+        raise MbtError(status, _lib.mbt_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16")
+
+
+def _dev(*tensors):
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libmbt operates on GPU tensors only")
+        if not t.is_contiguous():
+            raise ValueError("libmbt needs contiguous tensors")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _same_dtype(ref, *tensors):
+    for t in tensors:
+        if t is not None and t.dtype != ref.dtype:
+            raise TypeError(f"dtype mismatch: {t.dtype} vs {ref.dtype}")
+
+
+def qknorm_rope(q, k, w_q, w_k, cos_sin, pos, rot_dim, eps=1e-6, weight_offset=0,
+                layout=ROTATE_HALF, q_out=None, k_out=None, max_pos=None, stream=None):
+    """q [T, Q, D], k [T, K, D] -> (q_out, k_out) of the same shapes.
+    Pass q_out=q / k_out=k for the in-place form.  cos_sin is float32
+    [max_pos, rot_dim] (cos | sin), pos int64 [T]."""
+    _dev(q, k, w_q, w_k, cos_sin, pos, q_out, k_out)
+    _same_dtype(q, k, w_q, w_k, q_out, k_out)
+    if pos.dtype != torch.int64 or (cos_sin is not None and cos_sin.dtype != torch.float32):
+        raise TypeError("pos must be int64 and cos_sin float32")
+    T, Q, D = q.shape
+    K = k.shape[1]
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if k_out is None:
+        k_out = torch.empty_like(k)
+    mp = (cos_sin.shape[0] if cos_sin is not None else 0) if max_pos is None else max_pos
+    _check(_lib.mbt_qknorm_rope(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(w_q),
+                                _ptr(w_k), _ptr(cos_sin), mp, _ptr(pos), Q, K, T, D, rot_dim,
+                                eps, weight_offset, layout, _dtype(q), _stream(stream)))
+    return q_out, k_out
+
+
+def fused_add_rmsnorm(x, residual, w, eps=1e-6, weight_offset=0, stream=None):
+    """In place: residual <- R(x + residual); x <- RMSNorm of it.  x [T, H]."""
+    _dev(x, residual, w)
+    _same_dtype(x, residual, w)
+    H = x.shape[-1]
+    _check(_lib.mbt_fused_add_rmsnorm(_ptr(x), _ptr(residual), _ptr(w), x.numel() // H, H, eps,
+                                      weight_offset, _dtype(x), _stream(stream)))
+    return x
+
+
+def fused_add_rmsnorm_fp8(x, residual, w, inv_scale, eps=1e-6, weight_offset=0, y=None,
+                          stream=None):
+    """residual <- R(x + residual); returns y = e4m3fn codes (uint8 [T, H])."""
+    _dev(x, residual, w, y)
+    _same_dtype(x, residual, w)
+    H = x.shape[-1]
+    if y is None:
+        y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(_lib.mbt_fused_add_rmsnorm_fp8(_ptr(x), _ptr(residual), _ptr(w), _ptr(y),
+                                          float(inv_scale), x.numel() // H, H, eps,
+                                          weight_offset, _dtype(x), _stream(stream)))
+    return y
+
+
+def fused_add_rmsnorm_amax(x, residual, w, eps=1e-6, weight_offset=0, amax=None,
+                           stream=None):
+    """Calibration pass: returns a float32 [1] device tensor holding
+    max(amax_in, max |normalised value|).  A new `amax` starts at 0."""
+    _dev(x, residual, w, amax)
+    _same_dtype(x, residual, w)
+    H = x.shape[-1]
+    if amax is None:
+        amax = torch.zeros(1, dtype=torch.float32, device=x.device)
+    _check(_lib.mbt_fused_add_rmsnorm_amax(_ptr(x), _ptr(residual), _ptr(w), _ptr(amax),
+                                           x.numel() // H, H, eps, weight_offset, _dtype(x),
+                                           _stream(stream)))
+    return amax
+
+
+def gated_act(gate_up, act=SILU, out=None, stream=None):
+    """gate_up [T, 2d] = [g | u] -> out [T, d] = R(act(g) * u)."""
+    _dev(gate_up, out)
+    _same_dtype(gate_up, out)
+    d = gate_up.shape[-1] // 2
+    if out is None:
+        out = torch.empty(gate_up.shape[:-1] + (d,), dtype=gate_up.dtype, device=gate_up.device)
+    _check(_lib.mbt_gated_act(_ptr(gate_up), _ptr(out), gate_up.numel() // (2 * d), d, act,
+                              _dtype(gate_up), _stream(stream)))
+    return out
+
+
+def gated_act_fp8(gate_up, inv_scale, act=SILU, out=None, stream=None):
+    """gate_up [T, 2d] -> e4m3fn codes (uint8 [T, d]) of act(g) * u * inv_scale."""
+    _dev(gate_up, out)
+    d = gate_up.shape[-1] // 2
+    if out is None:
+        out = torch.empty(gate_up.shape[:-1] + (d,), dtype=torch.uint8, device=gate_up.device)
+    _check(_lib.mbt_gated_act_fp8(_ptr(gate_up), _ptr(out), float(inv_scale),
+                                  gate_up.numel() // (2 * d), d, act, _dtype(gate_up),
+                                  _stream(stream)))
+    return out
+
+
+def gated_act_amax(gate_up, act=SILU, amax=None, stream=None):
+    _dev(gate_up, amax)
+    d = gate_up.shape[-1] // 2
+    if amax is None:
+        amax = torch.zeros(1, dtype=torch.float32, device=gate_up.device)
+    _check(_lib.mbt_gated_act_amax(_ptr(gate_up), _ptr(amax), gate_up.numel() // (2 * d), d,
+                                   act, _dtype(gate_up), _stream(stream)))
+    return amax
+
+
+def quantize_fp8(x, inv_scale, y=None, stream=None):
+    """float32 x -> e4m3fn codes (uint8, same shape) of x * inv_scale."""
+    _dev(x, y)
+    if x.dtype != torch.float32:
+        raise TypeError("quantize_fp8 takes float32 input")
+    if y is None:
+        y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(_lib.mbt_quantize_fp8(_ptr(x), _ptr(y), x.numel(), float(inv_scale),
+                                 _stream(stream)))
+    return y

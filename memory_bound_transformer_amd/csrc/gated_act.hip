@@ -1,0 +1,240 @@
+// gated_act.hip -- gated SiLU / GELU-tanh activation for gfx950, with a
+// dtype output, a static-scale OCP e4m3fn output or a calibration amax; and
+// the standalone static FP8 quantizer.
+//
+// Operation ("thox-edge-ops v2", section 5.1: each input row holds the gate
+// projection followed by the up projection, [g || u]):
+//   out[t][j] = R(act(g) * u),  g = gate_up[t][j],  u = gate_up[t][d + j],
+//   SiLU(g) = g sigmoid(g),  GELU-tanh(g) = g sigmoid(2z),
+//   z = sqrt(2/pi) (g + 0.044715 g^3)      (0.5 (1 + tanh z) = sigmoid(2z)).
+// FP8 (FlashRT optimization details: GELU + gate + FP8 with packed 4 x FP8
+// stores; quantize_fp8_static): out = E4M3FN((act(g) * u) * inv_scale).
+//
+// MI355X design: a pure stream.  Each lane moves one 16-byte chunk of g and
+// the matching chunk of u (8 bf16 / fp16 or 4 fp32) and stores 16 bytes of
+// output or 8 / 4 packed e4m3fn codes; a 256-thread block covers U chunks per
+// lane of one token's row, so the token index is a scalar division per block,
+// not per lane.  sigmoid uses the hardware exp (v_exp_f32) on -|x| so it can
+// neither overflow nor cancel; fp32 I/O uses the full-accuracy expf.
+
+#include "mbt_device.hpp"
+#include "mbt_launch.hpp"
+
+namespace mbt {
+namespace {
+
+struct ActParams {
+    const void* gate_up;
+    void* out;
+    uint8_t* out8;
+    float* amax;
+    float inv_scale;
+    int64_t T;
+    int32_t d;
+    int32_t chunks;           // d / Vec (vector kernel)
+    int32_t blocks_per_row;   // vector kernel
+};
+
+template <int DT>
+__device__ __forceinline__ float sigmoid(float x) {
+    const float ax = fabsf(x);
+    float e;
+    if constexpr (DT == kF32) e = expf(-ax);
+    else e = __expf(-ax);
+    const float r = 1.0f / (1.0f + e);
+    return x >= 0.0f ? r : e * r;
+}
+
+template <int DT, int ACT>
+__device__ __forceinline__ float act_mul(float g, float u) {
+    float a;
+    if constexpr (ACT == 0) {
+        a = g * sigmoid<DT>(g);
+    } else {
+        const float z = 0.7978845608f * (g + 0.044715f * g * g * g);
+        a = g * sigmoid<DT>(2.0f * z);
+    }
+    return a * u;
+}
+
+// Vector kernel: d a multiple of Vec<DT>; gate_up and out 16-byte aligned,
+// out8 aligned to its 8- (16-bit) or 4-byte (fp32) store.
+template <int DT, int ACT, int MODE, int U>
+__global__ __launch_bounds__(256) void gated_vec(ActParams p) {
+    constexpr int V = Vec<DT>::n;
+    constexpr int EB = EltBytes<DT>::n;
+    const uint32_t bpr = (uint32_t)p.blocks_per_row;
+    const int64_t t = (int64_t)(blockIdx.x / bpr);
+    const int cb = (int)(blockIdx.x % bpr);
+    const char* row = (const char*)p.gate_up + t * (int64_t)(2 * p.d) * EB;
+    u32x4 gv[U], uv[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int ch = (cb * U + k) * 256 + threadIdx.x;
+        gv[k] = u32x4{0u, 0u, 0u, 0u};
+        uv[k] = u32x4{0u, 0u, 0u, 0u};
+        if (ch < p.chunks) {
+            gv[k] = ld16(row + (int64_t)ch * 16);
+            uv[k] = ld16(row + (int64_t)p.d * EB + (int64_t)ch * 16);
+        }
+    }
+    float amax_acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int ch = (cb * U + k) * 256 + threadIdx.x;
+        float g[V], u[V], y[V];
+        unpack<DT>(gv[k], g);
+        unpack<DT>(uv[k], u);
+#pragma unroll
+        for (int i = 0; i < V; ++i) y[i] = act_mul<DT, ACT>(g[i], u[i]);
+        if (ch >= p.chunks) continue;
+        const int64_t e0 = t * (int64_t)p.d + (int64_t)ch * V;
+        if constexpr (MODE == kActDtype) {
+            st16((char*)p.out + e0 * EB, pack<DT>(y));
+        } else if constexpr (MODE == kActFp8) {
+            if constexpr (V == 8) {
+                u32x2 c;
+                c[0] = fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
+                             y[3] * p.inv_scale);
+                c[1] = fp8x4(y[4] * p.inv_scale, y[5] * p.inv_scale, y[6] * p.inv_scale,
+                             y[7] * p.inv_scale);
+                *reinterpret_cast<u32x2*>(p.out8 + e0) = c;
+            } else {
+                *reinterpret_cast<uint32_t*>(p.out8 + e0) =
+                    fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
+                          y[3] * p.inv_scale);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; ++i) amax_acc = fmaxf(amax_acc, fabsf(y[i]));
+        }
+    }
+    if constexpr (MODE == kActAmax) {
+        amax_acc = seg_max<64>(amax_acc);
+        if ((threadIdx.x & 63) == 0) atomic_max_nonneg(p.amax, amax_acc);
+    }
+}
+
+// Scalar kernel: any d, element-aligned pointers; 256 elements of one row
+// per block.
+template <int DT, int ACT, int MODE>
+__global__ __launch_bounds__(256) void gated_scalar(ActParams p) {
+    const uint32_t bpr = (uint32_t)p.blocks_per_row;
+    const int64_t t = (int64_t)(blockIdx.x / bpr);
+    const int j = (int)(blockIdx.x % bpr) * 256 + threadIdx.x;
+    float amax_acc = 0.0f;
+    if (j < p.d) {
+        const int64_t gi = t * (int64_t)(2 * p.d) + j;
+        const float y = act_mul<DT, ACT>(ld_elt<DT>(p.gate_up, gi),
+                                         ld_elt<DT>(p.gate_up, gi + p.d));
+        const int64_t o = t * (int64_t)p.d + j;
+        if constexpr (MODE == kActDtype) st_elt<DT>(p.out, o, y);
+        else if constexpr (MODE == kActFp8) p.out8[o] = fp8x1(y * p.inv_scale);
+        else amax_acc = fabsf(y);
+    }
+    if constexpr (MODE == kActAmax) {
+        amax_acc = seg_max<64>(amax_acc);
+        if ((threadIdx.x & 63) == 0) atomic_max_nonneg(p.amax, amax_acc);
+    }
+}
+
+template <int DT, int ACT, int MODE>
+hipError_t launch_mode(const ActArgs& a, hipStream_t s) {
+    constexpr int V = Vec<DT>::n;
+    ActParams p{};
+    p.gate_up = a.gate_up; p.out = a.out; p.out8 = a.out8; p.amax = a.amax;
+    p.inv_scale = a.inv_scale; p.T = a.T; p.d = a.d;
+    bool vec = (a.d % V == 0) && aligned16(a.gate_up);
+    if (MODE == kActDtype) vec = vec && aligned16(a.out);
+    if (MODE == kActFp8)
+        vec = vec && ((reinterpret_cast<uintptr_t>(a.out8) & (V == 8 ? 7u : 3u)) == 0);
+    if (vec) {
+        p.chunks = a.d / V;
+        // Two chunks per lane once a row alone fills a block twice over.
+        const int U = (p.chunks >= 512 && a.T >= 64) ? 2 : 1;
+        p.blocks_per_row = (p.chunks + 256 * U - 1) / (256 * U);
+        const int64_t blocks = a.T * (int64_t)p.blocks_per_row;
+        if (blocks <= 0x7FFFFFFFll) {
+            if (U == 2)
+                hipLaunchKernelGGL((gated_vec<DT, ACT, MODE, 2>), dim3((uint32_t)blocks),
+                                   dim3(256), 0, s, p);
+            else
+                hipLaunchKernelGGL((gated_vec<DT, ACT, MODE, 1>), dim3((uint32_t)blocks),
+                                   dim3(256), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    p.blocks_per_row = (a.d + 255) / 256;
+    const int64_t blocks = a.T * (int64_t)p.blocks_per_row;
+    if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gated_scalar<DT, ACT, MODE>), dim3((uint32_t)blocks), dim3(256), 0, s,
+                       p);
+    return hipGetLastError();
+}
+
+template <int DT, int ACT>
+hipError_t launch_act(const ActArgs& a, hipStream_t s) {
+    switch (a.mode) {
+    case kActDtype: return launch_mode<DT, ACT, kActDtype>(a, s);
+    case kActFp8: return launch_mode<DT, ACT, kActFp8>(a, s);
+    default: return launch_mode<DT, ACT, kActAmax>(a, s);
+    }
+}
+
+template <int DT>
+hipError_t launch_dt(const ActArgs& a, hipStream_t s) {
+    return a.act == 0 ? launch_act<DT, 0>(a, s) : launch_act<DT, 1>(a, s);
+}
+
+// Standalone quantizer: 4 fp32 values -> one packed u32 of codes per lane.
+__global__ __launch_bounds__(256) void quantize_vec(const float* x, uint8_t* y, int64_t n4,
+                                                    float inv_scale) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const u32x4 v = ld16(x + 4 * i);
+    reinterpret_cast<uint32_t*>(y)[i] =
+        fp8x4(__uint_as_float(v[0]) * inv_scale, __uint_as_float(v[1]) * inv_scale,
+              __uint_as_float(v[2]) * inv_scale, __uint_as_float(v[3]) * inv_scale);
+}
+__global__ __launch_bounds__(256) void quantize_scalar(const float* x, uint8_t* y, int64_t n,
+                                                       float inv_scale) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) y[i] = fp8x1(x[i] * inv_scale);
+}
+
+}  // namespace
+
+hipError_t launch_gated_act(const ActArgs& a, hipStream_t s) {
+    switch (a.dtype) {
+    case kF32: return launch_dt<kF32>(a, s);
+    case kF16: return launch_dt<kF16>(a, s);
+    default: return launch_dt<kBF16>(a, s);
+    }
+}
+
+hipError_t launch_quantize_fp8(const float* x, uint8_t* y, int64_t n, float inv_scale,
+                               hipStream_t s) {
+    if (aligned16(x) && (reinterpret_cast<uintptr_t>(y) & 3u) == 0) {
+        const int64_t n4 = n / 4;
+        if (n4 > 0) {
+            const int64_t blocks = (n4 + 255) / 256;
+            if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+            hipLaunchKernelGGL(quantize_vec, dim3((uint32_t)blocks), dim3(256), 0, s, x, y, n4,
+                               inv_scale);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        const int64_t rest = n - 4 * n4;
+        if (rest > 0)
+            hipLaunchKernelGGL(quantize_scalar, dim3(1), dim3(256), 0, s, x + 4 * n4,
+                               y + 4 * n4, rest, inv_scale);
+        return hipGetLastError();
+    }
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quantize_scalar, dim3((uint32_t)blocks), dim3(256), 0, s, x, y, n,
+                       inv_scale);
+    return hipGetLastError();
+}
+
+}  // namespace mbt

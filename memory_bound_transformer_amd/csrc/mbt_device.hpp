@@ -1,0 +1,206 @@
+// mbt_device.hpp -- device-side building blocks shared by the libmbt kernels
+// (gfx950 / CDNA4, wave64).
+//
+//  * element codecs for fp32 / fp16 / bf16 and the OCP e4m3fn epilogue;
+//  * 16-byte vector loads and stores (global_load/store_dwordx4);
+//  * DPP and cross-row reductions over 4..64-lane segments of a wavefront.
+//
+// Numerics follow the contract of "thox-edge-ops v2" (section 3, R1): every
+// input decodes exactly to fp32, arithmetic is fp32, and each output is
+// rounded once to nearest-even by the hardware conversions
+// (v_cvt_pk_bf16_f32, v_cvt_pk_f16_f32, v_cvt_pk_fp8_f32), which honour the
+// default round-to-nearest-even mode.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mbt {
+
+enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Elements carried by one 16-byte vector.
+template <int DT> struct Vec { static constexpr int n = (DT == kF32) ? 4 : 8; };
+template <int DT> struct EltBytes { static constexpr int n = (DT == kF32) ? 4 : 2; };
+
+// ---- 16-byte global memory access -----------------------------------------
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ---- codecs ----------------------------------------------------------------
+
+// Decode the 16-byte vector `v` (Vec<DT>::n elements) to fp32, exactly.
+template <int DT>
+__device__ __forceinline__ void unpack(const u32x4 v, float* f) {
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+    } else if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(v[i] << 16);
+            f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f16x2_t h = __builtin_bit_cast(f16x2_t, v[i]);
+            f[2 * i] = (float)h[0];
+            f[2 * i + 1] = (float)h[1];
+        }
+    }
+}
+
+// Round two fp32 values to a packed pair of 16-bit elements (RNE).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    if constexpr (DT == kBF16) {
+        bf16x2_t v = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        f16x2_t v = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+// Round Vec<DT>::n fp32 values to one 16-byte vector of DT.
+template <int DT>
+__device__ __forceinline__ u32x4 pack(const float* f) {
+    u32x4 v;
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = pack2<DT>(f[2 * i], f[2 * i + 1]);
+    }
+    return v;
+}
+
+// Scalar element access for the unaligned / odd-width kernels.
+template <int DT>
+__device__ __forceinline__ float ld_elt(const void* p, int64_t i) {
+    if constexpr (DT == kF32) {
+        return reinterpret_cast<const float*>(p)[i];
+    } else if constexpr (DT == kBF16) {
+        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16);
+    } else {
+        return (float)reinterpret_cast<const _Float16*>(p)[i];
+    }
+}
+template <int DT>
+__device__ __forceinline__ void st_elt(void* p, int64_t i, float v) {
+    if constexpr (DT == kF32) {
+        reinterpret_cast<float*>(p)[i] = v;
+    } else if constexpr (DT == kBF16) {
+        reinterpret_cast<__bf16*>(p)[i] = (__bf16)v;
+    } else {
+        reinterpret_cast<_Float16*>(p)[i] = (_Float16)v;
+    }
+}
+// R(v) read back as fp32: the value a later step of a fused op consumes.
+template <int DT>
+__device__ __forceinline__ float round_trip(float v) {
+    if constexpr (DT == kF32) {
+        return v;
+    } else if constexpr (DT == kBF16) {
+        return (float)(__bf16)v;
+    } else {
+        return (float)(_Float16)v;
+    }
+}
+
+// OCP e4m3fn with saturation: +-inf and |v| > 448 clamp to +-448, NaN stays
+// NaN; the hardware conversion then rounds to nearest-even (subnormals
+// included).  Two values -> 16 bits; `hi` selects the upper half of `old`.
+__device__ __forceinline__ float fp8_clamp(float v) {
+    return (v != v) ? v : __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+}
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(a), fp8_clamp(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(c), fp8_clamp(d), w, true);
+    return (uint32_t)w;
+}
+__device__ __forceinline__ uint8_t fp8x1(float a) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(a), fp8_clamp(a), 0, false);
+    return (uint8_t)(w & 0xff);
+}
+
+// ---- reductions ------------------------------------------------------------
+
+// DPP controls (GCN / CDNA encoding).
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane i <- 7 - i (in 8)
+constexpr int kDppMirror = 0x140;     // row_mirror: lane i <- 15 - i (in 16)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned segments of SEG lanes (SEG in 4, 8, 16, 32, 64); every lane
+// of a segment receives the segment's total.  Within a 16-lane DPP row the
+// steps are xor-1, xor-2 (quad permutes) and the half / full row mirrors,
+// which act as xor-4 / xor-8 once each quad / half-row already holds one
+// value; wider segments add across rows with lane shuffles.
+template <int SEG>
+__device__ __forceinline__ float seg_sum(float v) {
+    static_assert(SEG == 4 || SEG == 8 || SEG == 16 || SEG == 32 || SEG == 64, "segment");
+    v += dpp<kDppQuadXor1>(v);
+    v += dpp<kDppQuadXor2>(v);
+    if constexpr (SEG >= 8) v += dpp<kDppHalfMirror>(v);
+    if constexpr (SEG >= 16) v += dpp<kDppMirror>(v);
+    if constexpr (SEG >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (SEG >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+template <int SEG>
+__device__ __forceinline__ float seg_max(float v) {
+    v = fmaxf(v, dpp<kDppQuadXor1>(v));
+    v = fmaxf(v, dpp<kDppQuadXor2>(v));
+    if constexpr (SEG >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    if constexpr (SEG >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+    if constexpr (SEG >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+    if constexpr (SEG >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+// XCD-aware block renumbering.  MI355X dispatches workgroup b to XCD b % 8;
+// XCD x therefore runs hardware blocks x, x + 8, x + 16, ...  Map them to the
+// contiguous logical range [x q + min(x, r), ... + count(x)), q = nb / 8,
+// r = nb % 8, count(x) = q + (x < r): a bijection on [0, nb) that keeps
+// neighbouring logical blocks (and the data they share) on one XCD's L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb) {
+    const uint32_t x = b & 7u, slot = b >> 3;
+    const uint32_t q = nb >> 3, r = nb & 7u;
+    return x * q + (x < r ? x : r) + slot;
+}
+
+// Wave-uniform value as a scalar register.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Fold a non-negative float into a device-wide maximum (bit patterns of
+// non-negative floats order like the integers).
+__device__ __forceinline__ void atomic_max_nonneg(float* dst, float v) {
+    atomicMax(reinterpret_cast<unsigned int*>(dst), __float_as_uint(v));
+}
+
+// 1 / sqrt(m) on the hardware reciprocal square root (about 1 ulp).
+__device__ __forceinline__ float rsqrt_hw(float m) { return __builtin_amdgcn_rsqf(m); }
+
+}  // namespace mbt
