@@ -14,8 +14,9 @@
 // the matching chunk of u (8 bf16 / fp16 or 4 fp32) and stores 16 bytes of
 // output or 8 / 4 packed e4m3fn codes; a 256-thread block covers U chunks per
 // lane of one token's row, so the token index is a scalar division per block,
-// not per lane.  sigmoid uses the hardware exp (v_exp_f32) on -|x| so it can
-// neither overflow nor cancel; fp32 I/O uses the full-accuracy expf.
+// not per lane.  sigmoid is evaluated from e^-|x| so it can neither overflow
+// nor cancel; 16-bit I/O takes e^-|x| from the hardware exp2 (with a rescale
+// that keeps results below FLT_MIN), fp32 I/O from the full-accuracy expf.
 
 #include "mbt_device.hpp"
 #include "mbt_launch.hpp"
@@ -35,12 +36,23 @@ struct ActParams {
     int32_t blocks_per_row;   // vector kernel
 };
 
+// e^-a for a >= 0 on the hardware exp2 (v_exp_f32).  v_exp_f32 returns 0
+// for results below the smallest normal float, yet e.g. SiLU(-90) =
+// -90 e^-90 ~ -7e-38 is still a normal bf16; so exponents below -126 are
+// raised by 32 and the result scaled back by the exact power 2^-32.
+__device__ __forceinline__ float exp_neg(float a) {
+    const float t = a * -1.4426950408889634f;          // -a log2(e)
+    const bool tiny = t < -126.0f;
+    const float e = __builtin_amdgcn_exp2f(tiny ? t + 32.0f : t);
+    return tiny ? e * 2.3283064365386963e-10f : e;
+}
+
 template <int DT>
 __device__ __forceinline__ float sigmoid(float x) {
     const float ax = fabsf(x);
     float e;
-    if constexpr (DT == kF32) e = expf(-ax);
-    else e = __expf(-ax);
+    if constexpr (DT == kF32) e = expf(-ax);           // full accuracy for fp32 I/O
+    else e = exp_neg(ax);
     const float r = 1.0f / (1.0f + e);
     return x >= 0.0f ? r : e * r;
 }

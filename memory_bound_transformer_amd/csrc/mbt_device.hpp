@@ -56,7 +56,10 @@ __device__ __forceinline__ void unpack(const u32x4 v, float* f) {
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            f16x2_t h = __builtin_bit_cast(f16x2_t, v[i]);
+            // copy the element out first: a bit_cast applied directly to the
+            // vector-element expression v[i] reads element 0 for every i
+            const uint32_t w = v[i];
+            const f16x2_t h = __builtin_bit_cast(f16x2_t, w);
             f[2 * i] = (float)h[0];
             f[2 * i + 1] = (float)h[1];
         }

@@ -31,6 +31,7 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 
 #ifndef MBT_ORACLE_MUTATION
@@ -391,22 +392,22 @@ static void residual_sum(const void* x, void* residual, int64_t t, int32_t H,
 }
 
 static int norm_args_ok(int64_t T, int32_t H, int32_t delta, int32_t dtype) {
-    return dtype_ok(dtype) && T >= 0 && H > 0 && H <= 65536 && !(delta & ~1);
+    return dtype_ok(dtype) && T >= 0 && H > 0 && !(delta & ~1);
 }
-
-static float row_buf[65536];
 
 int mbt_ref_fused_add_rmsnorm(void* x, void* residual, const void* w,
                               int64_t T, int32_t H, float eps,
                               int32_t weight_offset, int32_t dtype) {
     if (!norm_args_ok(T, H, weight_offset, dtype)) return -1;
-    float* s = row_buf;
+    float* s = (float*)malloc((size_t)H * sizeof(float));
+    if (!s) return -1;
     for (int64_t t = 0; t < T; t++) {
         residual_sum(x, residual, t, H, dtype, 1, s);
         float inv = inv_rms(s, H, 0, eps);
         for (int32_t i = 0; i < H; i++)
             st(x, t * H + i, dtype, (s[i] * inv) * weight_term(w, i, dtype, weight_offset));
     }
+    free(s);
     return 0;
 }
 
@@ -415,7 +416,8 @@ int mbt_ref_fused_add_rmsnorm_fp8(const void* x, void* residual, const void* w,
                                   int32_t H, float eps, int32_t weight_offset,
                                   int32_t dtype) {
     if (!norm_args_ok(T, H, weight_offset, dtype)) return -1;
-    float* s = row_buf;
+    float* s = (float*)malloc((size_t)H * sizeof(float));
+    if (!s) return -1;
     for (int64_t t = 0; t < T; t++) {
         residual_sum(x, residual, t, H, dtype, 1, s);
         float inv = inv_rms(s, H, 0, eps);
@@ -424,6 +426,7 @@ int mbt_ref_fused_add_rmsnorm_fp8(const void* x, void* residual, const void* w,
             y[t * H + i] = mbt_ref_f32_to_e4m3fn(v * inv_scale);
         }
     }
+    free(s);
     return 0;
 }
 
@@ -432,7 +435,8 @@ float mbt_ref_fused_add_rmsnorm_amax(const void* x, const void* residual,
                                      float eps, int32_t weight_offset,
                                      int32_t dtype) {
     if (!norm_args_ok(T, H, weight_offset, dtype)) return -1.0f;
-    float* s = row_buf;
+    float* s = (float*)malloc((size_t)H * sizeof(float));
+    if (!s) return -1;
     float amax = 0.0f;
     for (int64_t t = 0; t < T; t++) {
         residual_sum(x, (void*)residual, t, H, dtype, 0, s);
@@ -442,6 +446,7 @@ float mbt_ref_fused_add_rmsnorm_amax(const void* x, const void* residual,
             if (v > amax) amax = v;
         }
     }
+    free(s);
     return amax;
 }
 
