@@ -18,6 +18,8 @@
 // nor cancel; 16-bit I/O takes e^-|x| from the hardware exp2 (with a rescale
 // that keeps results below FLT_MIN), fp32 I/O from the full-accuracy expf.
 
+#include <stdlib.h>
+
 #include "mbt_device.hpp"
 #include "mbt_launch.hpp"
 
@@ -53,7 +55,7 @@ __device__ __forceinline__ float sigmoid(float x) {
     float e;
     if constexpr (DT == kF32) e = expf(-ax);           // full accuracy for fp32 I/O
     else e = exp_neg(ax);
-    const float r = 1.0f / (1.0f + e);
+    const float r = __builtin_amdgcn_rcpf(1.0f + e);   // v_rcp_f32, 1 ulp
     return x >= 0.0f ? r : e * r;
 }
 
@@ -86,8 +88,8 @@ __global__ __launch_bounds__(256) void gated_vec(ActParams p) {
         gv[k] = u32x4{0u, 0u, 0u, 0u};
         uv[k] = u32x4{0u, 0u, 0u, 0u};
         if (ch < p.chunks) {
-            gv[k] = ld16(row + (int64_t)ch * 16);
-            uv[k] = ld16(row + (int64_t)p.d * EB + (int64_t)ch * 16);
+            gv[k] = ld16_nt(row + (int64_t)ch * 16);
+            uv[k] = ld16_nt(row + (int64_t)p.d * EB + (int64_t)ch * 16);
         }
     }
     float amax_acc = 0.0f;
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(256) void gated_vec(ActParams p) {
         if (ch >= p.chunks) continue;
         const int64_t e0 = t * (int64_t)p.d + (int64_t)ch * V;
         if constexpr (MODE == kActDtype) {
-            st16((char*)p.out + e0 * EB, pack<DT>(y));
+            st16_nt((char*)p.out + e0 * EB, pack<DT>(y));
         } else if constexpr (MODE == kActFp8) {
             if constexpr (V == 8) {
                 u32x2 c;
@@ -110,11 +112,10 @@ __global__ __launch_bounds__(256) void gated_vec(ActParams p) {
                              y[3] * p.inv_scale);
                 c[1] = fp8x4(y[4] * p.inv_scale, y[5] * p.inv_scale, y[6] * p.inv_scale,
                              y[7] * p.inv_scale);
-                *reinterpret_cast<u32x2*>(p.out8 + e0) = c;
+                st8_nt(p.out8 + e0, c);
             } else {
-                *reinterpret_cast<uint32_t*>(p.out8 + e0) =
-                    fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
-                          y[3] * p.inv_scale);
+                st4_nt(p.out8 + e0, fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale,
+                                          y[2] * p.inv_scale, y[3] * p.inv_scale));
             }
         } else {
 #pragma unroll
@@ -150,6 +151,21 @@ __global__ __launch_bounds__(256) void gated_scalar(ActParams p) {
     }
 }
 
+// Launch-shape tunables, read once from the environment (sweeps only; the
+// defaults are the measured best on MI355X).
+int env_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    return e ? atoi(e) : dflt;
+}
+int tun_act_u() {
+    static const int v = env_int("MBT_ACT_U", 0);
+    return v;
+}
+int64_t tun_act_u2_chunks() {
+    static const int v = env_int("MBT_ACT_U2_CHUNKS", 400000);
+    return v;
+}
+
 template <int DT, int ACT, int MODE>
 hipError_t launch_mode(const ActArgs& a, hipStream_t s) {
     constexpr int V = Vec<DT>::n;
@@ -162,8 +178,10 @@ hipError_t launch_mode(const ActArgs& a, hipStream_t s) {
         vec = vec && ((reinterpret_cast<uintptr_t>(a.out8) & (V == 8 ? 7u : 3u)) == 0);
     if (vec) {
         p.chunks = a.d / V;
-        // Two chunks per lane once a row alone fills a block twice over.
-        const int U = (p.chunks >= 512 && a.T >= 64) ? 2 : 1;
+        // Two chunks per lane only at prefill widths: at decode widths the
+        // per-wave latency matters more than the per-wave overhead.
+        int U = (a.T * (int64_t)p.chunks >= tun_act_u2_chunks()) ? 2 : 1;
+        if (tun_act_u() == 1 || tun_act_u() == 2) U = tun_act_u();
         p.blocks_per_row = (p.chunks + 256 * U - 1) / (256 * U);
         const int64_t blocks = a.T * (int64_t)p.blocks_per_row;
         if (blocks <= 0x7FFFFFFFll) {
@@ -203,10 +221,9 @@ __global__ __launch_bounds__(256) void quantize_vec(const float* x, uint8_t* y, 
                                                     float inv_scale) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n4) return;
-    const u32x4 v = ld16(x + 4 * i);
-    reinterpret_cast<uint32_t*>(y)[i] =
-        fp8x4(__uint_as_float(v[0]) * inv_scale, __uint_as_float(v[1]) * inv_scale,
-              __uint_as_float(v[2]) * inv_scale, __uint_as_float(v[3]) * inv_scale);
+    const u32x4 v = ld16_nt(x + 4 * i);
+    st4_nt(y + 4 * i, fp8x4(__uint_as_float(v[0]) * inv_scale, __uint_as_float(v[1]) * inv_scale,
+                            __uint_as_float(v[2]) * inv_scale, __uint_as_float(v[3]) * inv_scale));
 }
 __global__ __launch_bounds__(256) void quantize_scalar(const float* x, uint8_t* y, int64_t n,
                                                        float inv_scale) {

@@ -38,6 +38,23 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 __device__ __forceinline__ void st16(void* p, u32x4 v) {
     *reinterpret_cast<u32x4*>(p) = v;
 }
+// Streaming (nontemporal) forms for tensors each launch touches exactly
+// once: the loads and stores carry the nt hint, so the lines neither evict
+// reused data (weights, rotary rows) from L2 / Infinity Cache nor wait there.
+// Measured on MI355X: a cold 59 MB copy runs at 5.4 TB/s with the hint and
+// 4.6 TB/s without.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st8_nt(void* p, u32x2 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st4_nt(void* p, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
 
 // ---- codecs ----------------------------------------------------------------
 
@@ -154,12 +171,42 @@ __device__ __forceinline__ float dpp(float v) {
     return __int_as_float(
         __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Cross-row exchanges on gfx950's VALU lane swaps (no LDS traffic):
+// v_permlane16_swap on (v, v) leaves rows (r0, r0, r2, r2) in the first
+// result and (r1, r1, r3, r3) in the second; v_permlane32_swap on (v, v)
+// leaves (lo, lo) and (hi, hi).  Adding the two halves in that fixed order
+// gives every lane of the 32- / 64-lane group the same bits.
+__device__ __forceinline__ float xrow16_sum(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                              false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xrow32_sum(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                              false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xrow16_max(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                              false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xrow32_max(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                              false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // Sum over aligned segments of SEG lanes (SEG in 4, 8, 16, 32, 64); every lane
 // of a segment receives the segment's total.  Within a 16-lane DPP row the
 // steps are xor-1, xor-2 (quad permutes) and the half / full row mirrors,
 // which act as xor-4 / xor-8 once each quad / half-row already holds one
-// value; wider segments add across rows with lane shuffles.
+// value; wider segments add across rows with the lane swaps above.
 template <int SEG>
 __device__ __forceinline__ float seg_sum(float v) {
     static_assert(SEG == 4 || SEG == 8 || SEG == 16 || SEG == 32 || SEG == 64, "segment");
@@ -167,8 +214,8 @@ __device__ __forceinline__ float seg_sum(float v) {
     v += dpp<kDppQuadXor2>(v);
     if constexpr (SEG >= 8) v += dpp<kDppHalfMirror>(v);
     if constexpr (SEG >= 16) v += dpp<kDppMirror>(v);
-    if constexpr (SEG >= 32) v += __shfl_xor(v, 16, 64);
-    if constexpr (SEG >= 64) v += __shfl_xor(v, 32, 64);
+    if constexpr (SEG >= 32) v = xrow16_sum(v);
+    if constexpr (SEG >= 64) v = xrow32_sum(v);
     return v;
 }
 
@@ -178,8 +225,8 @@ __device__ __forceinline__ float seg_max(float v) {
     v = fmaxf(v, dpp<kDppQuadXor2>(v));
     if constexpr (SEG >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
     if constexpr (SEG >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
-    if constexpr (SEG >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
-    if constexpr (SEG >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
+    if constexpr (SEG >= 32) v = xrow16_max(v);
+    if constexpr (SEG >= 64) v = xrow32_max(v);
     return v;
 }
 

@@ -50,7 +50,7 @@ __device__ __forceinline__ void emit(const NormParams& p, int64_t row, int64_t e
     constexpr int V = Vec<DT>::n;
     constexpr int EB = EltBytes<DT>::n;
     if constexpr (MODE == kNormInPlace) {
-        st16((char*)p.x_out + (row * p.H + e0) * EB, pack<DT>(y));
+        st16_nt((char*)p.x_out + (row * p.H + e0) * EB, pack<DT>(y));
     } else if constexpr (MODE == kNormFp8) {
         uint8_t* dst = p.y8 + row * p.H + e0;
         if constexpr (V == 8) {
@@ -59,11 +59,10 @@ __device__ __forceinline__ void emit(const NormParams& p, int64_t row, int64_t e
                          y[3] * p.inv_scale);
             c[1] = fp8x4(y[4] * p.inv_scale, y[5] * p.inv_scale, y[6] * p.inv_scale,
                          y[7] * p.inv_scale);
-            *reinterpret_cast<u32x2*>(dst) = c;
+            st8_nt(dst, c);
         } else {
-            *reinterpret_cast<uint32_t*>(dst) =
-                fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
-                      y[3] * p.inv_scale);
+            st4_nt(dst, fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
+                              y[3] * p.inv_scale));
         }
     } else {
 #pragma unroll
@@ -97,8 +96,8 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
         wv[k] = u32x4{0u, 0u, 0u, 0u};
         if (live && ch < chunks) {
             const int64_t off = (row * p.H + (int64_t)ch * V) * EB;
-            xv[k] = ld16((const char*)p.x + off);
-            if (has_res) rv[k] = ld16((const char*)p.residual + off);
+            xv[k] = ld16_nt((const char*)p.x + off);
+            if (has_res) rv[k] = ld16_nt((const char*)p.residual + off);
             wv[k] = ld16((const char*)p.w + (int64_t)ch * V * EB);
         }
     }
@@ -134,7 +133,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
         if (!(live && ch < chunks)) continue;
         const int64_t e0 = (int64_t)ch * V;
         if (has_res && MODE != kNormAmax)
-            st16((char*)p.residual + (row * p.H + e0) * EB, xv[k]);
+            st16_nt((char*)p.residual + (row * p.H + e0) * EB, xv[k]);
         float s[V], wf[V], y[V];
         unpack<DT>(xv[k], s);
         unpack<DT>(wv[k], wf);
@@ -189,23 +188,27 @@ __global__ __launch_bounds__(256) void rmsnorm_scalar(NormParams p) {
 }
 
 // Launch shape: waves per row for a row of `chunks` 16-byte chunks.
-// Decode widths (few rows) spread each row over many waves, one or two
-// chunks per lane; prefill widths keep a row in one wave (no barrier) as
-// long as that needs at most kMaxNch chunks per lane (more would spill under
-// the 1024-thread launch bound, which caps a wave at 128 VGPRs).
+// Decode widths (few rows) spread each row over as many waves as it has
+// 64-chunk groups, one chunk per lane (the shortest per-wave latency);
+// prefill widths keep a row in as few waves as kMaxNch chunks per lane
+// allow (more chunks per lane would spill under the 1024-thread launch
+// bound, which caps a wave at 128 VGPRs).
 constexpr int kMaxNch = 6;
 
+int env_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    return e ? atoi(e) : dflt;
+}
+
 int pick_wpr(int64_t T, int chunks) {
-    static const int forced = [] {
-        const char* e = getenv("MBT_NORM_WPR");
-        return e ? atoi(e) : 0;
-    }();
+    static const int forced = env_int("MBT_NORM_WPR", 0);
+    static const int wide_rows = env_int("MBT_NORM_WIDE_CHUNKS", 32768);
     const int per64 = (chunks + kWave - 1) / kWave;    // chunks per lane at WPR 1
     const int min_wpr = (per64 + kMaxNch - 1) / kMaxNch;
-    if (forced > 0) return forced < min_wpr ? min_wpr : (forced > 16 ? 16 : forced);
     int wpr;
-    if (T * per64 >= 4096) wpr = min_wpr;              // enough rows to fill the chip
-    else wpr = (per64 + 1) / 2;                         // about two chunks per lane
+    if (forced > 0) wpr = forced;
+    else if (T * per64 >= wide_rows) wpr = min_wpr;    // enough rows to fill the chip
+    else wpr = per64;                                   // one chunk per lane
     if (wpr < min_wpr) wpr = min_wpr;
     if (wpr > 16) wpr = 16;
     if (wpr < 1) wpr = 1;
