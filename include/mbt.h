@@ -121,6 +121,31 @@ MBT_API mbt_status mbt_qknorm_rope(const void* q_in, const void* k_in, void* q_o
                            int32_t layout, int32_t dtype, void* stream);
 
 /*
+ * mbt_rope -- standalone rotary position embedding, in place.
+ *
+ * P1 section 5.1 (rotary embedding of every query and key head by the angles
+ * cached for the token's position) and section 3 R5 (a position outside the
+ * cache leaves that token untouched): for each token t with
+ * 0 <= p = pos[t] < max_pos, each pair (a, b) of the first rot_dim channels
+ * of every head (rotate-half: (j, j + rot_dim/2); interleaved: (2j, 2j+1)) is
+ *   a <- R(a c - b s),  b <- R(b c + a s),  c = cos_sin[p][j],
+ *   s = cos_sin[p][rot_dim/2 + j],
+ * each product rounded on its own; other channels and out-of-range tokens are
+ * not written.  Together with mbt_fused_add_rmsnorm (residual = NULL) on the
+ * head rows it is the three-call route the fused prologue replaces, and it
+ * reproduces mbt_qknorm_rope bit for bit.
+ *
+ *  q [T][Q][head_dim], k [T][K][head_dim]  dtype, read and written in place;
+ *                                          must not overlap each other
+ *  cos_sin, pos, max_pos, Q, K, T, head_dim, rot_dim, layout, dtype: as for
+ *  mbt_qknorm_rope.
+ */
+MBT_API mbt_status mbt_rope(void* q, void* k, const float* cos_sin, int64_t max_pos,
+                            const int64_t* pos, int32_t Q, int32_t K, int64_t T,
+                            int32_t head_dim, int32_t rot_dim, int32_t layout, int32_t dtype,
+                            void* stream);
+
+/*
  * mbt_fused_add_rmsnorm -- residual add + RMSNorm in one pass, in place.
  *
  * Defined by P1 section 5.1 (the residual sum is stored back into the

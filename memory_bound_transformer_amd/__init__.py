@@ -8,6 +8,7 @@ eager fallback: if the library is missing, importing this package fails.
 The entry points mirror include/mbt.h:
 
     qknorm_rope            fused per-head QK-RMSNorm + RoPE prologue
+    rope                   standalone rotary embedding, in place
     fused_add_rmsnorm      residual add + RMSNorm, in place
     fused_add_rmsnorm_fp8  the same with static-scale e4m3fn output
     fused_add_rmsnorm_amax calibration pass (amax of the FP8 input)
@@ -22,7 +23,7 @@ import os
 import torch
 
 __all__ = [
-    "qknorm_rope", "fused_add_rmsnorm", "fused_add_rmsnorm_fp8", "fused_add_rmsnorm_amax",
+    "qknorm_rope", "rope", "fused_add_rmsnorm", "fused_add_rmsnorm_fp8", "fused_add_rmsnorm_amax",
     "gated_act", "gated_act_fp8", "gated_act_amax", "quantize_fp8", "MbtError",
     "ROTATE_HALF", "INTERLEAVED", "SILU", "GELU_TANH", "LIB_PATH", "abi_version",
 ]
@@ -44,6 +45,7 @@ _vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.
 _SIGS = {
     "mbt_qknorm_rope": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i64, _i32,
                         _i32, _f32, _i32, _i32, _i32, _vp],
+    "mbt_rope": [_vp, _vp, _vp, _i64, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp],
     "mbt_fused_add_rmsnorm": [_vp, _vp, _vp, _i64, _i32, _f32, _i32, _i32, _vp],
     "mbt_fused_add_rmsnorm_fp8": [_vp, _vp, _vp, _vp, _f32, _i64, _i32, _f32, _i32, _i32, _vp],
     "mbt_fused_add_rmsnorm_amax": [_vp, _vp, _vp, _vp, _i64, _i32, _f32, _i32, _i32, _vp],
@@ -134,6 +136,21 @@ def qknorm_rope(q, k, w_q, w_k, cos_sin, pos, rot_dim, eps=1e-6, weight_offset=0
                                 _ptr(w_k), _ptr(cos_sin), mp, _ptr(pos), Q, K, T, D, rot_dim,
                                 eps, weight_offset, layout, _dtype(q), _stream(stream)))
     return q_out, k_out
+
+
+def rope(q, k, cos_sin, pos, rot_dim, layout=ROTATE_HALF, max_pos=None, stream=None):
+    """In place: rotate the first rot_dim channels of q [T, Q, D] and
+    k [T, K, D] by cos_sin[pos[t]]; tokens outside the cache are untouched."""
+    _dev(q, k, cos_sin, pos)
+    _same_dtype(q, k)
+    if pos.dtype != torch.int64 or (cos_sin is not None and cos_sin.dtype != torch.float32):
+        raise TypeError("pos must be int64 and cos_sin float32")
+    T, Q, D = q.shape
+    K = k.shape[1]
+    mp = (cos_sin.shape[0] if cos_sin is not None else 0) if max_pos is None else max_pos
+    _check(_lib.mbt_rope(_ptr(q), _ptr(k), _ptr(cos_sin), mp, _ptr(pos), Q, K, T, D, rot_dim,
+                         layout, _dtype(q), _stream(stream)))
+    return q, k
 
 
 def fused_add_rmsnorm(x, residual, w, eps=1e-6, weight_offset=0, stream=None):

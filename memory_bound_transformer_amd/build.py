@@ -3,7 +3,8 @@
     python -m memory_bound_transformer_amd.build        (or python .../build.py)
 
 Every source under csrc/ is compiled by hipcc for --offload-arch=gfx950 with
-packed-fp32 instruction selection switched off, then linked into
+packed-fp32 instruction selection and floating-point contraction switched
+off, then linked into
 memory_bound_transformer_amd/libmbt.so next to the Python binding.  Only the
 symbols declared in include/mbt.h are exported.
 """
@@ -20,10 +21,14 @@ LIB = os.path.join(HERE, "libmbt.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["mbt_api.cpp", "qknorm_rope.hip", "rmsnorm.hip", "gated_act.hip"]
+SOURCES = ["mbt_api.cpp", "qknorm_rope.hip", "rope.hip", "rmsnorm.hip", "gated_act.hip"]
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-Wall", "-Wno-unused-function",
+         # every fp32 operation rounds where the source writes it: no product is
+         # fused with an add or with a narrowing conversion (v_fma_mix*) unless
+         # the source calls fmaf, so every kernel rounds in the same places
+         "-ffp-contract=off",
          # no v_pk_*_f32 from the compiler: scalar fp32 arithmetic only
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -162,6 +162,48 @@ mbt_status mbt_qknorm_rope(const void* q_in, const void* k_in, void* q_out, void
     return hip_status(mbt::launch_qknorm_rope(a, (hipStream_t)stream), "qknorm_rope launch");
 }
 
+mbt_status mbt_rope(void* q, void* k, const float* cos_sin, int64_t max_pos, const int64_t* pos,
+                    int32_t Q, int32_t K, int64_t T, int32_t head_dim, int32_t rot_dim,
+                    int32_t layout, int32_t dtype, void* stream) {
+    if (!valid_dtype(dtype)) return fail(MBT_ERR_BAD_DTYPE, "dtype %d", dtype);
+    if (layout != MBT_ROPE_ROTATE_HALF && layout != MBT_ROPE_INTERLEAVED)
+        return fail(MBT_ERR_BAD_ENUM, "layout %d", layout);
+    if (Q < 0 || K < 0 || Q + K < 1) return fail(MBT_ERR_BAD_SHAPE, "Q=%d K=%d", Q, K);
+    if (T < 0) return fail(MBT_ERR_BAD_SHAPE, "T=%lld", (long long)T);
+    if (head_dim < 1 || head_dim > 512)
+        return fail(MBT_ERR_BAD_SHAPE, "head_dim %d not in [1, 512]", head_dim);
+    if (rot_dim < 0 || rot_dim > head_dim || (rot_dim % 2) != 0)
+        return fail(MBT_ERR_BAD_SHAPE, "rot_dim %d (head_dim %d)", rot_dim, head_dim);
+    if (max_pos < 0) return fail(MBT_ERR_BAD_SCALAR, "max_pos %lld", (long long)max_pos);
+    const int eb = elt_bytes(dtype);
+    const int64_t q_bytes = mul(mul(mul(T, Q), head_dim), eb);
+    const int64_t k_bytes = mul(mul(mul(T, K), head_dim), eb);
+    const int64_t cs_bytes = mul(mul(max_pos, rot_dim), 4);
+    if (q_bytes < 0 || k_bytes < 0 || cs_bytes < 0 || mul(T, Q + K) > (INT64_C(1) << 40))
+        return fail(MBT_ERR_BAD_SHAPE, "tensor sizes overflow");
+    if (T == 0) return ok();
+    const bool need_cache = rot_dim > 0 && max_pos > 0;
+    if ((Q > 0 && !q) || (K > 0 && !k)) return fail(MBT_ERR_NULL_POINTER, "q / k required");
+    if (!pos) return fail(MBT_ERR_NULL_POINTER, "pos is required");
+    if (need_cache && !cos_sin)
+        return fail(MBT_ERR_NULL_POINTER, "cos_sin is required when rot_dim > 0");
+    if ((Q > 0 && !aligned(q, eb)) || (K > 0 && !aligned(k, eb)) || !aligned(pos, 8) ||
+        (need_cache && !aligned(cos_sin, 4)))
+        return fail(MBT_ERR_ALIGN, "a pointer is not aligned to its element size");
+    const Range qr{(const char*)(Q ? q : nullptr), q_bytes, "q"};
+    const Range kr{(const char*)(K ? k : nullptr), k_bytes, "k"};
+    const Range cs{(const char*)(need_cache ? cos_sin : nullptr), cs_bytes, "cos_sin"};
+    const Range ps{(const char*)pos, T * 8, "pos"};
+    if (overlap(qr, kr)) return fail(MBT_ERR_ALIAS, "q overlaps k");
+    for (const Range* o : {&qr, &kr})
+        for (const Range* i : {&cs, &ps}) {
+            mbt_status st = check_alias(*o, *i, false);
+            if (st != MBT_OK) return st;
+        }
+    mbt::RopeArgs a{q, k, cos_sin, max_pos, pos, Q, K, T, head_dim, rot_dim, layout, dtype};
+    return hip_status(mbt::launch_rope(a, (hipStream_t)stream), "rope launch");
+}
+
 namespace {
 
 mbt_status norm_common(const void* x, const void* residual, const void* w, int64_t T,

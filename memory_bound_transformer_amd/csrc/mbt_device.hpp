@@ -83,6 +83,17 @@ __device__ __forceinline__ void unpack(const u32x4 v, float* f) {
     }
 }
 
+// An fp32 value the compiler must treat as already rounded to fp32.  The
+// AMDGPU backend otherwise folds an fp32 product followed by a narrowing to
+// fp16 into one v_fma_mixlo_f16, which rounds the exact product once, straight
+// to fp16, instead of to fp32 and then to fp16 (and turns -0 into +0); even
+// -ffp-contract=off does not stop that fold.  The empty asm costs nothing.
+__device__ __forceinline__ float as_f32(float v) {
+    asm("" : "+v"(v));
+    return v;
+}
+__device__ __forceinline__ _Float16 to_f16(float v) { return (_Float16)as_f32(v); }
+
 // Round two fp32 values to a packed pair of 16-bit elements (RNE).
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -90,7 +101,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
         bf16x2_t v = {(__bf16)a, (__bf16)b};
         return __builtin_bit_cast(uint32_t, v);
     } else {
-        f16x2_t v = {(_Float16)a, (_Float16)b};
+        f16x2_t v = {to_f16(a), to_f16(b)};
         return __builtin_bit_cast(uint32_t, v);
     }
 }
@@ -127,7 +138,7 @@ __device__ __forceinline__ void st_elt(void* p, int64_t i, float v) {
     } else if constexpr (DT == kBF16) {
         reinterpret_cast<__bf16*>(p)[i] = (__bf16)v;
     } else {
-        reinterpret_cast<_Float16*>(p)[i] = (_Float16)v;
+        reinterpret_cast<_Float16*>(p)[i] = to_f16(v);
     }
 }
 // R(v) read back as fp32: the value a later step of a fused op consumes.
@@ -138,7 +149,7 @@ __device__ __forceinline__ float round_trip(float v) {
     } else if constexpr (DT == kBF16) {
         return (float)(__bf16)v;
     } else {
-        return (float)(_Float16)v;
+        return (float)to_f16(v);
     }
 }
 
@@ -230,6 +241,56 @@ __device__ __forceinline__ float seg_max(float v) {
     return v;
 }
 
+// ---- rotate-half partner exchange -----------------------------------------
+//
+// A row's chunk j (j < hv) pairs with chunk j + hv, hv = rot/2 / Vec.  With
+// chunks in natural lane order the partner sits hv lanes away: inside one
+// 16-lane DPP row for hv <= 8 (row_shl / row_shr by hv), one row away for
+// hv == 16 (v_permlane16_swap) and half a wave away for hv == 32
+// (v_permlane32_swap).  `is_a` marks the lanes holding the first half.
+template <int HV>
+__device__ __forceinline__ uint32_t partner_dpp(uint32_t v, bool is_a) {
+    const uint32_t from_right = dpp_u<0x100 + HV>(v);   // row_shl:HV -> lane i + HV
+    const uint32_t from_left = dpp_u<0x110 + HV>(v);    // row_shr:HV -> lane i - HV
+    return is_a ? from_right : from_left;
+}
+
+__device__ __forceinline__ u32x4 rot_partner(u32x4 v, int hv, bool is_a) {
+    u32x4 r;
+    switch (hv) {
+#define MBT_PARTNER_CASE(H)                                                  \
+    case H:                                                                  \
+        for (int d = 0; d < 4; ++d) r[d] = partner_dpp<H>(v[d], is_a);      \
+        break;
+    MBT_PARTNER_CASE(1) MBT_PARTNER_CASE(2) MBT_PARTNER_CASE(3) MBT_PARTNER_CASE(4)
+    MBT_PARTNER_CASE(5) MBT_PARTNER_CASE(6) MBT_PARTNER_CASE(7) MBT_PARTNER_CASE(8)
+#undef MBT_PARTNER_CASE
+    case 16:
+        for (int d = 0; d < 4; ++d) {
+            auto w = __builtin_amdgcn_permlane16_swap(v[d], v[d], false, false);
+            r[d] = is_a ? w[1] : w[0];          // even row takes the odd row and back
+        }
+        break;
+    default:                                    // 32
+        for (int d = 0; d < 4; ++d) {
+            auto w = __builtin_amdgcn_permlane32_swap(v[d], v[d], false, false);
+            r[d] = is_a ? w[1] : w[0];          // low half takes the high half and back
+        }
+        break;
+    }
+    return r;
+}
+
+// Rotation of one pair exactly as the operation is written: two rounded
+// products and one rounded sum, never contracted into an FMA, so every
+// route (fused prologue, standalone rotation) rounds identically.
+__device__ __forceinline__ float rot_mac(float own, float c, float other, float s) {
+#pragma clang fp contract(off)
+    const float p = own * c;
+    const float q = other * s;
+    return p + q;
+}
+
 // XCD-aware block renumbering.  MI355X dispatches workgroup b to XCD b % 8;
 // XCD x therefore runs hardware blocks x, x + 8, x + 16, ...  Map them to the
 // contiguous logical range [x q + min(x, r), ... + count(x)), q = nb / 8,
@@ -239,6 +300,25 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb) {
     const uint32_t x = b & 7u, slot = b >> 3;
     const uint32_t q = nb >> 3, r = nb & 7u;
     return x * q + (x < r ? x : r) + slot;
+}
+
+// Sum of squares of one 16-byte chunk, as an explicit FMA chain in element
+// order.  Every kernel forms a row's sum the same way -- per-chunk chains,
+// then a balanced tree over the chunk index (DPP and lane swaps in a wave,
+// chunk groups combined pairwise) -- so the result does not depend on the
+// launch shape, the alignment or which entry point computed it.
+template <int DT>
+__device__ __forceinline__ float chunk_sumsq(const float* f) {
+    constexpr int V = Vec<DT>::n;
+    float p = f[0] * f[0];
+#pragma unroll
+    for (int i = 1; i < V; ++i) p = __builtin_fmaf(f[i], f[i], p);
+    return p;
+}
+
+// inv = 1 / sqrt(ss / n + eps) with the same rounding everywhere.
+__device__ __forceinline__ float inv_rms(float ss, float inv_n, float eps) {
+    return __builtin_amdgcn_rsqf(__builtin_fmaf(ss, inv_n, eps));
 }
 
 // Wave-uniform value as a scalar register.

@@ -58,7 +58,19 @@ struct ActArgs {
     int mode;             // ActOut
 };
 
+struct RopeArgs {
+    void* q;
+    void* k;
+    const float* cos_sin;
+    int64_t max_pos;
+    const int64_t* pos;
+    int32_t Q, K;
+    int64_t T;
+    int32_t head_dim, rot_dim, layout, dtype;
+};
+
 hipError_t launch_qknorm_rope(const QkArgs& a, hipStream_t s);
+hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s);
 hipError_t launch_gated_act(const ActArgs& a, hipStream_t s);
 hipError_t launch_quantize_fp8(const float* x, uint8_t* y, int64_t n, float inv_scale,

@@ -22,13 +22,18 @@
 //    flattened token-major), so a single set of norm weights sits in its
 //    registers and the rows it streams are contiguous in memory.  Each lane
 //    finds its row's token with a float reciprocal and one correction.
-//  * The sum of squares reduces inside the G-lane segment with DPP (and the
-//    gfx950 permlane swaps past 16 lanes); no LDS, no barrier.  The
-//    normalised value stays in registers between the norm and the rotation,
-//    so in-place calls are safe.
-//  * Rotate-half pairs chunk j with chunk j + rot/2 / Vec; lanes 2j and
-//    2j + 1 of a row hold that pair, so the partner arrives with one DPP quad
-//    permute per dword.  Interleaved pairs are lane-local.
+//  * The sum of squares is a fixed tree: an FMA chain inside each chunk, then
+//    a balanced tree over the chunk index -- DPP inside the G-lane segment
+//    (gfx950 permlane swaps past 16 lanes), chunk groups combined pairwise.
+//    C = 1 and C = 4 therefore give identical bits, so the result does not
+//    depend on the batch width, and the standalone norm and rotation entry
+//    points reproduce the fused op exactly.  No LDS reduction, no barrier:
+//    the normalised value stays in registers between norm and rotation, so
+//    in-place calls are safe.
+//  * Chunks sit in natural order; the rotate-half partner of chunk j
+//    (j + rot/2 / Vec) arrives by DPP row shift (<= 8 lanes away) or a
+//    permlane swap (16 / 32 lanes).  Interleaved pairs are lane-local.  Each
+//    pair is rotated as written -- two rounded products, one rounded sum.
 //  * q / k chunks are streamed with nontemporal loads and stores; weights,
 //    positions and cos/sin rows use ordinary cached loads.
 //  * Workgroups are renumbered so each of the 8 XCDs (dispatched round-robin)
@@ -69,8 +74,9 @@ struct QkParams {
 // Vector kernel.  DT: dtype; G: lanes per head-row; C: chunks per lane
 // (G * C * Vec<DT> = D); LAYOUT: rotary pairing.  Requires 16-byte aligned
 // q / k / w tensors, every rotated chunk inside chunk group 0, rows of each
-// tensor below 2^24, and for rotate-half rot/2 a multiple of Vec<DT> with a
-// 16-byte aligned cos/sin cache (interleaved reads its run element-wise).
+// tensor below 2^24, and for rotate-half rot/2 = hv * Vec<DT> with hv in
+// 1..8, 16 or 32 and a 16-byte aligned cos/sin cache (interleaved reads its
+// run element-wise).
 template <int DT, int G, int C, int LAYOUT>
 __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
     constexpr int V = Vec<DT>::n;
@@ -97,26 +103,16 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
     const int64_t row = row0 + lane / G;
     const bool live = row < nrows;
     const int half = p.rot >> 1;
-
-    // chunk of group 0 held by this lane, and its rotation role
-    int c0 = j;
-    bool is_a = false, is_b = false;
-    if constexpr (LAYOUT == 0) {
-        const int hv = half / V;
-        if (j < 2 * hv) {
-            is_a = (j & 1) == 0;
-            is_b = !is_a;
-            c0 = is_a ? (j >> 1) : hv + (j >> 1);
-        }
-    }
-    auto chunk = [&](int k) { return k == 0 ? c0 : k * G + j; };
+    const int hv = half / V;                                // rotate-half: chunks per half
+    const bool is_a = LAYOUT == 0 && j < hv;
+    const bool is_b = LAYOUT == 0 && j >= hv && j < 2 * hv;
 
     // ---- issue every independent load before any arithmetic ----
     const char* rsrc = src + row * (int64_t)p.D * EB;
     u32x4 x[C];
 #pragma unroll
     for (int k = 0; k < C; ++k)
-        x[k] = live ? ld16_nt(rsrc + chunk(k) * 16) : u32x4{0u, 0u, 0u, 0u};
+        x[k] = live ? ld16_nt(rsrc + (k * G + j) * 16) : u32x4{0u, 0u, 0u, 0u};
     // token of the row: float reciprocal, then one correction each way
     const uint32_t r32 = live ? (uint32_t)row : 0u;
     int32_t t = (int32_t)((float)r32 * inv_heads);
@@ -132,7 +128,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
         }
         __syncthreads();                                   // x loads already in flight
     } else {
-        unpack<DT>(wave_live ? ld16(wp + c0 * 16) : u32x4{0u, 0u, 0u, 0u}, wreg);
+        unpack<DT>(wave_live ? ld16(wp + j * 16) : u32x4{0u, 0u, 0u, 0u}, wreg);
 #pragma unroll
         for (int i = 0; i < V; ++i) wreg[i] += p.delta;
     }
@@ -143,7 +139,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
     if constexpr (LAYOUT == 0) {
         lane_rot = rotate && (is_a || is_b);
         if (lane_rot) {
-            const int j0 = (j >> 1) * V;                    // first pair index
+            const int j0 = (is_a ? j : j - hv) * V;         // first pair index
             const float* crow = p.cos_sin + ppos * (int64_t)p.rot;
 #pragma unroll
             for (int i = 0; i < V; i += 4) {
@@ -158,7 +154,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
             }
         }
     } else {
-        const int j0 = c0 * (V / 2);                        // first pair index
+        const int j0 = j * (V / 2);                         // first pair index
         lane_rot = rotate && (j0 < half);
         if (lane_rot) {
             const float* crow = p.cos_sin + ppos * (int64_t)p.rot;
@@ -173,17 +169,21 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
         }
     }
 
-    // ---- norm, round, rotate (group 0 only), store ----
-    float ss = 0.0f;
+    // ---- sum of squares: chunk chains, G-lane tree, groups pairwise ----
+    float part[C];
 #pragma unroll
     for (int k = 0; k < C; ++k) {
         float f[V];
         unpack<DT>(x[k], f);
-#pragma unroll
-        for (int i = 0; i < V; ++i) ss += f[i] * f[i];
+        part[k] = seg_sum<G>(chunk_sumsq<DT>(f));
     }
-    ss = seg_sum<G>(ss);
-    const float inv = rsqrt_hw(ss * p.inv_D + p.eps);
+    float ss;
+    if constexpr (C == 1) ss = part[0];
+    else if constexpr (C == 2) ss = part[0] + part[1];
+    else ss = (part[0] + part[1]) + (part[2] + part[3]);
+    const float inv = inv_rms(ss, p.inv_D, p.eps);
+
+    // ---- normalise, round, rotate (group 0 only), store ----
     char* rdst = dst + row * (int64_t)p.D * EB;
     const float* wrow = wsh[(C >= 2 && !is_q) ? 1 : 0];
 #pragma unroll
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
         float f[V], n[V];
         unpack<DT>(x[k], f);                                // decoded again: fewer live VGPRs
         if constexpr (C >= 2) {
-            const float* wk = wrow + chunk(k) * V;
+            const float* wk = wrow + (k * G + j) * V;
 #pragma unroll
             for (int i = 0; i < V; ++i) n[i] = (f[i] * inv) * wk[i];
         } else {
@@ -201,15 +201,13 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
         u32x4 out = pack<DT>(n);                            // R(n): the rounded value
         if (k == 0) {
             if constexpr (LAYOUT == 0) {
-                u32x4 pb;                                   // partner: neighbouring lane
-#pragma unroll
-                for (int d = 0; d < 4; ++d) pb[d] = dpp_u<kDppQuadXor1>(out[d]);
+                const u32x4 pb = rot_partner(out, hv, is_a);
                 if (lane_rot) {
                     float a[V], b[V], o[V];
                     unpack<DT>(out, a);
                     unpack<DT>(pb, b);
 #pragma unroll
-                    for (int i = 0; i < V; ++i) o[i] = a[i] * cs_c[i] + b[i] * cs_s[i];
+                    for (int i = 0; i < V; ++i) o[i] = rot_mac(a[i], cs_c[i], b[i], cs_s[i]);
                     out = pack<DT>(o);
                 }
             } else {
@@ -218,23 +216,26 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
                     unpack<DT>(out, a);
 #pragma unroll
                     for (int i = 0; i < V / 2; ++i) {
-                        o[2 * i] = a[2 * i] * cs_c[i] - a[2 * i + 1] * cs_s[i];
-                        o[2 * i + 1] = a[2 * i + 1] * cs_c[i] + a[2 * i] * cs_s[i];
+                        o[2 * i] = rot_mac(a[2 * i], cs_c[i], a[2 * i + 1], -cs_s[i]);
+                        o[2 * i + 1] = rot_mac(a[2 * i + 1], cs_c[i], a[2 * i], cs_s[i]);
                     }
                     out = pack<DT>(o);
                 }
             }
         }
-        if (live) st16_nt(rdst + chunk(k) * 16, out);
+        if (live) st16_nt(rdst + (k * G + j) * 16, out);
     }
 }
 
 // Scalar kernel: any D <= 512, any even rot, element-aligned pointers.  One
-// wave per head-row (4 rows per 256-thread block); lane i owns elements
-// i, i + 64, ...; the rounded normalised row is staged in LDS so each lane
-// can read its rotation partner.
+// wave per head-row (4 rows per 256-thread block).  Lane c owns chunk c
+// (Vec<DT> consecutive elements; lane c + 64 too for fp32 rows past 256), so
+// the sum of squares follows the vector kernels' tree (zero lanes add
+// nothing); the rounded normalised row is staged in LDS for the rotation.
 template <int DT>
 __global__ __launch_bounds__(256) void qknorm_rope_scalar(QkParams p) {
+    constexpr int V = Vec<DT>::n;
+    constexpr int CPL = (512 / V + kWave - 1) / kWave;      // chunks per lane
     __shared__ float stage[4][512];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + w;
@@ -249,22 +250,29 @@ __global__ __launch_bounds__(256) void qknorm_rope_scalar(QkParams p) {
     const void* wp = is_q ? p.w_q : p.w_k;
     const int64_t base = is_q ? (t * p.Q + h) * (int64_t)p.D
                               : (t * p.K + (h - p.Q)) * (int64_t)p.D;
-    constexpr int MAXE = 512 / kWave;
-    float f[MAXE];
+    float f[CPL][V];
     float ss = 0.0f;
 #pragma unroll
-    for (int k = 0; k < MAXE; ++k) {
-        const int i = lane + k * kWave;
-        f[k] = (live && i < p.D) ? ld_elt<DT>(src, base + i) : 0.0f;
-        ss += f[k] * f[k];
-    }
-    ss = seg_sum<64>(ss);
-    const float inv = rsqrt_hw(ss * p.inv_D + p.eps);
+    for (int k = 0; k < CPL; ++k) {
+        const int c = lane + k * kWave;
 #pragma unroll
-    for (int k = 0; k < MAXE; ++k) {
-        const int i = lane + k * kWave;
-        if (live && i < p.D)
-            stage[w][i] = round_trip<DT>((f[k] * inv) * (ld_elt<DT>(wp, i) + p.delta));
+        for (int i = 0; i < V; ++i) {
+            const int e = c * V + i;
+            f[k][i] = (live && e < p.D) ? ld_elt<DT>(src, base + e) : 0.0f;
+        }
+        // 64-chunk groups reduce on their own, then add: the canonical tree
+        const float part = seg_sum<64>(chunk_sumsq<DT>(f[k]));
+        ss = (k == 0) ? part : ss + part;
+    }
+    const float inv = inv_rms(ss, p.inv_D, p.eps);
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int e = (lane + k * kWave) * V + i;
+            if (live && e < p.D)
+                stage[w][e] = round_trip<DT>((f[k][i] * inv) * (ld_elt<DT>(wp, e) + p.delta));
+        }
     }
     __syncthreads();
     if (!live) return;
@@ -272,27 +280,24 @@ __global__ __launch_bounds__(256) void qknorm_rope_scalar(QkParams p) {
     const bool rotate = (ppos >= 0) && (ppos < p.max_pos) && (p.rot > 0);
     const int half = p.rot >> 1;
     const float* cs = p.cos_sin + (rotate ? ppos * (int64_t)p.rot : 0);
-#pragma unroll
-    for (int k = 0; k < MAXE; ++k) {
-        const int i = lane + k * kWave;
-        if (i >= p.D) continue;
-        float o = stage[w][i];
-        if (rotate && i < p.rot) {
-            int j, a, b;
+    for (int e = lane; e < p.D; e += kWave) {
+        float o = stage[w][e];
+        if (rotate && e < p.rot) {
+            int jj, a, b;
             if (p.layout == 0) {                     // rotate-half
-                j = (i < half) ? i : i - half;
-                a = j;
-                b = j + half;
+                jj = (e < half) ? e : e - half;
+                a = jj;
+                b = jj + half;
             } else {                                 // interleaved
-                j = i >> 1;
-                a = 2 * j;
-                b = 2 * j + 1;
+                jj = e >> 1;
+                a = 2 * jj;
+                b = 2 * jj + 1;
             }
-            const float c = cs[j], s = cs[half + j];
-            o = (i == a) ? (stage[w][a] * c - stage[w][b] * s)
-                         : (stage[w][b] * c + stage[w][a] * s);
+            const float c = cs[jj], s = cs[half + jj];
+            o = (e == a) ? rot_mac(stage[w][a], c, stage[w][b], -s)
+                         : rot_mac(stage[w][b], c, stage[w][a], s);
         }
-        st_elt<DT>(dst, base + i, o);
+        st_elt<DT>(dst, base + e, o);
     }
 }
 
@@ -355,12 +360,10 @@ hipError_t launch_dt(const QkArgs& a, hipStream_t s) {
     bool vec = (a.head_dim % V == 0) && (L == 4 || L == 8 || L == 16 || L == 32 || L == 64);
     vec = vec && aligned16(a.q_in) && aligned16(a.k_in) && aligned16(a.q_out) &&
           aligned16(a.k_out) && aligned16(a.w_q) && aligned16(a.w_k);
-    if (a.rot_dim > 0 && a.max_pos > 0) {
-        if (a.layout == 0)
-            vec = vec && ((a.rot_dim / 2) % V == 0) && aligned16(a.cos_sin) &&
-                  (a.rot_dim % 4 == 0);
-        else
-            vec = vec && aligned16(a.cos_sin);
+    if (a.rot_dim > 0 && a.max_pos > 0 && a.layout == 0) {
+        const int hv = (a.rot_dim / 2) / V;
+        vec = vec && ((a.rot_dim / 2) % V == 0) && aligned16(a.cos_sin) &&
+              ((hv >= 1 && hv <= 8) || hv == 16 || hv == 32);
     }
     const int QK = a.Q + a.K;
     const int64_t rows = a.T * (int64_t)QK;

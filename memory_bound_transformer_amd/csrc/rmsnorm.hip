@@ -12,14 +12,22 @@
 // into a device scalar and writes nothing else.
 //
 // MI355X design: the row stays in registers from load to store (the single
-// read pass the FlashRT notes credit for their norm speed-up), so HBM sees exactly
-// one read of x, r, w and one write of r and the output.  A row of H
-// elements is spread over WPR waves of NCH 16-byte chunks per lane; the
-// fp32 sum of squares reduces inside each wave with DPP and, only when
-// WPR > 1, across waves through LDS with one barrier.  With WPR == 1 a
-// 256-thread block carries four independent rows and no barrier at all.
-// Odd widths and unaligned pointers take a two-pass scalar kernel with the
-// same arithmetic.
+// read pass the FlashRT notes credit for their norm speed-up), so HBM sees
+// exactly one read of x, r, w and one write of r and the output.
+//
+//  * Rows of at most 64 16-byte chunks (e.g. a 256-wide head, or H <= 512
+//    bf16) are G-lane segments of a wave, several rows per wave, one chunk
+//    per lane: no barrier.
+//  * Wider rows are spread over WPR waves of NCH chunks per lane (one chunk
+//    per lane at decode widths, measured best); each 64-chunk group reduces
+//    inside a wave with DPP and the group sums combine through LDS.
+//  * The sum of squares is the same fixed tree in every kernel: an FMA chain
+//    inside each chunk, then a balanced tree over the chunk index padded with
+//    zeros to a power of two.  The result therefore does not depend on the
+//    launch shape or the alignment, and a row normalised here equals the
+//    fused QK-norm prologue's normalisation of the same head bit for bit.
+//  * Odd widths and unaligned pointers take a two-pass scalar kernel with
+//    the same tree.
 
 #include <stdlib.h>
 
@@ -40,8 +48,8 @@ struct NormParams {
     int64_t T;
     int32_t H;
     float eps, inv_H, delta;
-    int32_t wpr;   // waves per row
-    int32_t rpb;   // rows per block
+    int32_t wpr;   // wide kernel: waves per row
+    int32_t rpb;   // wide kernel: rows per block
 };
 
 template <int DT, int MODE>
@@ -70,19 +78,96 @@ __device__ __forceinline__ void emit(const NormParams& p, int64_t row, int64_t e
     }
 }
 
-// Vector kernel: H a multiple of Vec<DT>, 16-byte aligned x / residual / w /
-// x_out, and (FP8) y8 aligned to its store width.
+// Balanced tree over g[0 .. n-1] padded with zeros to a power of two (a
+// missing right operand adds nothing).  Leaves the total in g[0].  Padding to
+// a larger power of two only adds +0 at the top, so N may exceed the count of
+// non-zero entries.
+template <int N>
+__device__ __forceinline__ float fixed_tree(float* g) {
+#pragma unroll
+    for (int w = 1; w < N; w <<= 1)
+#pragma unroll
+        for (int i = 0; i + w < N; i += 2 * w) g[i] += g[i + w];
+    return g[0];
+}
+__device__ __forceinline__ float group_tree(float* g, int n) {
+    for (int w = 1; w < n; w <<= 1)
+        for (int i = 0; i + w < n; i += 2 * w) g[i] += g[i + w];
+    return g[0];
+}
+
+// s = R(x + r) for one chunk (fp32 add of the decoded operands, one rounding),
+// returned packed; x alone without a residual.
+template <int DT>
+__device__ __forceinline__ u32x4 residual_sum(u32x4 xv, u32x4 rv, bool has_res) {
+    constexpr int V = Vec<DT>::n;
+    if (!has_res) return xv;
+    float a[V], b[V];
+    unpack<DT>(xv, a);
+    unpack<DT>(rv, b);
+#pragma unroll
+    for (int i = 0; i < V; ++i) a[i] += b[i];
+    return pack<DT>(a);
+}
+
+// Rows of at most G chunks (G in 4..64): G-lane segments, 64 / G rows per wave,
+// four waves per block, one chunk per lane.
+template <int DT, int G, int MODE>
+__global__ __launch_bounds__(256) void rmsnorm_small(NormParams p) {
+    constexpr int V = Vec<DT>::n;
+    constexpr int EB = EltBytes<DT>::n;
+    constexpr int RPW = kWave / G;
+    const int lane = threadIdx.x & 63;
+    const int j = lane % G;
+    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / G;
+    const int chunks = p.H / V;
+    const bool have = row < p.T && j < chunks;
+    const bool has_res = p.residual != nullptr;
+    const int64_t off = (row * p.H + (int64_t)j * V) * EB;
+    u32x4 xv = u32x4{0u, 0u, 0u, 0u}, rv = xv, wv = xv;
+    if (have) {
+        xv = ld16_nt((const char*)p.x + off);
+        if (has_res) rv = ld16_nt((const char*)p.residual + off);
+        wv = ld16((const char*)p.w + (int64_t)j * V * EB);
+    }
+    const u32x4 sv = residual_sum<DT>(xv, rv, has_res);
+    float s[V];
+    unpack<DT>(sv, s);
+    const float ss = seg_sum<G>(have ? chunk_sumsq<DT>(s) : 0.0f);
+    const float inv = inv_rms(ss, p.inv_H, p.eps);
+    float amax_acc = 0.0f;
+    if (have) {
+        if (has_res && MODE != kNormAmax) st16_nt((char*)p.residual + off, sv);
+        float wf[V], y[V];
+        unpack<DT>(wv, wf);
+#pragma unroll
+        for (int i = 0; i < V; ++i) y[i] = (s[i] * inv) * (wf[i] + p.delta);
+        emit<DT, MODE>(p, row, (int64_t)j * V, y, amax_acc);
+    }
+    if constexpr (MODE == kNormAmax) {
+        amax_acc = seg_max<64>(amax_acc);
+        if (lane == 0) atomic_max_nonneg(p.amax, amax_acc);
+    }
+}
+
+// Rows of more than 64 chunks: WPR waves per row (RPB rows per block when
+// WPR divides 4), NCH chunks per lane.  Chunk ch = k * 64 * WPR + wave * 64
+// + lane, so chunk group g = k * WPR + wave holds 64 consecutive chunks.
+constexpr int kMaxNch = 6;
+constexpr int kMaxGroups = kMaxNch * 16;
+
 template <int DT, int NCH, int MODE>
 __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
     constexpr int V = Vec<DT>::n;
     constexpr int EB = EltBytes<DT>::n;
-    __shared__ float part[16];
+    __shared__ float gsum[4][kMaxGroups];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wpr = p.wpr;
     const int rib = wave / wpr, wir = wave % wpr;
     const int64_t row = (int64_t)blockIdx.x * p.rpb + rib;
     const bool live = row < p.T;
     const int chunks = p.H / V;
+    const int ngroups = (chunks + kWave - 1) / kWave;
     const int stride = kWave * wpr;
     const bool has_res = p.residual != nullptr;
 
@@ -101,31 +186,34 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
             wv[k] = ld16((const char*)p.w + (int64_t)ch * V * EB);
         }
     }
-    // s = R(x + r): fp32 add of the decoded operands, one rounding.
-    float ss = 0.0f;
+    // group sums: chunk chains, then the 64-lane tree of each group
+    float gs[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-        if (has_res) {
-            float a[V], b[V];
-            unpack<DT>(xv[k], a);
-            unpack<DT>(rv[k], b);
-#pragma unroll
-            for (int i = 0; i < V; ++i) a[i] += b[i];
-            xv[k] = pack<DT>(a);          // xv now holds the rounded sum s
-        }
+        const int ch = k * stride + wir * kWave + lane;
+        xv[k] = residual_sum<DT>(xv[k], rv[k], has_res);   // xv now holds s = R(x + r)
         float s[V];
         unpack<DT>(xv[k], s);
+        gs[k] = seg_sum<64>((live && ch < chunks) ? chunk_sumsq<DT>(s) : 0.0f);
+    }
+    float ss;
+    if (wpr == 1) {
+        ss = fixed_tree<NCH>(gs);                      // groups past the row are 0
+    } else {
 #pragma unroll
-        for (int i = 0; i < V; ++i) ss += s[i] * s[i];
-    }
-    ss = seg_sum<64>(ss);
-    if (wpr > 1) {
-        if (lane == 0) part[wave] = ss;
+        for (int k = 0; k < NCH; ++k) {
+            const int g = k * wpr + wir;
+            if (lane == 0 && g < ngroups) gsum[rib][g] = gs[k];
+        }
         __syncthreads();
-        ss = 0.0f;
-        for (int i = 0; i < wpr; ++i) ss += part[rib * wpr + i];
+        // group g in lane g (and g - 64): the 64-lane tree is the balanced
+        // tree over the padded group slots
+        const float lo = lane < ngroups ? gsum[rib][lane] : 0.0f;
+        const float hi = lane + kWave < ngroups ? gsum[rib][lane + kWave] : 0.0f;
+        ss = seg_sum<64>(lo);
+        if (ngroups > kWave) ss += seg_sum<64>(hi);
     }
-    const float inv = rsqrt_hw(ss * p.inv_H + p.eps);
+    const float inv = inv_rms(ss, p.inv_H, p.eps);
     float amax_acc = 0.0f;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
@@ -147,28 +235,53 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
     }
 }
 
-// Scalar kernel: any H and element-aligned pointers.  One 256-thread block
-// per row; the first pass forms s and its sum of squares, the second pass
-// recomputes s from the untouched x and r and writes everything, so each
-// element is read before it is overwritten by the same thread.
+// Scalar kernel: any H and element-aligned pointers; one 256-thread block per
+// row.  Pass 1: wave (g % 4) forms group g's chunk chains (Vec<DT> elements
+// each, scalar loads) and its 64-lane tree; the group sums meet in LDS (up to
+// kScalarGroups at a time, tree-summed; further blocks of groups are added in
+// order).  Pass 2 recomputes s from the untouched x and r and writes, so each
+// element is read before the same thread overwrites it.
+constexpr int kScalarGroups = 1024;
+
 template <int DT, int MODE>
 __global__ __launch_bounds__(256) void rmsnorm_scalar(NormParams p) {
-    __shared__ float part[4];
+    constexpr int V = Vec<DT>::n;
+    __shared__ float gsum[kScalarGroups];
     const int64_t row = blockIdx.x;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const bool has_res = p.residual != nullptr;
     const int64_t base = row * p.H;
+    const int chunks = (p.H + V - 1) / V;
+    const int ngroups = (chunks + kWave - 1) / kWave;
     float ss = 0.0f;
-    for (int i = threadIdx.x; i < p.H; i += 256) {
-        float s = ld_elt<DT>(p.x, base + i);
-        if (has_res) s = round_trip<DT>(s + ld_elt<DT>(p.residual, base + i));
-        ss += s * s;
+    for (int g0 = 0; g0 < ngroups; g0 += kScalarGroups) {
+        const int gn = (ngroups - g0) < kScalarGroups ? (ngroups - g0) : kScalarGroups;
+        for (int gi = wave; gi < gn; gi += 4) {
+            const int c = (g0 + gi) * kWave + lane;
+            float s[V];
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const int64_t e = (int64_t)c * V + i;
+                float v = 0.0f;
+                if (e < p.H) {
+                    v = ld_elt<DT>(p.x, base + e);
+                    if (has_res) v = round_trip<DT>(v + ld_elt<DT>(p.residual, base + e));
+                }
+                s[i] = v;
+            }
+            const float gsq = seg_sum<64>(chunk_sumsq<DT>(s));
+            if (lane == 0) gsum[gi] = gsq;
+        }
+        __syncthreads();
+        float blk = 0.0f;
+        if (threadIdx.x == 0) blk = group_tree(gsum, gn);
+        __syncthreads();
+        if (threadIdx.x == 0) gsum[0] = blk;
+        __syncthreads();
+        ss = (g0 == 0) ? gsum[0] : ss + gsum[0];
+        __syncthreads();
     }
-    ss = seg_sum<64>(ss);
-    if (lane == 0) part[wave] = ss;
-    __syncthreads();
-    ss = part[0] + part[1] + part[2] + part[3];
-    const float inv = rsqrt_hw(ss * p.inv_H + p.eps);
+    const float inv = inv_rms(ss, p.inv_H, p.eps);
     float amax_acc = 0.0f;
     for (int i = threadIdx.x; i < p.H; i += 256) {
         float s = ld_elt<DT>(p.x, base + i);
@@ -187,14 +300,11 @@ __global__ __launch_bounds__(256) void rmsnorm_scalar(NormParams p) {
     }
 }
 
-// Launch shape: waves per row for a row of `chunks` 16-byte chunks.
-// Decode widths (few rows) spread each row over as many waves as it has
-// 64-chunk groups, one chunk per lane (the shortest per-wave latency);
-// prefill widths keep a row in as few waves as kMaxNch chunks per lane
-// allow (more chunks per lane would spill under the 1024-thread launch
-// bound, which caps a wave at 128 VGPRs).
-constexpr int kMaxNch = 6;
-
+// Launch shape of the wide kernel: waves per row for a row of `chunks`
+// 16-byte chunks.  One chunk per lane (as many waves as 64-chunk groups, the
+// shortest per-wave latency) unless there are rows enough to fill the chip,
+// then as few waves as kMaxNch chunks per lane allow (more would spill under
+// the 1024-thread launch bound, which caps a wave at 128 VGPRs).
 int env_int(const char* name, int dflt) {
     const char* e = getenv(name);
     return e ? atoi(e) : dflt;
@@ -203,12 +313,12 @@ int env_int(const char* name, int dflt) {
 int pick_wpr(int64_t T, int chunks) {
     static const int forced = env_int("MBT_NORM_WPR", 0);
     static const int wide_rows = env_int("MBT_NORM_WIDE_CHUNKS", 32768);
-    const int per64 = (chunks + kWave - 1) / kWave;    // chunks per lane at WPR 1
+    const int per64 = (chunks + kWave - 1) / kWave;    // chunk groups
     const int min_wpr = (per64 + kMaxNch - 1) / kMaxNch;
     int wpr;
     if (forced > 0) wpr = forced;
-    else if (T * per64 >= wide_rows) wpr = min_wpr;    // enough rows to fill the chip
-    else wpr = per64;                                   // one chunk per lane
+    else if (T * per64 >= wide_rows) wpr = min_wpr;
+    else wpr = per64;
     if (wpr < min_wpr) wpr = min_wpr;
     if (wpr > 16) wpr = 16;
     if (wpr < 1) wpr = 1;
@@ -224,6 +334,16 @@ hipError_t launch_vec_n(const NormParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int DT, int MODE, int G>
+hipError_t launch_small(const NormParams& p, hipStream_t s) {
+    constexpr int RPB = 4 * (kWave / G);                 // rows per 256-thread block
+    const int64_t blocks = (p.T + RPB - 1) / RPB;
+    if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((rmsnorm_small<DT, G, MODE>), dim3((uint32_t)blocks), dim3(256), 0, s,
+                       p);
+    return hipGetLastError();
+}
+
 template <int DT, int MODE>
 hipError_t launch_mode(const NormArgs& a, hipStream_t s) {
     constexpr int V = Vec<DT>::n;
@@ -234,11 +354,17 @@ hipError_t launch_mode(const NormArgs& a, hipStream_t s) {
 
     const int chunks = a.H / V;
     bool vec = (a.H % V == 0) && chunks <= kMaxNch * kWave * 16 && aligned16(a.x) &&
-               aligned16(a.w) &&
-               (a.residual == nullptr || aligned16(a.residual));
+               aligned16(a.w) && (a.residual == nullptr || aligned16(a.residual));
     if (MODE == kNormInPlace) vec = vec && aligned16(a.x_out);
     if (MODE == kNormFp8)
         vec = vec && ((reinterpret_cast<uintptr_t>(a.y8) & (V == 8 ? 7u : 3u)) == 0);
+    if (vec && chunks <= kWave) {
+        if (chunks <= 4) return launch_small<DT, MODE, 4>(p, s);
+        if (chunks <= 8) return launch_small<DT, MODE, 8>(p, s);
+        if (chunks <= 16) return launch_small<DT, MODE, 16>(p, s);
+        if (chunks <= 32) return launch_small<DT, MODE, 32>(p, s);
+        return launch_small<DT, MODE, 64>(p, s);
+    }
     if (vec) {
         p.wpr = pick_wpr(a.T, chunks);
         p.rpb = (p.wpr <= 4 && 4 % p.wpr == 0) ? 4 / p.wpr : 1;

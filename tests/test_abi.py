@@ -35,6 +35,7 @@ def lib():
     sigs = {
         "mbt_qknorm_rope": [vp, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, i64, i32, i32, f32,
                             i32, i32, i32, vp],
+        "mbt_rope": [vp, vp, vp, i64, vp, i32, i32, i64, i32, i32, i32, i32, vp],
         "mbt_fused_add_rmsnorm": [vp, vp, vp, i64, i32, f32, i32, i32, vp],
         "mbt_fused_add_rmsnorm_fp8": [vp, vp, vp, vp, f32, i64, i32, f32, i32, i32, vp],
         "mbt_fused_add_rmsnorm_amax": [vp, vp, vp, vp, i64, i32, f32, i32, i32, vp],
@@ -55,7 +56,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), f"{n} declared in mbt.h but not exported"
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
@@ -174,3 +175,27 @@ def test_act_rejects(lib):
     assert q(A + 2, B, 16, 1.0, None) == ALIGN
     assert q(A, A + 8, 16, 1.0, None) == ALIAS
     assert q(None, None, 0, 1.0, None) == OK
+
+
+def test_rope_rejects(lib):
+    f = lib.mbt_rope
+    ok = dict(q=A, k=B, cs=CS, mp=4096, pos=POS, Q=16, K=2, T=8, D=256, rot=64, lay=0, dt=BF16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["k"], a["cs"], a["mp"], a["pos"], a["Q"], a["K"], a["T"], a["D"],
+                 a["rot"], a["lay"], a["dt"], None)
+    assert call(dt=5) == DTYPE
+    assert call(lay=3) == ENUM
+    assert call(Q=0, K=0) == SHAPE
+    assert call(rot=65) == SHAPE
+    assert call(D=600) == SHAPE
+    assert call(mp=-1) == SCALAR
+    assert call(pos=None) == NULLP
+    assert call(q=None) == NULLP
+    assert call(cs=None) == NULLP
+    assert call(q=A + 1) == ALIGN
+    assert call(k=A + 1024) == ALIAS            # k inside q
+    assert call(q=CS + 64) == ALIAS             # q over the cache
+    assert call(T=0, q=None, k=None, cs=None, pos=None) == OK

@@ -1,0 +1,168 @@
+"""Routes and invariances on the GPU.
+
+* the standalone rotation (mbt_rope) equals the oracle bit for bit: it gets
+  the same decoded inputs and rotates each pair as written;
+* the three-call split route -- RMSNorm of the q head-rows, of the k
+  head-rows (mbt_fused_add_rmsnorm, residual NULL), then mbt_rope -- equals
+  the fused prologue bit for bit (the property the ninfer PR states for its
+  fused op and the calls it replaces);
+* the fused prologue gives the same bits for a token whether it is launched
+  alone (decode launch shape) or inside a 2048-token batch (prefill launch
+  shape), and whether its tensors are 16-byte aligned (vector kernel) or not
+  (scalar kernel);
+* the residual RMSNorm gives the same bits for a row at any batch width and
+  alignment.
+"""
+import numpy as np
+import pytest
+import torch
+
+import compare as C
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def mbt():
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU is required for the gpu-marked tests")
+    import memory_bound_transformer_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def dev(bits, dtype, offset=0):
+    """Device copy of `bits`, optionally `offset` elements into a larger buffer."""
+    flat = np.concatenate([np.zeros(offset, bits.dtype), bits.ravel()])
+    return W.to_torch(flat, dtype, DEV)[offset:].view(bits.shape)
+
+
+def host(t, dtype):
+    torch.cuda.synchronize()
+    return W.from_torch(t, dtype)
+
+
+def _cell(**kw):
+    base = dict(name="route", config=93, cell=0, T=37, Q=6, K=2, D=256, rot=64, theta=1e7,
+                layout=W.ROTATE_HALF, dtype=W.BF16, weight_offset=1, w_mean=0.0, w_std=0.05,
+                x_std=2.0, max_pos=64, outside=((3, -1), (5, 64)))
+    base.update(kw)
+    return W.PrologueCell(**base)
+
+
+ROUTE_CELLS = [
+    _cell(name="bf16_d256_rot64", cell=1),
+    _cell(name="f16_d256_rot64", dtype=W.F16, cell=2),
+    _cell(name="f32_d256_rot64", dtype=W.F32, cell=3),
+    _cell(name="bf16_d128_full", D=128, rot=128, weight_offset=0, w_mean=1.0, cell=4),
+    _cell(name="bf16_d256_full_half", rot=256, cell=5),
+    _cell(name="bf16_d512_full_half", D=512, rot=512, cell=6),
+    _cell(name="bf16_d256_inter", rot=256, layout=W.INTERLEAVED, cell=7),
+    _cell(name="bf16_d256_inter_partial", rot=40, layout=W.INTERLEAVED, cell=8),
+    _cell(name="f32_d128_inter", dtype=W.F32, D=128, rot=128, layout=W.INTERLEAVED, cell=9),
+    _cell(name="bf16_d256_rot48_shift3", rot=48, cell=10),
+    _cell(name="bf16_d256_rot40_scalar", rot=40, cell=13),
+    _cell(name="bf16_d96_scalar", D=96, rot=32, cell=11),
+    _cell(name="bf16_prefill_24x4", T=2048, Q=24, K=4, positions="arange", max_pos=4096,
+          outside=(), cell=12),
+]
+
+
+@pytest.mark.parametrize("cell", ROUTE_CELLS, ids=lambda c: c.name)
+def test_rope_matches_oracle_bitwise(mbt, orc, cell):
+    i = cell.inputs()
+    dt = cell.dtype
+    q, k = dev(i["q"], dt), dev(i["k"], dt)
+    cs = torch.from_numpy(i["cos_sin"]).to(DEV)
+    pos = torch.from_numpy(i["pos"]).to(DEV)
+    mbt.rope(q, k, cs, pos, cell.rot, cell.layout)
+    C.check_bitwise(host(q, dt), orc.rope(i["q"], i["cos_sin"], i["pos"], cell.rot, cell.layout,
+                                          dt), label=f"{cell.name} q")
+    C.check_bitwise(host(k, dt), orc.rope(i["k"], i["cos_sin"], i["pos"], cell.rot, cell.layout,
+                                          dt), label=f"{cell.name} k")
+
+
+def fused(mbt, cell, i, offset=0):
+    dt = cell.dtype
+    qo, ko = mbt.qknorm_rope(dev(i["q"], dt, offset), dev(i["k"], dt, offset),
+                             dev(i["w_q"], dt, offset), dev(i["w_k"], dt, offset),
+                             torch.from_numpy(i["cos_sin"]).to(DEV),
+                             torch.from_numpy(i["pos"]).to(DEV), cell.rot, cell.eps,
+                             cell.weight_offset, cell.layout)
+    return host(qo, dt), host(ko, dt)
+
+
+@pytest.mark.parametrize("cell", ROUTE_CELLS, ids=lambda c: c.name)
+def test_split_route_equals_fused(mbt, cell):
+    i = cell.inputs()
+    dt = cell.dtype
+    fq, fk = fused(mbt, cell, i)
+    q, k = dev(i["q"], dt), dev(i["k"], dt)
+    mbt.fused_add_rmsnorm(q.view(-1, cell.D), None, dev(i["w_q"], dt), cell.eps,
+                          cell.weight_offset)
+    mbt.fused_add_rmsnorm(k.view(-1, cell.D), None, dev(i["w_k"], dt), cell.eps,
+                          cell.weight_offset)
+    mbt.rope(q, k, torch.from_numpy(i["cos_sin"]).to(DEV), torch.from_numpy(i["pos"]).to(DEV),
+             cell.rot, cell.layout)
+    C.check_bitwise(host(q, dt), fq, label=f"{cell.name} split q vs fused")
+    C.check_bitwise(host(k, dt), fk, label=f"{cell.name} split k vs fused")
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F16, W.F32])
+@pytest.mark.parametrize("QK", [(24, 4), (16, 2)])
+def test_prologue_batch_invariant(mbt, dtype, QK):
+    """A 2048-token launch (strided, 4 chunks per lane) and one-token launches
+    (1 chunk per lane) give the same bits for the same token."""
+    cell = _cell(name="batch", T=2048, Q=QK[0], K=QK[1], dtype=dtype, positions="arange",
+                 max_pos=4096, outside=(), cell=20 + dtype)
+    i = cell.inputs()
+    fq, fk = fused(mbt, cell, i)
+    for t in (0, 1, 777, 2047):
+        one = {k: (v[t:t + 1] if k in ("q", "k", "pos") else v) for k, v in i.items()}
+        c1 = _cell(name="one", T=1, Q=QK[0], K=QK[1], dtype=dtype, max_pos=4096, outside=())
+        oq, ok = fused(mbt, c1, one)
+        C.check_bitwise(oq[0], fq[t], label=f"token {t} q")
+        C.check_bitwise(ok[0], fk[t], label=f"token {t} k")
+
+
+@pytest.mark.parametrize("cell", [c for c in ROUTE_CELLS if c.D % 8 == 0],
+                         ids=lambda c: c.name)
+def test_prologue_alignment_invariant(mbt, cell):
+    """The scalar kernel (storage offset by one element) and the vector
+    kernel give the same bits."""
+    i = cell.inputs()
+    aq, ak = fused(mbt, cell, i)
+    uq, uk = fused(mbt, cell, i, offset=1)
+    C.check_bitwise(uq, aq, label=f"{cell.name} unaligned q")
+    C.check_bitwise(uk, ak, label=f"{cell.name} unaligned k")
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+@pytest.mark.parametrize("H", [256, 1024, 2560, 6144])
+def test_norm_shape_invariant(mbt, dtype, H):
+    """A row's output does not depend on how many rows share the launch (one
+    chunk per lane at small widths, up to six at large ones) or on alignment
+    (vector vs scalar kernel)."""
+    big_T = max(64, (1 << 16) // max(1, H * (4 if dtype == W.F32 else 2) // 1024))
+    c = W.NormCell(name="inv", config=94, cell=H, T=big_T, H=H, dtype=dtype, weight_offset=1,
+                   w_mean=0.0, w_std=0.05)
+    i = c.inputs()
+
+    def run(T, offset=0):
+        x, r = dev(i["x"][:T], dtype, offset), dev(i["residual"][:T], dtype, offset)
+        mbt.fused_add_rmsnorm(x, r, dev(i["w"], dtype, offset), c.eps, 1)
+        return host(x, dtype), host(r, dtype)
+
+    bx, br = run(big_T)
+    for T, off in ((1, 0), (7, 0), (7, 1)):
+        x, r = run(T, off)
+        C.check_bitwise(x, bx[:T], label=f"H={H} T={T} offset={off} x")
+        C.check_bitwise(r, br[:T], label=f"H={H} T={T} offset={off} residual")
