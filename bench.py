@@ -238,6 +238,68 @@ def prologue_cold_us(torch, mbt, W, cell, launches=2000):
     return us
 
 
+def route_us(torch, mbt, W, cell, cold, passes=5, samples=50, inner=32, launches=2000):
+    """The fused prologue against the split route it replaces -- RMSNorm of
+    the q head-rows, RMSNorm of the k head-rows (mbt_fused_add_rmsnorm with
+    residual NULL), then mbt_rope -- both in place, with a null arm: the
+    fused route is timed twice per pass, before and after the split route,
+    and a pass whose two fused timings differ by more than 1 % is dropped.
+    Returns medians over the kept passes (None if every pass was dropped).
+    Warm: a graph of `inner` calls on one buffer set; cold: graphs over a
+    ring of buffer sets larger than the Infinity Cache."""
+    dev = "cuda:0"
+    i = cell.inputs()
+    t = lambda b: W.to_torch(b, cell.dtype, dev)
+    wq, wk = t(i["w_q"]), t(i["w_k"])
+    cs = torch.from_numpy(i["cos_sin"]).to(dev)
+    pos = torch.from_numpy(i["pos"]).to(dev)
+    R = max(8, -(-RING_BYTES // cell.bytes_algorithmic())) if cold else 1
+    q0, k0 = t(i["q"]), t(i["k"])
+    ring = [(q0.clone(), k0.clone()) for _ in range(R)]
+
+    def fused(j):
+        q, k = ring[j % R]
+        mbt.qknorm_rope(q, k, wq, wk, cs, pos, cell.rot, cell.eps, cell.weight_offset,
+                        cell.layout, q_out=q, k_out=k)
+
+    def split(j):
+        q, k = ring[j % R]
+        mbt.fused_add_rmsnorm(q.view(-1, cell.D), None, wq, cell.eps, cell.weight_offset)
+        mbt.fused_add_rmsnorm(k.view(-1, cell.D), None, wk, cell.eps, cell.weight_offset)
+        mbt.rope(q, k, cs, pos, cell.rot, cell.layout)
+
+    n = R if cold else inner
+    g = {"fused": capture(torch, fused, n), "split": capture(torch, split, n)}
+    for gg in g.values():
+        for _ in range(3):
+            gg.replay()
+    reps = max(1, launches // n) if cold else 1
+
+    def one(name):
+        if cold:
+            return 1000.0 * timed_replays(torch, [g[name]] * reps) / (reps * n)
+        return median([1000.0 * timed_replays(torch, [g[name]]) / n for _ in range(samples)])
+
+    kept, dropped = [], 0
+    for _ in range(passes):
+        a = one("fused")
+        b = one("split")
+        c = one("fused")
+        if abs(a - c) > 0.01 * min(a, c):
+            dropped += 1
+            continue
+        kept.append((0.5 * (a + c), b, abs(a - c) / min(a, c)))
+    del ring, g
+    torch.cuda.empty_cache()
+    if not kept:
+        return {"T": cell.T, "QK": f"{cell.Q}x{cell.K}", "dropped": dropped}
+    fu = median([x[0] for x in kept])
+    sp = median([x[1] for x in kept])
+    return {"T": cell.T, "QK": f"{cell.Q}x{cell.K}", "fused_us": round(fu, 3),
+            "split_us": round(sp, 3), "split_over_fused": round(sp / fu, 3),
+            "null_arm_max_diff": round(max(x[2] for x in kept), 4), "dropped": dropped}
+
+
 def copy_ceiling_gbps(torch, nbytes, launches=1000):
     """torch's device copy of nbytes/2 -> nbytes/2 (nbytes of traffic), cold."""
     half = max(16, nbytes // 2)
@@ -259,8 +321,11 @@ def prefill_cell(W):
 
 def source_digest(kernel):
     h = hashlib.sha256()
-    for name in (KERNEL_SOURCES[kernel], "mbt_device.hpp"):
-        with open(os.path.join(ROOT, "memory_bound_transformer_amd", "csrc", name), "rb") as f:
+    pkg = os.path.join(ROOT, "memory_bound_transformer_amd")
+    # the compiler flags (build.py) shape the kernel as much as its source
+    for path in (os.path.join(pkg, "csrc", KERNEL_SOURCES[kernel]),
+                 os.path.join(pkg, "csrc", "mbt_device.hpp"), os.path.join(pkg, "build.py")):
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
@@ -412,6 +477,13 @@ def main():
                         "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
                         "tokens_per_s": round(c.T / us * 1e6, 1)})
         prologue["prefill_cold"] = pre
+        # fused vs split route (norm q rows, norm k rows, rope), in place
+        routes = {"warm": [route_us(torch, mbt, W, c, cold=False)
+                           for c in W.config2_cells() if c.T in (1, 8, 32, 128)],
+                  "cold": [route_us(torch, mbt, W, c, cold=True)
+                           for c in W.config3_cells()
+                           if c.dtype == W.BF16 and c.layout == W.ROTATE_HALF]}
+        prologue["routes"] = routes
         # the prefill launch the >= 70 % HBM target is set for
         big = prefill_cell(W)
         us = [x for x in pre if x["QK"] == f"{big.Q}x{big.K}" and x["T"] == big.T][0]["cold_us"]

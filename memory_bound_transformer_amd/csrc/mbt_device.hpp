@@ -244,40 +244,19 @@ __device__ __forceinline__ float seg_max(float v) {
 // ---- rotate-half partner exchange -----------------------------------------
 //
 // A row's chunk j (j < hv) pairs with chunk j + hv, hv = rot/2 / Vec.  With
-// chunks in natural lane order the partner sits hv lanes away: inside one
-// 16-lane DPP row for hv <= 8 (row_shl / row_shr by hv), one row away for
-// hv == 16 (v_permlane16_swap) and half a wave away for hv == 32
-// (v_permlane32_swap).  `is_a` marks the lanes holding the first half.
-template <int HV>
-__device__ __forceinline__ uint32_t partner_dpp(uint32_t v, bool is_a) {
-    const uint32_t from_right = dpp_u<0x100 + HV>(v);   // row_shl:HV -> lane i + HV
-    const uint32_t from_left = dpp_u<0x110 + HV>(v);    // row_shr:HV -> lane i - HV
-    return is_a ? from_right : from_left;
-}
-
+// chunks in natural lane order the partner sits hv lanes away, so one
+// ds_bpermute per dword (a lane permute through the LDS crossbar; no LDS
+// memory is touched) fetches it for every hv with a single straight-line
+// path.  A switch over per-hv DPP shifts was measured slower at decode
+// widths: the jump into cold code costs more than the permute.  Every lane of
+// the wave must execute this call; `is_a` marks the lanes holding the first
+// half, and the result of lanes outside the rotated span is unused.
 __device__ __forceinline__ u32x4 rot_partner(u32x4 v, int hv, bool is_a) {
+    const int lane = (int)__lane_id();
+    const int src = ((lane + (is_a ? hv : -hv)) & (kWave - 1)) << 2;   // byte index
     u32x4 r;
-    switch (hv) {
-#define MBT_PARTNER_CASE(H)                                                  \
-    case H:                                                                  \
-        for (int d = 0; d < 4; ++d) r[d] = partner_dpp<H>(v[d], is_a);      \
-        break;
-    MBT_PARTNER_CASE(1) MBT_PARTNER_CASE(2) MBT_PARTNER_CASE(3) MBT_PARTNER_CASE(4)
-    MBT_PARTNER_CASE(5) MBT_PARTNER_CASE(6) MBT_PARTNER_CASE(7) MBT_PARTNER_CASE(8)
-#undef MBT_PARTNER_CASE
-    case 16:
-        for (int d = 0; d < 4; ++d) {
-            auto w = __builtin_amdgcn_permlane16_swap(v[d], v[d], false, false);
-            r[d] = is_a ? w[1] : w[0];          // even row takes the odd row and back
-        }
-        break;
-    default:                                    // 32
-        for (int d = 0; d < 4; ++d) {
-            auto w = __builtin_amdgcn_permlane32_swap(v[d], v[d], false, false);
-            r[d] = is_a ? w[1] : w[0];          // low half takes the high half and back
-        }
-        break;
-    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) r[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v[d]);
     return r;
 }
 

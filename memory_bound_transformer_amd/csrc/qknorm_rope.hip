@@ -31,8 +31,8 @@
 //    the normalised value stays in registers between norm and rotation, so
 //    in-place calls are safe.
 //  * Chunks sit in natural order; the rotate-half partner of chunk j
-//    (j + rot/2 / Vec) arrives by DPP row shift (<= 8 lanes away) or a
-//    permlane swap (16 / 32 lanes).  Interleaved pairs are lane-local.  Each
+//    (j + rot/2 / Vec, hv lanes away) arrives by one lane permute
+//    (ds_bpermute) per dword.  Interleaved pairs are lane-local.  Each
 //    pair is rotated as written -- two rounded products, one rounded sum.
 //  * q / k chunks are streamed with nontemporal loads and stores; weights,
 //    positions and cos/sin rows use ordinary cached loads.
@@ -74,9 +74,8 @@ struct QkParams {
 // Vector kernel.  DT: dtype; G: lanes per head-row; C: chunks per lane
 // (G * C * Vec<DT> = D); LAYOUT: rotary pairing.  Requires 16-byte aligned
 // q / k / w tensors, every rotated chunk inside chunk group 0, rows of each
-// tensor below 2^24, and for rotate-half rot/2 = hv * Vec<DT> with hv in
-// 1..8, 16 or 32 and a 16-byte aligned cos/sin cache (interleaved reads its
-// run element-wise).
+// tensor below 2^24, and for rotate-half rot/2 a multiple of Vec<DT> and a
+// 16-byte aligned cos/sin cache (interleaved reads its run element-wise).
 template <int DT, int G, int C, int LAYOUT>
 __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
     constexpr int V = Vec<DT>::n;
@@ -360,11 +359,8 @@ hipError_t launch_dt(const QkArgs& a, hipStream_t s) {
     bool vec = (a.head_dim % V == 0) && (L == 4 || L == 8 || L == 16 || L == 32 || L == 64);
     vec = vec && aligned16(a.q_in) && aligned16(a.k_in) && aligned16(a.q_out) &&
           aligned16(a.k_out) && aligned16(a.w_q) && aligned16(a.w_k);
-    if (a.rot_dim > 0 && a.max_pos > 0 && a.layout == 0) {
-        const int hv = (a.rot_dim / 2) / V;
-        vec = vec && ((a.rot_dim / 2) % V == 0) && aligned16(a.cos_sin) &&
-              ((hv >= 1 && hv <= 8) || hv == 16 || hv == 32);
-    }
+    if (a.rot_dim > 0 && a.max_pos > 0 && a.layout == 0)
+        vec = vec && ((a.rot_dim / 2) % V == 0) && aligned16(a.cos_sin);
     const int QK = a.Q + a.K;
     const int64_t rows = a.T * (int64_t)QK;
     // rows of each tensor below 2^24: the token index uses a float reciprocal

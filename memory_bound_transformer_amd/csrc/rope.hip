@@ -11,7 +11,7 @@
 // MI355X design: only the rotated span of each head is read and written.  A
 // row's rotated chunks (16 bytes each) are a G-lane segment of a wave, G the
 // power of two covering them, so 64 / G rows share a wave; the rotate-half
-// partner arrives by DPP row shift or permlane swap, interleaved pairs are
+// partner arrives by one lane permute (ds_bpermute), interleaved pairs are
 // lane-local.  A scalar kernel covers other shapes and alignments.
 
 #include "mbt_device.hpp"
@@ -168,8 +168,7 @@ hipError_t launch_dt(const RopeArgs& a, hipStream_t s) {
     bool vec = (a.head_dim % V == 0) && G <= kWave && aligned16(a.cos_sin) &&
                (a.Q == 0 || aligned16(a.q)) && (a.K == 0 || aligned16(a.k)) &&
                a.T * (int64_t)(a.Q > a.K ? a.Q : a.K) < (int64_t(1) << 24);
-    if (a.layout == 0)
-        vec = vec && (half % V == 0) && ((hv >= 1 && hv <= 8) || hv == 16 || hv == 32);
+    if (a.layout == 0) vec = vec && (half % V == 0);
     if (vec)
         return a.layout == 0 ? launch_g<DT, 0>(p, G, s) : launch_g<DT, 1>(p, G, s);
     const int64_t n = a.T * (int64_t)(a.Q + a.K) * half;

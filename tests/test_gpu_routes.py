@@ -71,6 +71,8 @@ ROUTE_CELLS = [
     _cell(name="bf16_d256_rot48_shift3", rot=48, cell=10),
     _cell(name="bf16_d256_rot40_scalar", rot=40, cell=13),
     _cell(name="bf16_d96_scalar", D=96, rot=32, cell=11),
+    _cell(name="bf16_d256_rot192_hv12", rot=192, cell=14),
+    _cell(name="f32_d256_rot112_hv14", dtype=W.F32, rot=112, cell=15),
     _cell(name="bf16_prefill_24x4", T=2048, Q=24, K=4, positions="arange", max_pos=4096,
           outside=(), cell=12),
 ]
