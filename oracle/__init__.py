@@ -58,7 +58,10 @@ def _ptr(a):
 
 
 def _c(a, dtype):
-    """Fresh C-contiguous copy with the storage type the oracle expects."""
+    """Fresh C-contiguous copy with the storage type the oracle expects
+    (None stays None: a NULL pointer)."""
+    if a is None:
+        return None
     return np.array(a, dtype=_STORAGE[dtype] if isinstance(dtype, int) else dtype,
                     order="C", copy=True)
 

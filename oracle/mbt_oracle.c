@@ -220,17 +220,31 @@ static float weight_term(const void* w, int64_t i, int32_t dtype, int32_t delta)
 #endif
 }
 
+/* (x * inv) times the weight term; with no weight (w == NULL, the norm's
+ * scale folded into the next GEMM's weights: FlashRT optimization details,
+ * the weight-folding paragraph) the product is used as it is. */
+static float apply_weight(float xn, const void* w, int64_t i, int32_t dtype, int32_t delta) {
+    if (w) return xn * weight_term(w, i, dtype, delta);
+#if MBT_ORACLE_MUTATION == 13
+    return xn * 2.0f;                    /* planted: a missing weight read as 1 + 1 */
+#else
+    return xn;
+#endif
+}
+
 int mbt_ref_rmsnorm_rows(const void* x, void* y, const void* w, int64_t rows,
                          int32_t D, float eps, int32_t weight_offset,
                          int32_t dtype) {
-    if (!dtype_ok(dtype) || D <= 0 || rows < 0 || (weight_offset & ~1)) return -1;
+    if (!dtype_ok(dtype) || D <= 0 || rows < 0 || (weight_offset & ~1) ||
+        (!w && weight_offset))
+        return -1;
     float xs[4096];
     if (D > 4096) return -1;
     for (int64_t r = 0; r < rows; r++) {
         for (int32_t i = 0; i < D; i++) xs[i] = ld(x, r * D + i, dtype);
         float inv = inv_rms(xs, D, 0, eps);
         for (int32_t i = 0; i < D; i++)
-            st(y, r * D + i, dtype, (xs[i] * inv) * weight_term(w, i, dtype, weight_offset));
+            st(y, r * D + i, dtype, apply_weight(xs[i] * inv, w, i, dtype, weight_offset));
     }
     return 0;
 }
@@ -391,21 +405,22 @@ static void residual_sum(const void* x, void* residual, int64_t t, int32_t H,
     }
 }
 
-static int norm_args_ok(int64_t T, int32_t H, int32_t delta, int32_t dtype) {
-    return dtype_ok(dtype) && T >= 0 && H > 0 && !(delta & ~1);
+/* A missing weight (w == NULL) admits no offset: there is nothing to add it to. */
+static int norm_args_ok(const void* w, int64_t T, int32_t H, int32_t delta, int32_t dtype) {
+    return dtype_ok(dtype) && T >= 0 && H > 0 && !(delta & ~1) && (w || delta == 0);
 }
 
 int mbt_ref_fused_add_rmsnorm(void* x, void* residual, const void* w,
                               int64_t T, int32_t H, float eps,
                               int32_t weight_offset, int32_t dtype) {
-    if (!norm_args_ok(T, H, weight_offset, dtype)) return -1;
+    if (!norm_args_ok(w, T, H, weight_offset, dtype)) return -1;
     float* s = (float*)malloc((size_t)H * sizeof(float));
     if (!s) return -1;
     for (int64_t t = 0; t < T; t++) {
         residual_sum(x, residual, t, H, dtype, 1, s);
         float inv = inv_rms(s, H, 0, eps);
         for (int32_t i = 0; i < H; i++)
-            st(x, t * H + i, dtype, (s[i] * inv) * weight_term(w, i, dtype, weight_offset));
+            st(x, t * H + i, dtype, apply_weight(s[i] * inv, w, i, dtype, weight_offset));
     }
     free(s);
     return 0;
@@ -415,14 +430,14 @@ int mbt_ref_fused_add_rmsnorm_fp8(const void* x, void* residual, const void* w,
                                   uint8_t* y, float inv_scale, int64_t T,
                                   int32_t H, float eps, int32_t weight_offset,
                                   int32_t dtype) {
-    if (!norm_args_ok(T, H, weight_offset, dtype)) return -1;
+    if (!norm_args_ok(w, T, H, weight_offset, dtype)) return -1;
     float* s = (float*)malloc((size_t)H * sizeof(float));
     if (!s) return -1;
     for (int64_t t = 0; t < T; t++) {
         residual_sum(x, residual, t, H, dtype, 1, s);
         float inv = inv_rms(s, H, 0, eps);
         for (int32_t i = 0; i < H; i++) {
-            float v = (s[i] * inv) * weight_term(w, i, dtype, weight_offset);
+            float v = apply_weight(s[i] * inv, w, i, dtype, weight_offset);
             y[t * H + i] = mbt_ref_f32_to_e4m3fn(v * inv_scale);
         }
     }
@@ -434,7 +449,7 @@ float mbt_ref_fused_add_rmsnorm_amax(const void* x, const void* residual,
                                      const void* w, int64_t T, int32_t H,
                                      float eps, int32_t weight_offset,
                                      int32_t dtype) {
-    if (!norm_args_ok(T, H, weight_offset, dtype)) return -1.0f;
+    if (!norm_args_ok(w, T, H, weight_offset, dtype)) return -1.0f;
     float* s = (float*)malloc((size_t)H * sizeof(float));
     if (!s) return -1;
     float amax = 0.0f;
@@ -442,7 +457,7 @@ float mbt_ref_fused_add_rmsnorm_amax(const void* x, const void* residual,
         residual_sum(x, (void*)residual, t, H, dtype, 0, s);
         float inv = inv_rms(s, H, 0, eps);
         for (int32_t i = 0; i < H; i++) {
-            float v = fabsf((s[i] * inv) * weight_term(w, i, dtype, weight_offset));
+            float v = fabsf(apply_weight(s[i] * inv, w, i, dtype, weight_offset));
             if (v > amax) amax = v;
         }
     }

@@ -61,7 +61,9 @@ void mbt_ref_decode_e4m3fn(const uint8_t* in, float* out, int64_t n);
 
 /* RMSNorm of `rows` independent rows of width D (thox-edge-ops v2, 5.1):
  * y = R((x * inv) * (w + delta)), inv = 1 / sqrt(sum(x^2)/D + eps).
- * y may alias x exactly. */
+ * y may alias x exactly.  In this and the fused norms below, w == NULL means
+ * no weight (FlashRT optimization details, weight folding): y = R(x * inv),
+ * and then weight_offset must be 0. */
 int mbt_ref_rmsnorm_rows(const void* x, void* y, const void* w, int64_t rows,
                          int32_t D, float eps, int32_t weight_offset,
                          int32_t dtype);

@@ -250,6 +250,54 @@ def pin_rmsnorm_bruteforce(orc):
         assert amb <= rows.size // 200, f"brute force D={D}: {amb} midpoint cases"
 
 
+def pin_rmsnorm_no_weight(orc):
+    """No weight (w = None; the norm's scale folded into the next GEMM, as in
+    the FlashRT weight-folding paragraph): fp32 rows against torch's
+    rms_norm with weight=None in float64 (same bound as with a weight);
+    power-of-two constant rows give exactly +-1 in every dtype; every row of
+    D = 4 over the bf16 grid against mpmath rounded once; and the fused
+    residual, FP8 and amax variants agree with the plain row function."""
+    g = np.random.default_rng(13)
+    for D in (7, 256, 2560):
+        for eps in (1e-6, 0.5):
+            x = g.standard_normal((16, D)).astype(np.float32) * 1.7
+            y = orc.rmsnorm_rows(x, None, eps, 0, F32).astype(np.float64)
+            ref = F.rms_norm(torch.from_numpy(x.astype(np.float64)), (D,), weight=None,
+                             eps=float(np.float32(eps))).numpy()
+            tol = ((D + 8) / 2.0) * U32 * np.abs(ref) + 1e-30
+            assert np.all(np.abs(y - ref) <= tol), f"no-weight rmsnorm vs torch D={D}"
+    for dtype in (BF16, F16, F32):
+        for c in (1.0, -4.0, 0.25, 64.0):
+            x = W.to_bits(np.full((1, 64), c), dtype)
+            y = f32(orc.rmsnorm_rows(x, None, 0.0, 0, dtype), dtype)
+            assert np.all(y == np.sign(c)), f"no-weight constant row c={c}"
+    mpmath.mp.dps = 40
+    eps = float(np.float32(1e-6))
+    rows = np.array(np.meshgrid(*([_GRID] * 4), indexing="ij")).reshape(4, -1).T
+    xb = W.to_bits(rows, BF16)
+    y = f32(orc.rmsnorm_rows(xb, None, eps, 0, BF16), BF16)
+    xv = f32(xb, BF16).astype(np.float64)
+    amb = bad = 0
+    for r in range(rows.shape[0]):
+        inv = 1 / mpmath.sqrt(mpmath.fsum(mpmath.mpf(v) ** 2 for v in xv[r]) / 4
+                              + mpmath.mpf(eps))
+        for i in range(4):
+            exact, a = round_exact(mpmath.mpf(xv[r, i]) * inv, BF16)
+            if y[r, i] != exact:
+                amb, bad = (amb + 1, bad) if a else (amb, bad + 1)
+    assert bad == 0 and amb <= rows.size // 200, f"no-weight brute force: {bad} / {amb}"
+    x = W.to_bits(g.standard_normal((6, 1024)), BF16)
+    r = W.to_bits(g.standard_normal((6, 1024)), BF16)
+    xo, ro = orc.fused_add_rmsnorm(x, r, None, 1e-6, 0, BF16)
+    assert same_bits(xo, orc.rmsnorm_rows(ro, None, 1e-6, 0, BF16), BF16)
+    xf, rf = f32(x, BF16), f32(r, BF16)
+    xo32, _ = orc.fused_add_rmsnorm(xf, rf, None, 1e-6, 0, F32)
+    amax = orc.fused_add_rmsnorm_amax(xf, rf, None, 1e-6, 0, F32)
+    assert amax == float(np.max(np.abs(xo32))), "no-weight amax"
+    y8, _ = orc.fused_add_rmsnorm_fp8(xf, rf, None, np.float32(448.0 / amax), 1e-6, 0, F32)
+    assert np.array_equal(y8, orc.quantize_fp8(xo32, np.float32(448.0 / amax)))
+
+
 # ---------------------------------------------------------------------------
 # rotary embedding
 # ---------------------------------------------------------------------------
@@ -528,6 +576,7 @@ def pin_act_fp8(orc):
 ALL_PINS = [
     pin_bf16_converter, pin_f16_converter, pin_e4m3fn_converter,
     pin_rmsnorm_vs_torch, pin_rmsnorm_closed_forms, pin_rmsnorm_bruteforce,
+    pin_rmsnorm_no_weight,
     pin_rope_complex, pin_rope_closed_forms, pin_rope_invariants,
     pin_prologue_composition, pin_prologue_constant_head,
     pin_residual_add, pin_norm_fp8, pin_quantize_vs_torch,

@@ -27,6 +27,7 @@ MUTATIONS = {
     10: "residual sum normalised before rounding",
     11: "key heads normalised with the query weight",
     12: "positions past the cache clamped to its last row",
+    13: "a missing weight read as 1 + 1 (no-weight norm doubled)",
 }
 
 # fast pins first: most mutations are caught within a second
