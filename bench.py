@@ -300,6 +300,27 @@ def route_us(torch, mbt, W, cell, cold, passes=5, samples=50, inner=32, launches
             "null_arm_max_diff": round(max(x[2] for x in kept), 4), "dropped": dropped}
 
 
+def norm_fp8_cold_us(torch, mbt, W, cell, inv_scale, launches=2000):
+    """Residual RMSNorm -> FP8, cold: each launch uses its own ring slot."""
+    dev = "cuda:0"
+    i = cell.inputs()
+    t = lambda b: W.to_torch(b, cell.dtype, dev)
+    w = None if i["w"] is None else t(i["w"])
+    R = max(8, -(-RING_BYTES // cell.bytes_algorithmic()))
+    x0, r0 = t(i["x"]), t(i["residual"])
+    ring = [(x0.clone(), r0.clone(), torch.empty(x0.shape, dtype=torch.uint8, device=dev))
+            for _ in range(R)]
+
+    def call(j):
+        x, r, y = ring[j]
+        mbt.fused_add_rmsnorm_fp8(x, r, w, inv_scale, cell.eps, cell.weight_offset, y=y)
+
+    us = kernel_time_us(torch, call, R, launches)
+    del ring
+    torch.cuda.empty_cache()
+    return us
+
+
 def copy_ceiling_gbps(torch, nbytes, launches=1000):
     """torch's device copy of nbytes/2 -> nbytes/2 (nbytes of traffic), cold."""
     half = max(16, nbytes // 2)
@@ -496,6 +517,22 @@ def main():
             "algorithmic_bytes_per_launch": big.bytes_algorithmic(),
             "copy_ceiling_GBps": round(copy_ceiling_gbps(torch, big.bytes_algorithmic()), 1)}
 
+    # RMSNorm -> FP8 with the weight against the no-weight form (the scale
+    # folded into the next GEMM), H = 2048, bf16, cold
+    noweight = []
+    if not args.no_sweep:
+        for T in (args.tokens, 512):
+            row = {"T": T, "H": st.H}
+            for wt in (True, False):
+                c = W.NormCell(name="nw", config=5, cell=60 + T, T=T, H=st.H, dtype=W.BF16,
+                               weight_offset=0 if not wt else 1, w_mean=0.0, w_std=0.05,
+                               fp8=True, weight=wt)
+                us = norm_fp8_cold_us(torch, mbt, W, c, st.inv_n)
+                key = "weighted" if wt else "no_weight"
+                row[key + "_us"] = round(us, 3)
+                row[key + "_GBps"] = round(c.bytes_algorithmic() / us / 1e3, 1)
+            noweight.append(row)
+
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
@@ -510,6 +547,7 @@ def main():
         "roofline": roofline,
         "kernels": per,
         "prologue": prologue,
+        "norm_fp8_weight_vs_none": noweight,
     }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(W, st, args.cpu_seconds)

@@ -160,9 +160,13 @@ MBT_API mbt_status mbt_rope(void* q, void* k, const float* cos_sin, int64_t max_
  *  x        [T][H] dtype  read, then overwritten with the normalised row
  *  residual [T][H] dtype  read, then overwritten with s; may be NULL; must
  *                         not overlap x
- *  w        [H]    dtype  norm weight
+ *  w        [H]    dtype  norm weight; may be NULL: no weight multiply,
+ *                         x_i <- R(s_i * inv) (P3, weight folding: the scale
+ *                         is folded into the next GEMM's weight at load
+ *                         time), and then weight_offset must be 0
  *  T >= 0; H >= 1 (any width, odd included); eps finite >= 0;
  *  weight_offset in {0,1}; dtype mbt_dtype.
+ *  Errors: NULL x (T > 0), or NULL w with weight_offset 1 -> NULL_POINTER.
  */
 MBT_API mbt_status mbt_fused_add_rmsnorm(void* x, void* residual, const void* w, int64_t T,
                                  int32_t H, float eps, int32_t weight_offset,
@@ -180,7 +184,8 @@ MBT_API mbt_status mbt_fused_add_rmsnorm(void* x, void* residual, const void* w,
  *
  *  x        [T][H] dtype  read only
  *  residual [T][H] dtype  read, then overwritten with s; may be NULL
- *  w        [H]    dtype
+ *  w        [H]    dtype  may be NULL (no weight, weight_offset 0): the
+ *                         rms_norm_fp8_noweight form of P3's weight folding
  *  y        [T][H] uint8  e4m3fn codes, written; must not overlap the inputs
  *  inv_scale finite, > 0 (e.g. 448 / calibration amax)
  */
@@ -195,7 +200,8 @@ MBT_API mbt_status mbt_fused_add_rmsnorm_fp8(const void* x, void* residual, cons
  * quantization point).  Computes max |(s_i * inv) * (w_i + weight_offset)|
  * over all T x H values and folds it into *amax: *amax <- max(*amax, that).
  * Nothing else is written (the residual is NOT updated).  The caller
- * initialises *amax (a device float, >= 0), e.g. to 0.
+ * initialises *amax (a device float, >= 0), e.g. to 0.  w may be NULL, as for
+ * the FP8 variant.
  */
 MBT_API mbt_status mbt_fused_add_rmsnorm_amax(const void* x, const void* residual, const void* w,
                                       float* amax, int64_t T, int32_t H, float eps,

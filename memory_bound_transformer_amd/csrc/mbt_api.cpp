@@ -219,8 +219,10 @@ mbt_status norm_common(const void* x, const void* residual, const void* w, int64
     if (bytes < 0) return fail(MBT_ERR_BAD_SHAPE, "tensor sizes overflow");
     *row_bytes = bytes;
     if (T == 0) return MBT_OK;
-    if (!x || !w) return fail(MBT_ERR_NULL_POINTER, "x and w are required");
-    if (!aligned(x, eb) || !aligned(w, eb) || (residual && !aligned(residual, eb)))
+    if (!x) return fail(MBT_ERR_NULL_POINTER, "x is required");
+    if (!w && weight_offset != 0)
+        return fail(MBT_ERR_NULL_POINTER, "w is required with weight_offset 1");
+    if (!aligned(x, eb) || (w && !aligned(w, eb)) || (residual && !aligned(residual, eb)))
         return fail(MBT_ERR_ALIGN, "a pointer is not aligned to its element size");
     const Range xr{(const char*)x, bytes, "x"};
     const Range rr{(const char*)residual, bytes, "residual"};

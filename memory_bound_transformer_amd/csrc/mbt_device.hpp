@@ -120,6 +120,13 @@ __device__ __forceinline__ u32x4 pack(const float* f) {
     return v;
 }
 
+// 16 bytes of the value 1.0 in DT (the weight vector of a norm without one).
+template <int DT>
+__device__ __forceinline__ u32x4 ones16() {
+    constexpr uint32_t one = DT == kF32 ? 0x3F800000u : DT == kBF16 ? 0x3F803F80u : 0x3C003C00u;
+    return u32x4{one, one, one, one};
+}
+
 // Scalar element access for the unaligned / odd-width kernels.
 template <int DT>
 __device__ __forceinline__ float ld_elt(const void* p, int64_t i) {

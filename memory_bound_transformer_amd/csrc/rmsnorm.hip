@@ -6,6 +6,9 @@
 // the stored sum equals an eager elementwise add bit for bit):
 //   s = R(x + r);  r <- s;  x <- R((s * inv) * (w + delta)),
 //   inv = 1 / sqrt(mean(s^2) + eps).
+// Without a weight (w == NULL, delta 0; FlashRT optimization details, weight
+// folding) x <- R(s * inv): the weight vector becomes a register constant of
+// ones, so no weight is loaded and the multiply by exactly 1 changes nothing.
 // FP8 epilogue (FlashRT optimization details, fused kernel table and static
 // FP8 calibration): y = E4M3FN(((s * inv) * (w + delta)) * inv_scale) with x
 // left unchanged; the calibration pass instead folds max |(s*inv)*(w+delta)|
@@ -124,11 +127,11 @@ __global__ __launch_bounds__(256) void rmsnorm_small(NormParams p) {
     const bool have = row < p.T && j < chunks;
     const bool has_res = p.residual != nullptr;
     const int64_t off = (row * p.H + (int64_t)j * V) * EB;
-    u32x4 xv = u32x4{0u, 0u, 0u, 0u}, rv = xv, wv = xv;
+    u32x4 xv = u32x4{0u, 0u, 0u, 0u}, rv = xv, wv = ones16<DT>();
     if (have) {
         xv = ld16_nt((const char*)p.x + off);
         if (has_res) rv = ld16_nt((const char*)p.residual + off);
-        wv = ld16((const char*)p.w + (int64_t)j * V * EB);
+        if (p.w) wv = ld16((const char*)p.w + (int64_t)j * V * EB);
     }
     const u32x4 sv = residual_sum<DT>(xv, rv, has_res);
     float s[V];
@@ -178,12 +181,12 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
         const int ch = k * stride + wir * kWave + lane;
         xv[k] = u32x4{0u, 0u, 0u, 0u};
         rv[k] = u32x4{0u, 0u, 0u, 0u};
-        wv[k] = u32x4{0u, 0u, 0u, 0u};
+        wv[k] = ones16<DT>();
         if (live && ch < chunks) {
             const int64_t off = (row * p.H + (int64_t)ch * V) * EB;
             xv[k] = ld16_nt((const char*)p.x + off);
             if (has_res) rv[k] = ld16_nt((const char*)p.residual + off);
-            wv[k] = ld16((const char*)p.w + (int64_t)ch * V * EB);
+            if (p.w) wv[k] = ld16((const char*)p.w + (int64_t)ch * V * EB);
         }
     }
     // group sums: chunk chains, then the 64-lane tree of each group
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(256) void rmsnorm_scalar(NormParams p) {
             s = round_trip<DT>(s + ld_elt<DT>(p.residual, base + i));
             if (MODE != kNormAmax) st_elt<DT>(p.residual, base + i, s);
         }
-        const float y = (s * inv) * (ld_elt<DT>(p.w, i) + p.delta);
+        const float y = (s * inv) * ((p.w ? ld_elt<DT>(p.w, i) : 1.0f) + p.delta);
         if constexpr (MODE == kNormInPlace) st_elt<DT>(p.x_out, base + i, y);
         else if constexpr (MODE == kNormFp8) p.y8[base + i] = fp8x1(y * p.inv_scale);
         else amax_acc = fmaxf(amax_acc, fabsf(y));
@@ -354,7 +357,8 @@ hipError_t launch_mode(const NormArgs& a, hipStream_t s) {
 
     const int chunks = a.H / V;
     bool vec = (a.H % V == 0) && chunks <= kMaxNch * kWave * 16 && aligned16(a.x) &&
-               aligned16(a.w) && (a.residual == nullptr || aligned16(a.residual));
+               (a.w == nullptr || aligned16(a.w)) &&
+               (a.residual == nullptr || aligned16(a.residual));
     if (MODE == kNormInPlace) vec = vec && aligned16(a.x_out);
     if (MODE == kNormFp8)
         vec = vec && ((reinterpret_cast<uintptr_t>(a.y8) & (V == 8 ? 7u : 3u)) == 0);

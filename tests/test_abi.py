@@ -134,7 +134,11 @@ def test_norm_rejects(lib):
     assert f(A, B, W1, -1, 8, 1e-6, 0, BF16, None) == SHAPE
     assert f(A, B, W1, 4, 8, NAN, 0, BF16, None) == SCALAR
     assert f(None, B, W1, 4, 8, 1e-6, 0, BF16, None) == NULLP
-    assert f(A, B, None, 4, 8, 1e-6, 0, BF16, None) == NULLP
+    assert f(A, B, None, 4, 8, 1e-6, 1, BF16, None) == NULLP     # no weight needs offset 0
+    # no weight with offset 0 passes the pointer check (each call below still
+    # fails later, on alignment or aliasing, so nothing is launched)
+    assert f(A + 1, B, None, 4, 8, 1e-6, 0, BF16, None) == ALIGN
+    assert f(A, A + 16, None, 4, 8, 1e-6, 0, BF16, None) == ALIAS
     assert f(A + 1, B, W1, 4, 8, 1e-6, 0, BF16, None) == ALIGN
     assert f(A, A, W1, 4, 8, 1e-6, 0, BF16, None) == ALIAS       # residual == x
     assert f(A, A + 16, W1, 4, 8, 1e-6, 0, BF16, None) == ALIAS  # residual inside x
@@ -144,9 +148,13 @@ def test_norm_rejects(lib):
     assert g(A, B, W1, C, 0.0, 4, 8, 1e-6, 0, BF16, None) == SCALAR
     assert g(A, B, W1, C, INF, 4, 8, 1e-6, 0, BF16, None) == SCALAR
     assert g(A, B, W1, None, 1.0, 4, 8, 1e-6, 0, BF16, None) == NULLP
+    assert g(A, B, None, C, 1.0, 4, 8, 1e-6, 1, BF16, None) == NULLP
+    assert g(A, B, None, B + 3, 1.0, 4, 8, 1e-6, 0, BF16, None) == ALIAS
     assert g(A, B, W1, B + 3, 1.0, 4, 8, 1e-6, 0, BF16, None) == ALIAS  # y inside residual
     h = lib.mbt_fused_add_rmsnorm_amax
     assert h(A, B, W1, None, 4, 8, 1e-6, 0, BF16, None) == NULLP
+    assert h(A, B, None, C, 4, 8, 1e-6, 1, BF16, None) == NULLP
+    assert h(A, B, None, C + 2, 4, 8, 1e-6, 0, BF16, None) == ALIGN
     assert h(A, B, W1, C + 2, 4, 8, 1e-6, 0, BF16, None) == ALIGN
     assert h(A, B, W1, A + 4, 4, 8, 1e-6, 0, BF16, None) == ALIAS
 

@@ -270,6 +270,15 @@ EDGE_NORM = [
     _ncell(name="fp8_odd", H=333, fp8=True, cell=10),
     _ncell(name="fp8_f32", dtype=W.F32, H=2048, fp8=True, cell=11),
     _ncell(name="eps_big", eps=0.5, cell=12),
+    # no weight (w = NULL): the scale is folded into the next GEMM
+    _ncell(name="noweight_bf16_H1024", weight=False, cell=13),
+    _ncell(name="noweight_bf16_H256_small", weight=False, H=256, T=33, cell=14),
+    _ncell(name="noweight_f16_H2560", weight=False, dtype=W.F16, H=2560, cell=15),
+    _ncell(name="noweight_f32_H8192", weight=False, dtype=W.F32, H=8192, T=3, cell=16),
+    _ncell(name="noweight_odd_H37", weight=False, H=37, cell=17),
+    _ncell(name="noweight_no_residual", weight=False, residual=False, cell=18),
+    _ncell(name="noweight_fp8_H2048_T512", weight=False, fp8=True, H=2048, T=512, cell=19),
+    _ncell(name="noweight_fp8_odd", weight=False, fp8=True, H=333, cell=20),
 ]
 
 
@@ -282,6 +291,28 @@ def test_norm_edges(mbt, orc, cell):
 def test_norm_unaligned(mbt, orc, dtype):
     check_norm_cell(mbt, orc, _ncell(name=f"unaligned_{dtype}", dtype=dtype, cell=30 + dtype),
                     offset=1)
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F16, W.F32])
+def test_norm_no_weight_unaligned(mbt, orc, dtype):
+    check_norm_cell(mbt, orc, _ncell(name=f"noweight_unaligned_{dtype}", dtype=dtype,
+                                     weight=False, cell=40 + dtype), offset=1)
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_norm_no_weight_equals_unit_weight(mbt, dtype):
+    """w = NULL gives the bits of a weight of ones (multiplying by exactly 1
+    changes nothing), for the vector and the scalar kernel."""
+    for H in (1024, 37):
+        c = _ncell(name="unit", dtype=dtype, H=H, cell=50 + H)
+        i = c.inputs()
+        outs = []
+        for w in (None, np.full(H, 1.0)):
+            x, r = dev(i["x"], dtype), dev(i["residual"], dtype)
+            mbt.fused_add_rmsnorm(x, r, None if w is None else dev(W.to_bits(w, dtype), dtype),
+                                  c.eps, 0)
+            outs.append(host(x, dtype))
+        C.check_bitwise(outs[0], outs[1], label=f"no weight vs ones H={H}")
 
 
 # ---------------------------------------------------------------------------

@@ -167,13 +167,15 @@ class NormCell:
     eps: float = 1e-6
     residual: bool = True
     fp8: bool = False
+    weight: bool = True         # False: no weight (w = None, weight_offset 0)
 
     def inputs(self):
         k = (self.config, self.cell)
         x = normal_bits(k + (T_Q,), (self.T, self.H), 0.0, self.x_std, self.dtype)
         r = normal_bits(k + (T_K,), (self.T, self.H), 0.0, self.x_std, self.dtype) \
             if self.residual else None
-        w = normal_bits(k + (T_WQ,), (self.H,), self.w_mean, self.w_std, self.dtype)
+        w = normal_bits(k + (T_WQ,), (self.H,), self.w_mean, self.w_std, self.dtype) \
+            if self.weight else None
         return dict(x=x, residual=r, w=w)
 
     def calibration_inputs(self):
@@ -187,11 +189,12 @@ class NormCell:
     def bytes_algorithmic(self):
         s = ELEM_BYTES[self.dtype]
         rd = 2 if self.residual else 1          # x (+ residual) read
+        wb = self.H * s if self.weight else 0   # the weight, once
         if self.fp8:
             wr = (1 if self.residual else 0) * s + 1
-            return (rd * s + wr) * self.H * self.T + self.H * s
+            return (rd * s + wr) * self.H * self.T + wb
         wr = rd                                 # x (+ residual) written back
-        return (rd + wr) * s * self.H * self.T + self.H * s
+        return (rd + wr) * s * self.H * self.T + wb
 
 
 @dataclass
