@@ -42,6 +42,8 @@ _SIGS = {
     "mbt_ref_rope": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _i32, _i32]),
     "mbt_ref_qknorm_rope": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp,
                                    _i32, _i32, _i64, _i32, _i32, _f32, _i32, _i32, _i32]),
+    "mbt_ref_qknorm_rope_round_once": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp,
+                                   _i32, _i32, _i64, _i32, _i32, _f32, _i32, _i32, _i32]),
     "mbt_ref_fused_add_rmsnorm": (_i32, [_vp, _vp, _vp, _i64, _i32, _f32, _i32, _i32]),
     "mbt_ref_fused_add_rmsnorm_fp8": (_i32, [_vp, _vp, _vp, _vp, _f32, _i64, _i32,
                                              _f32, _i32, _i32]),
@@ -135,8 +137,9 @@ class Oracle:
 
     # ---- the path --------------------------------------------------------
     def qknorm_rope(self, q, k, w_q, w_k, cos_sin, pos, rot_dim, eps,
-                    weight_offset, layout, dtype, max_pos=None):
-        """q: [T][Q][D], k: [T][K][D]; returns (q_out, k_out)."""
+                    weight_offset, layout, dtype, max_pos=None, round_once=False):
+        """q: [T][Q][D], k: [T][K][D]; returns (q_out, k_out).  round_once
+        selects the single-rounding variant."""
         q = _c(q, dtype)
         k = _c(k, dtype)
         T, Q, D = q.shape
@@ -145,7 +148,9 @@ class Oracle:
         p = np.ascontiguousarray(pos, dtype=np.int64)
         mp = cs.shape[0] if max_pos is None else max_pos
         qo, ko = np.empty_like(q), np.empty_like(k)
-        rc = self._lib.mbt_ref_qknorm_rope(
+        fn = (self._lib.mbt_ref_qknorm_rope_round_once if round_once
+              else self._lib.mbt_ref_qknorm_rope)
+        rc = fn(
             _ptr(q), _ptr(k), _ptr(qo), _ptr(ko), _ptr(_c(w_q, dtype)),
             _ptr(_c(w_k, dtype)), _ptr(cs), mp, _ptr(p), Q, K, T, D, rot_dim,
             eps, weight_offset, layout, dtype)

@@ -335,26 +335,39 @@ int mbt_ref_rope(void* x, const float* cos_sin, int64_t max_pos,
 /* tests can check that this op equals their composition.                    */
 /* ------------------------------------------------------------------------ */
 
+/* round_first = 1: the normalised value is rounded to the dtype and that
+ * rounded value is rotated (the contract of the fused op, P1 5.1 and P2
+ * "Implementation").  round_first = 0: the single-rounding variant the P2
+ * review asks for (review item 1): the rotated channels take the fp32 norm
+ * result straight into the rotation and are rounded once, after it; the
+ * channels past rot_dim (and every channel of a token outside the cache)
+ * are the norm result rounded once, as in the contract. */
 static void norm_rope_head(const void* in, void* out, int64_t base,
                            const void* w, int32_t D, int32_t rot,
                            float eps, int32_t delta, int32_t layout,
-                           int32_t dtype, const float* cs /* NULL: no rotation */) {
+                           int32_t dtype, const float* cs /* NULL: no rotation */,
+                           int round_first) {
     float x[4096], n[4096], o[4096];
     for (int32_t i = 0; i < D; i++) x[i] = ld(in, base + i, dtype);
     float inv = inv_rms(x, D, rot, eps);
-    for (int32_t i = 0; i < D; i++)
-        n[i] = rounded((x[i] * inv) * weight_term(w, i, dtype, delta), dtype);
+    for (int32_t i = 0; i < D; i++) {
+        n[i] = (x[i] * inv) * weight_term(w, i, dtype, delta);
+#if MBT_ORACLE_MUTATION == 14
+        round_first = 1;                          /* planted: single rounding ignored */
+#endif
+        if (round_first) n[i] = rounded(n[i], dtype);
+    }
     if (cs) rotate_head(n, o, D, rot, layout, cs);
     else for (int32_t i = 0; i < D; i++) o[i] = n[i];
     for (int32_t i = 0; i < D; i++) st(out, base + i, dtype, o[i]);
 }
 
-int mbt_ref_qknorm_rope(const void* q_in, const void* k_in, void* q_out,
-                        void* k_out, const void* w_q, const void* w_k,
-                        const float* cos_sin, int64_t max_pos,
-                        const int64_t* pos, int32_t Q, int32_t K, int64_t T,
-                        int32_t head_dim, int32_t rot_dim, float eps,
-                        int32_t weight_offset, int32_t layout, int32_t dtype) {
+static int qknorm_rope(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                       const void* w_q, const void* w_k, const float* cos_sin,
+                       int64_t max_pos, const int64_t* pos, int32_t Q, int32_t K,
+                       int64_t T, int32_t head_dim, int32_t rot_dim, float eps,
+                       int32_t weight_offset, int32_t layout, int32_t dtype,
+                       int round_first) {
     if (!rope_args_ok(head_dim, rot_dim, layout, dtype) || Q < 0 || K < 0 ||
         T < 0 || (weight_offset & ~1) || max_pos < 0)
         return -1;
@@ -363,18 +376,38 @@ int mbt_ref_qknorm_rope(const void* q_in, const void* k_in, void* q_out,
         const float* cs = cache_row(cos_sin, pos[t], max_pos, rot_dim);
         for (int32_t h = 0; h < Q; h++)
             norm_rope_head(q_in, q_out, (t * Q + h) * (int64_t)D, w_q, D, rot_dim,
-                           eps, weight_offset, layout, dtype, cs);
+                           eps, weight_offset, layout, dtype, cs, round_first);
         for (int32_t h = 0; h < K; h++)
 #if MBT_ORACLE_MUTATION == 11
             (void)w_k,
             norm_rope_head(k_in, k_out, (t * K + h) * (int64_t)D, w_q, D, rot_dim,
-                           eps, weight_offset, layout, dtype, cs); /* planted */
+                           eps, weight_offset, layout, dtype, cs, round_first); /* planted */
 #else
             norm_rope_head(k_in, k_out, (t * K + h) * (int64_t)D, w_k, D, rot_dim,
-                           eps, weight_offset, layout, dtype, cs);
+                           eps, weight_offset, layout, dtype, cs, round_first);
 #endif
     }
     return 0;
+}
+
+int mbt_ref_qknorm_rope(const void* q_in, const void* k_in, void* q_out,
+                        void* k_out, const void* w_q, const void* w_k,
+                        const float* cos_sin, int64_t max_pos,
+                        const int64_t* pos, int32_t Q, int32_t K, int64_t T,
+                        int32_t head_dim, int32_t rot_dim, float eps,
+                        int32_t weight_offset, int32_t layout, int32_t dtype) {
+    return qknorm_rope(q_in, k_in, q_out, k_out, w_q, w_k, cos_sin, max_pos, pos, Q, K, T,
+                       head_dim, rot_dim, eps, weight_offset, layout, dtype, 1);
+}
+
+int mbt_ref_qknorm_rope_round_once(const void* q_in, const void* k_in, void* q_out,
+                                   void* k_out, const void* w_q, const void* w_k,
+                                   const float* cos_sin, int64_t max_pos,
+                                   const int64_t* pos, int32_t Q, int32_t K, int64_t T,
+                                   int32_t head_dim, int32_t rot_dim, float eps,
+                                   int32_t weight_offset, int32_t layout, int32_t dtype) {
+    return qknorm_rope(q_in, k_in, q_out, k_out, w_q, w_k, cos_sin, max_pos, pos, Q, K, T,
+                       head_dim, rot_dim, eps, weight_offset, layout, dtype, 0);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -89,6 +89,16 @@ int mbt_ref_qknorm_rope(const void* q_in, const void* k_in, void* q_out,
                         int32_t head_dim, int32_t rot_dim, float eps,
                         int32_t weight_offset, int32_t layout, int32_t dtype);
 
+/* Single-rounding variant of the prologue (ninfer PR #273, review item 1):
+ * the first rot_dim channels are rotated from the fp32 norm result and
+ * rounded once, after the rotation; the other channels are as above. */
+int mbt_ref_qknorm_rope_round_once(const void* q_in, const void* k_in, void* q_out,
+                                   void* k_out, const void* w_q, const void* w_k,
+                                   const float* cos_sin, int64_t max_pos,
+                                   const int64_t* pos, int32_t Q, int32_t K, int64_t T,
+                                   int32_t head_dim, int32_t rot_dim, float eps,
+                                   int32_t weight_offset, int32_t layout, int32_t dtype);
+
 /* Fused residual-add RMSNorm, in place (thox-edge-ops v2, 5.1):
  * s = R(x + r); r <- s; x <- R((s * inv) * (w + delta)).
  * residual == NULL: s = x and only x is written. */

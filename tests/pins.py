@@ -426,6 +426,76 @@ def pin_prologue_constant_head(orc):
                 assert same_bits(ko[0, 0], wd, dtype), "k head"
 
 
+def pin_prologue_round_once(orc):
+    """Single-rounding variant (the ninfer PR's review item 1: rotate the fp32
+    norm result, round once).  Closed forms: with an identity, quarter-turn or
+    half-turn cache row the rotated channels are exactly R(n), (-R(n_b),
+    R(n_a)) and (-R(n_a), -R(n_b)) of the plain RMSNorm; channels past
+    rot_dim and tokens outside the cache equal the plain RMSNorm.  Against
+    float64: the exact rotation of the exact norm result, rounded once, must
+    match wherever it is farther from a rounding midpoint than the oracle's
+    own fp32 error bound (sum of squares (D+8)/2 u, products and sum 3 u)."""
+    g = np.random.default_rng(33)
+    for dtype in (BF16, F16, F32):
+        for layout in (W.ROTATE_HALF, W.INTERLEAVED):
+            D, rot, Q, K = 32, 16, 2, 1
+            q = W.to_bits(g.standard_normal((5, Q, D)) * 2, dtype)
+            k = W.to_bits(g.standard_normal((5, K, D)) * 2, dtype)
+            w = W.to_bits(g.standard_normal(D) * 0.05, dtype)
+            cs = np.zeros((3, rot), np.float32)
+            cs[0, :rot // 2] = 1.0                      # identity
+            cs[1, rot // 2:] = 1.0                      # quarter turn
+            cs[2, :rot // 2] = -1.0                     # half turn
+            a, b = _complex_pairs(None, rot, layout)
+            qn = f32(orc.rmsnorm_rows(q, w, 1e-6, 1, dtype), dtype)
+            for p, fa, fb in ((0, lambda v: v[..., a], lambda v: v[..., b]),
+                              (1, lambda v: -v[..., b], lambda v: v[..., a]),
+                              (2, lambda v: -v[..., a], lambda v: -v[..., b])):
+                qo, _ = orc.qknorm_rope(q, k, w, w, cs, np.full(5, p), rot, 1e-6, 1, layout,
+                                        dtype, round_once=True)
+                qo = f32(qo, dtype)
+                assert np.array_equal(qo[..., a], fa(qn)) and np.array_equal(qo[..., b], fb(qn)), \
+                    f"round-once closed form p={p} dtype={dtype} layout={layout}"
+                assert np.array_equal(qo[..., rot:], qn[..., rot:]), "round-once tail channels"
+            qo, _ = orc.qknorm_rope(q, k, w, w, cs, np.array([3, -1, 7, 1 << 40, 5]), rot, 1e-6,
+                                    1, layout, dtype, round_once=True)
+            assert np.array_equal(f32(qo, dtype), qn), "round-once outside the cache"
+    for dtype in (BF16, F16):
+        for layout in (W.ROTATE_HALF, W.INTERLEAVED):
+            D, rot, T, Q, K = 128, 64, 4, 3, 1
+            q = W.to_bits(g.standard_normal((T, Q, D)) * 2, dtype)
+            k = W.to_bits(g.standard_normal((T, K, D)) * 2, dtype)
+            wq = W.to_bits(g.standard_normal(D) * 0.05, dtype)
+            wk = W.to_bits(g.standard_normal(D) * 0.05, dtype)
+            cs = W.rope_cache(4096, rot, 1e6)
+            pos = g.integers(0, 4096, T)
+            qo, ko = orc.qknorm_rope(q, k, wq, wk, cs, pos, rot, 1e-6, 1, layout, dtype,
+                                     round_once=True)
+            a, b = _complex_pairs(None, rot, layout)
+            c = cs[pos][:, None, : rot // 2].astype(np.float64)
+            s_ = cs[pos][:, None, rot // 2:].astype(np.float64)
+            decided = amb = 0
+            for x, wt, y in ((q, wq, qo), (k, wk, ko)):
+                xv = f32(x, dtype).astype(np.float64)
+                inv = 1.0 / np.sqrt(np.mean(xv * xv, axis=-1, keepdims=True) + float(np.float32(1e-6)))
+                n = xv * inv * (f32(wt, dtype).astype(np.float64) + 1.0)
+                oa = n[..., a] * c - n[..., b] * s_
+                ob = n[..., b] * c + n[..., a] * s_
+                mag = np.abs(n[..., a] * c) + np.abs(n[..., b] * s_)
+                bound = ((D + 8) / 2.0 + 3) * U32 * mag
+                yv = f32(y, dtype)
+                for exact, got, bd in ((oa, yv[..., a], bound), (ob, yv[..., b], bound)):
+                    for e, gv, bb in zip(exact.ravel(), got.ravel(), bd.ravel()):
+                        lo, _ = round_exact(e - bb, dtype)
+                        hi, _ = round_exact(e + bb, dtype)
+                        if lo != hi:
+                            amb += 1
+                            continue
+                        decided += 1
+                        assert gv == lo, f"round-once rotation: {gv} vs exact {e} ({dtype})"
+            assert amb <= 0.08 * (decided + amb), f"round-once: {amb} undecided of {decided + amb}"
+
+
 # ---------------------------------------------------------------------------
 # fused residual-add RMSNorm and its FP8 variant
 # ---------------------------------------------------------------------------
@@ -578,7 +648,7 @@ ALL_PINS = [
     pin_rmsnorm_vs_torch, pin_rmsnorm_closed_forms, pin_rmsnorm_bruteforce,
     pin_rmsnorm_no_weight,
     pin_rope_complex, pin_rope_closed_forms, pin_rope_invariants,
-    pin_prologue_composition, pin_prologue_constant_head,
+    pin_prologue_composition, pin_prologue_constant_head, pin_prologue_round_once,
     pin_residual_add, pin_norm_fp8, pin_quantize_vs_torch,
     pin_act_vs_torch, pin_act_exhaustive_bf16, pin_act_identities, pin_act_fp8,
 ]

@@ -28,6 +28,7 @@ MUTATIONS = {
     11: "key heads normalised with the query weight",
     12: "positions past the cache clamped to its last row",
     13: "a missing weight read as 1 + 1 (no-weight norm doubled)",
+    14: "single-rounding prologue rounds the norm result before rotating",
 }
 
 # fast pins first: most mutations are caught within a second
