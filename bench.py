@@ -300,6 +300,53 @@ def route_us(torch, mbt, W, cell, cold, passes=5, samples=50, inner=32, launches
             "null_arm_max_diff": round(max(x[2] for x in kept), 4), "dropped": dropped}
 
 
+def qkv_cache_bytes(cell):
+    """Algorithmic bytes of the fused QKV -> q_out + KV-cache op: qkv read,
+    q_out and both cache rows written, the cos/sin rows, both weights, the
+    positions and the slots."""
+    s = 4 if cell.dtype == 0 else 2
+    T, Q, K, D = cell.T, cell.Q, cell.K, cell.D
+    return 2 * T * (Q + 2 * K) * D * s + 4 * cell.rot * T + 2 * D * s + 16 * T
+
+
+def extended_cold_us(torch, mbt, W, cell, form, launches=2000):
+    """Cold timing of the extended prologue forms over a ring of buffer sets:
+    form "once" (mbt_qknorm_rope_ex, single rounding, dense) or "qkv_cache"
+    (mbt_qkv_norm_rope_cache, each token to its own cache slot)."""
+    dev = "cuda:0"
+    i = cell.inputs()
+    t = lambda b: W.to_torch(b, cell.dtype, dev)
+    wq, wk = t(i["w_q"]), t(i["w_k"])
+    cs = torch.from_numpy(i["cos_sin"]).to(dev)
+    pos = torch.from_numpy(i["pos"]).to(dev)
+    T, Q, K, D = cell.T, cell.Q, cell.K, cell.D
+    nbytes = cell.bytes_algorithmic() if form == "once" else qkv_cache_bytes(cell)
+    R = max(8, -(-RING_BYTES // nbytes))
+    q0, k0 = t(i["q"]), t(i["k"])
+    if form == "once":
+        ring = [(q0.clone(), k0.clone(), torch.empty_like(q0), torch.empty_like(k0))
+                for _ in range(R)]
+
+        def call(j):
+            q, k, qo, ko = ring[j]
+            mbt.qknorm_rope_ex(q, k, wq, wk, cs, pos, cell.rot, cell.eps, cell.weight_offset,
+                               cell.layout, q_out=qo, k_out=ko, round_once=True)
+    else:
+        qkv0 = torch.cat([q0, k0, k0], dim=1).contiguous()      # [T, Q + 2K, D]
+        slot = torch.arange(T, dtype=torch.int64, device=dev)
+        ring = [(qkv0.clone(), torch.empty_like(q0), torch.empty_like(k0), torch.empty_like(k0))
+                for _ in range(R)]
+
+        def call(j):
+            qkv, qo, kc, vc = ring[j]
+            mbt.qkv_norm_rope_cache(qkv, wq, wk, cs, pos, slot, kc, vc, Q, cell.rot, cell.eps,
+                                    cell.weight_offset, cell.layout, q_out=qo)
+    us = kernel_time_us(torch, call, R, launches)
+    del ring
+    torch.cuda.empty_cache()
+    return us, nbytes
+
+
 def norm_fp8_cold_us(torch, mbt, W, cell, inv_scale, launches=2000):
     """Residual RMSNorm -> FP8, cold: each launch uses its own ring slot."""
     dev = "cuda:0"
@@ -516,6 +563,18 @@ def main():
             "kernel": f"prologue {big.Q}x{big.K} T={big.T} bf16", "avg_launch_us": us,
             "algorithmic_bytes_per_launch": big.bytes_algorithmic(),
             "copy_ceiling_GBps": round(copy_ceiling_gbps(torch, big.bytes_algorithmic()), 1)}
+        # the extended forms: single rounding, and the fused QKV -> KV-cache op
+        ext = []
+        for c in (st.pro, big):
+            base = [x for x in pre if x["QK"] == f"{c.Q}x{c.K}" and x["T"] == c.T]
+            row = {"QK": f"{c.Q}x{c.K}", "T": c.T,
+                   "contract_us": base[0]["cold_us"] if base else per["prologue"]["us"]}
+            for form in ("once", "qkv_cache"):
+                us, nb = extended_cold_us(torch, mbt, W, c, form)
+                row[form + "_us"] = round(us, 3)
+                row[form + "_GBps"] = round(nb / us / 1e3, 1)
+            ext.append(row)
+        prologue["extended_forms_cold"] = ext
 
     # RMSNorm -> FP8 with the weight against the no-weight form (the scale
     # folded into the next GEMM), H = 2048, bf16, cold

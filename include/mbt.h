@@ -80,6 +80,12 @@ typedef enum { MBT_ROPE_ROTATE_HALF = 0, MBT_ROPE_INTERLEAVED = 1 } mbt_rope_lay
  * and the tanh approximation of GELU (Gemma MLP). */
 typedef enum { MBT_ACT_SILU = 0, MBT_ACT_GELU_TANH = 1 } mbt_act;
 
+/* Flags of mbt_qknorm_rope_ex and mbt_qkv_norm_rope_cache.
+ * MBT_QK_ROUND_ONCE: the single-rounding variant (P2, review item 1): the
+ * first rot_dim channels are rotated from the fp32 norm result and rounded
+ * once, after the rotation, instead of rotating the rounded norm result. */
+#define MBT_QK_ROUND_ONCE 1
+
 /*
  * mbt_qknorm_rope -- fused per-head QK-RMSNorm + rotary embedding prologue.
  *
@@ -119,6 +125,74 @@ MBT_API mbt_status mbt_qknorm_rope(const void* q_in, const void* k_in, void* q_o
                            int32_t Q, int32_t K, int64_t T, int32_t head_dim,
                            int32_t rot_dim, float eps, int32_t weight_offset,
                            int32_t layout, int32_t dtype, void* stream);
+
+/*
+ * mbt_qknorm_rope_ex -- mbt_qknorm_rope on strided views, with flags.
+ *
+ * The same operation as mbt_qknorm_rope (flags 0), or its single-rounding
+ * variant (flags MBT_QK_ROUND_ONCE, P2 review item 1):
+ *   out_a = R(n'_a c - n'_b s),  out_b = R(n'_b c + n'_a s),
+ *   n'_i = (x_i * inv) * (w_i + weight_offset) in fp32, not rounded;
+ *   channels >= rot_dim and tokens outside the cache: R(n'_i) as before.
+ * Each tensor may be a strided view (P1 section 6: strided views, as when q
+ * and k are slices of one fused QKV projection buffer): the heads of one
+ * token are contiguous ([heads][head_dim]) and consecutive tokens are
+ * *_stride elements apart.
+ *
+ *  q_in_stride, k_in_stride, q_out_stride, k_out_stride
+ *         token strides in elements; 0 = dense (Q * head_dim or
+ *         K * head_dim); otherwise >= that and <= 2^40
+ *  flags  0 or MBT_QK_ROUND_ONCE
+ *  everything else: as for mbt_qknorm_rope.
+ * An output may be the very view of the input it replaces (in place, same
+ * pointer and stride); any other overlap of an output with an input or with
+ * the other output is MBT_ERR_ALIAS (views with equal strides are compared
+ * row by row, so q and k slices of one buffer may be updated in place).
+ * Alignment: element-aligned pointers and any stride; 16-byte aligned
+ * pointers and strides take the vector kernel.
+ */
+MBT_API mbt_status mbt_qknorm_rope_ex(const void* q_in, const void* k_in, void* q_out,
+                                      void* k_out, const void* w_q, const void* w_k,
+                                      const float* cos_sin, int64_t max_pos,
+                                      const int64_t* pos, int32_t Q, int32_t K, int64_t T,
+                                      int32_t head_dim, int32_t rot_dim, float eps,
+                                      int32_t weight_offset, int32_t layout, int32_t dtype,
+                                      int64_t q_in_stride, int64_t k_in_stride,
+                                      int64_t q_out_stride, int64_t k_out_stride, int32_t flags,
+                                      void* stream);
+
+/*
+ * mbt_qkv_norm_rope_cache -- the prologue on a fused QKV buffer with the
+ * key / value cache write fused in.
+ *
+ * P3's decoder kernel list (qkv_split_rope_kvcache: split Q/K/V, rotary
+ * embedding and the KV cache write in one kernel) and P1 section 10 (a KV
+ * write fused into the prologue), with the per-head norm of
+ * mbt_qknorm_rope: for every token t,
+ *   q_out[t]            <- the prologue's query heads of qkv[t][0 : Q]
+ *   k_cache[slot[t]]    <- the prologue's key heads of qkv[t][Q : Q + K]
+ *   v_cache[slot[t]]    <- qkv[t][Q + K : Q + 2K], copied unchanged
+ * A slot outside [0, n_slots) (e.g. -1 for padding) writes no cache row; the
+ * token's q_out row is still written.  Two valid tokens must not share a slot
+ * (their writes would race).
+ *
+ *  qkv      [T][Q + 2K][head_dim]  dtype  read
+ *  q_out    [T][Q][head_dim]       dtype  written (may be NULL when Q == 0)
+ *  k_cache, v_cache [n_slots][K][head_dim] dtype  rows written at the slots
+ *  slot     [T] int64                     cache row of each token
+ *  n_slots  >= 0
+ *  K >= 1; Q >= 0; flags 0 or MBT_QK_ROUND_ONCE; everything else as for
+ *  mbt_qknorm_rope.  No output may overlap qkv, the weights, the cache of
+ *  angles, pos, slot or another output.
+ */
+MBT_API mbt_status mbt_qkv_norm_rope_cache(const void* qkv, void* q_out, void* k_cache,
+                                           void* v_cache, const int64_t* slot, int64_t n_slots,
+                                           const void* w_q, const void* w_k,
+                                           const float* cos_sin, int64_t max_pos,
+                                           const int64_t* pos, int32_t Q, int32_t K, int64_t T,
+                                           int32_t head_dim, int32_t rot_dim, float eps,
+                                           int32_t weight_offset, int32_t layout, int32_t dtype,
+                                           int32_t flags, void* stream);
 
 /*
  * mbt_rope -- standalone rotary position embedding, in place.

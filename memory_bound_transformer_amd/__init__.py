@@ -8,6 +8,8 @@ eager fallback: if the library is missing, importing this package fails.
 The entry points mirror include/mbt.h:
 
     qknorm_rope            fused per-head QK-RMSNorm + RoPE prologue
+    qknorm_rope_ex         the same on strided views, optional single rounding
+    qkv_norm_rope_cache    the prologue on a fused QKV buffer + KV-cache write
     rope                   standalone rotary embedding, in place
     fused_add_rmsnorm      residual add + RMSNorm, in place
     fused_add_rmsnorm_fp8  the same with static-scale e4m3fn output
@@ -23,7 +25,7 @@ import os
 import torch
 
 __all__ = [
-    "qknorm_rope", "rope", "fused_add_rmsnorm", "fused_add_rmsnorm_fp8", "fused_add_rmsnorm_amax",
+    "qknorm_rope", "qknorm_rope_ex", "qkv_norm_rope_cache", "rope", "fused_add_rmsnorm", "fused_add_rmsnorm_fp8", "fused_add_rmsnorm_amax",
     "gated_act", "gated_act_fp8", "gated_act_amax", "quantize_fp8", "MbtError",
     "ROTATE_HALF", "INTERLEAVED", "SILU", "GELU_TANH", "LIB_PATH", "abi_version",
 ]
@@ -32,6 +34,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmbt.so")
 
 ROTATE_HALF, INTERLEAVED = 0, 1
+ROUND_ONCE = 1                      # MBT_QK_ROUND_ONCE
 SILU, GELU_TANH = 0, 1
 _DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
@@ -45,6 +48,10 @@ _vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.
 _SIGS = {
     "mbt_qknorm_rope": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i64, _i32,
                         _i32, _f32, _i32, _i32, _i32, _vp],
+    "mbt_qknorm_rope_ex": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _i32, _i64, _i32,
+                           _i32, _f32, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _i32, _vp],
+    "mbt_qkv_norm_rope_cache": [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _i32,
+                                _i32, _i64, _i32, _i32, _f32, _i32, _i32, _i32, _i32, _vp],
     "mbt_rope": [_vp, _vp, _vp, _i64, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp],
     "mbt_fused_add_rmsnorm": [_vp, _vp, _vp, _i64, _i32, _f32, _i32, _i32, _vp],
     "mbt_fused_add_rmsnorm_fp8": [_vp, _vp, _vp, _vp, _f32, _i64, _i32, _f32, _i32, _i32, _vp],
@@ -136,6 +143,74 @@ def qknorm_rope(q, k, w_q, w_k, cos_sin, pos, rot_dim, eps=1e-6, weight_offset=0
                                 _ptr(w_k), _ptr(cos_sin), mp, _ptr(pos), Q, K, T, D, rot_dim,
                                 eps, weight_offset, layout, _dtype(q), _stream(stream)))
     return q_out, k_out
+
+
+def _token_stride(t, name):
+    """Token stride (elements) of a [T, heads, D] view whose heads of one
+    token are contiguous; the tokens may be any distance apart."""
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [T, heads, head_dim]")
+    if t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != t.shape[2]):
+        raise ValueError(f"{name}: the heads of one token must be contiguous")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1] * t.shape[2]
+
+
+def qknorm_rope_ex(q_in, k_in, w_q, w_k, cos_sin, pos, rot_dim, eps=1e-6, weight_offset=0,
+                   layout=ROTATE_HALF, q_out=None, k_out=None, round_once=False, max_pos=None,
+                   stream=None):
+    """mbt_qknorm_rope on strided [T, heads, D] views (e.g. q and k slices of
+    a fused QKV buffer), with the single-rounding variant on request.  Pass
+    q_out=q_in / k_out=k_in for the in-place form."""
+    for t in (q_in, k_in, w_q, w_k, cos_sin, pos, q_out, k_out):
+        if t is not None and not t.is_cuda:
+            raise ValueError("libmbt operates on GPU tensors only")
+    for t in (w_q, w_k, cos_sin, pos):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("weights, cos_sin and pos must be contiguous")
+    _same_dtype(q_in, k_in, w_q, w_k, q_out, k_out)
+    if pos.dtype != torch.int64 or (cos_sin is not None and cos_sin.dtype != torch.float32):
+        raise TypeError("pos must be int64 and cos_sin float32")
+    T, Q, D = q_in.shape
+    K = k_in.shape[1]
+    if q_out is None:
+        q_out = torch.empty((T, Q, D), dtype=q_in.dtype, device=q_in.device)
+    if k_out is None:
+        k_out = torch.empty((T, K, D), dtype=k_in.dtype, device=k_in.device)
+    st = [_token_stride(t, n) for t, n in ((q_in, "q_in"), (k_in, "k_in"), (q_out, "q_out"),
+                                           (k_out, "k_out"))]
+    mp = (cos_sin.shape[0] if cos_sin is not None else 0) if max_pos is None else max_pos
+    _check(_lib.mbt_qknorm_rope_ex(_ptr(q_in), _ptr(k_in), _ptr(q_out), _ptr(k_out), _ptr(w_q),
+                                   _ptr(w_k), _ptr(cos_sin), mp, _ptr(pos), Q, K, T, D, rot_dim,
+                                   eps, weight_offset, layout, _dtype(q_in), *st,
+                                   ROUND_ONCE if round_once else 0, _stream(stream)))
+    return q_out, k_out
+
+
+def qkv_norm_rope_cache(qkv, w_q, w_k, cos_sin, pos, slot, k_cache, v_cache, Q, rot_dim,
+                        eps=1e-6, weight_offset=0, layout=ROTATE_HALF, q_out=None,
+                        round_once=False, max_pos=None, stream=None):
+    """qkv [T, Q + 2K, D] -> q_out [T, Q, D]; the prologue's key heads and
+    the unchanged value heads of token t go to row slot[t] of
+    k_cache / v_cache [n_slots, K, D] (slots outside [0, n_slots): no write)."""
+    _dev(qkv, w_q, w_k, cos_sin, pos, slot, k_cache, v_cache, q_out)
+    _same_dtype(qkv, w_q, w_k, k_cache, v_cache, q_out)
+    if pos.dtype != torch.int64 or slot.dtype != torch.int64:
+        raise TypeError("pos and slot must be int64")
+    T, QKV, D = qkv.shape
+    K = (QKV - Q) // 2
+    if K < 1 or Q + 2 * K != QKV:
+        raise ValueError("qkv must be [T, Q + 2K, head_dim] with K >= 1")
+    if k_cache.shape[1:] != (K, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [n_slots, K, head_dim]")
+    if q_out is None:
+        q_out = torch.empty((T, Q, D), dtype=qkv.dtype, device=qkv.device)
+    mp = (cos_sin.shape[0] if cos_sin is not None else 0) if max_pos is None else max_pos
+    _check(_lib.mbt_qkv_norm_rope_cache(_ptr(qkv), _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(slot), k_cache.shape[0], _ptr(w_q), _ptr(w_k),
+                                        _ptr(cos_sin), mp, _ptr(pos), Q, K, T, D, rot_dim, eps,
+                                        weight_offset, layout, _dtype(qkv),
+                                        ROUND_ONCE if round_once else 0, _stream(stream)))
+    return q_out
 
 
 def rope(q, k, cos_sin, pos, rot_dim, layout=ROTATE_HALF, max_pos=None, stream=None):

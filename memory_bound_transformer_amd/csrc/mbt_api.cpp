@@ -77,6 +77,158 @@ mbt_status hip_status(hipError_t e, const char* what) {
     return fail(MBT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// A strided view: `rows` rows of `len` bytes, `stride` bytes apart.
+struct View {
+    const char* p;
+    int64_t stride, len, rows;
+    const char* name;
+};
+
+int64_t span(const View& v) { return v.rows > 0 ? (v.rows - 1) * v.stride + v.len : 0; }
+
+int64_t floor_div(int64_t a, int64_t b) {     // b > 0
+    const int64_t q = a / b;
+    return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+
+// Do the two views share a byte?  Exact when the strides are equal (rows
+// a + t s + [0, la) and b + u s + [0, lb) meet iff -lb < d + k s < la for
+// some k = u - t in [-(ra - 1), rb - 1], d = b - a); otherwise the spans are
+// compared, which may report an overlap of interleaved views.
+bool views_overlap(const View& a, const View& b) {
+    if (!a.p || !b.p || a.rows <= 0 || b.rows <= 0 || a.len <= 0 || b.len <= 0) return false;
+    const intptr_t pa = reinterpret_cast<intptr_t>(a.p), pb = reinterpret_cast<intptr_t>(b.p);
+    if (!(pa < pb + span(b) && pb < pa + span(a))) return false;
+    if (a.stride != b.stride) return true;
+    const int64_t s = a.stride, d = (int64_t)(pb - pa);
+    int64_t k = floor_div(-b.len - d, s) + 1;          // least k with d + k s > -lb
+    if (k < -(a.rows - 1)) k = -(a.rows - 1);
+    return k <= b.rows - 1 && d + k * s < a.len;
+}
+
+bool same_view(const View& a, const View& b) {
+    return a.p == b.p && a.len == b.len && a.rows == b.rows && (a.rows <= 1 || a.stride == b.stride);
+}
+
+// Everything the three QK-norm + RoPE entry points take; strides in elements.
+struct QkCall {
+    const void* q_in;
+    const void* k_in;
+    void* q_out;
+    void* k_out;
+    const void* w_q;
+    const void* w_k;
+    const float* cos_sin;
+    int64_t max_pos;
+    const int64_t* pos;
+    int32_t Q, K;
+    int64_t T;
+    int32_t D, rot;
+    float eps;
+    int32_t weight_offset, layout, dtype, flags;
+    int64_t q_in_st, k_in_st, q_out_st, k_out_st;
+    const int64_t* slot;
+    int64_t n_slots;
+    const void* v_in;
+    void* v_out;
+    int64_t v_in_st, v_out_st;
+};
+
+// Validates a call completely, then launches.  Stride 0 means dense.
+mbt_status qk_run(QkCall c, void* stream) {
+    if (!valid_dtype(c.dtype)) return fail(MBT_ERR_BAD_DTYPE, "dtype %d", c.dtype);
+    if (c.layout != MBT_ROPE_ROTATE_HALF && c.layout != MBT_ROPE_INTERLEAVED)
+        return fail(MBT_ERR_BAD_ENUM, "layout %d", c.layout);
+    if (c.weight_offset != 0 && c.weight_offset != 1)
+        return fail(MBT_ERR_BAD_ENUM, "weight_offset %d", c.weight_offset);
+    if (c.flags & ~MBT_QK_ROUND_ONCE) return fail(MBT_ERR_BAD_ENUM, "flags 0x%x", c.flags);
+    if (c.Q < 0 || c.K < 0 || c.Q + c.K < 1) return fail(MBT_ERR_BAD_SHAPE, "Q=%d K=%d", c.Q, c.K);
+    if (c.T < 0) return fail(MBT_ERR_BAD_SHAPE, "T=%lld", (long long)c.T);
+    if (c.D < 1 || c.D > 512) return fail(MBT_ERR_BAD_SHAPE, "head_dim %d not in [1, 512]", c.D);
+    if (c.rot < 0 || c.rot > c.D || (c.rot % 2) != 0)
+        return fail(MBT_ERR_BAD_SHAPE, "rot_dim %d (head_dim %d)", c.rot, c.D);
+    if (!finite_nonneg(c.eps)) return fail(MBT_ERR_BAD_SCALAR, "eps must be finite and >= 0");
+    if (c.max_pos < 0) return fail(MBT_ERR_BAD_SCALAR, "max_pos %lld", (long long)c.max_pos);
+    if (c.n_slots < 0) return fail(MBT_ERR_BAD_SCALAR, "n_slots %lld", (long long)c.n_slots);
+    const bool has_v = c.v_in != nullptr || c.v_out != nullptr;
+    const int64_t qrow = (int64_t)c.Q * c.D, krow = (int64_t)c.K * c.D;
+    int64_t* sts[] = {&c.q_in_st, &c.k_in_st, &c.q_out_st, &c.k_out_st, &c.v_in_st, &c.v_out_st};
+    const int64_t need[] = {qrow, krow, qrow, krow, krow, krow};
+    for (int i = 0; i < 6; ++i) {
+        if (*sts[i] == 0) *sts[i] = need[i];
+        if (*sts[i] < need[i] || *sts[i] > (INT64_C(1) << 40))
+            return fail(MBT_ERR_BAD_SHAPE, "token stride %lld below the row width %lld",
+                        (long long)*sts[i], (long long)need[i]);
+    }
+    const int eb = elt_bytes(c.dtype);
+    const int64_t out_rows = c.slot ? c.n_slots : c.T;
+    auto view = [&](const void* p, int64_t st, int64_t len, int64_t rows, const char* n) {
+        return View{(const char*)p, mul(st, eb), mul(len, eb), rows, n};
+    };
+    const View qi = view(c.Q ? c.q_in : nullptr, c.q_in_st, qrow, c.T, "q_in");
+    const View ki = view(c.K ? c.k_in : nullptr, c.k_in_st, krow, c.T, "k_in");
+    const View vi = view(has_v ? c.v_in : nullptr, c.v_in_st, krow, c.T, "v_in");
+    const View qo = view(c.Q ? c.q_out : nullptr, c.q_out_st, qrow, c.T, "q_out");
+    const View ko = view(c.K ? c.k_out : nullptr, c.k_out_st, krow, out_rows, "k_out");
+    const View vo = view(has_v ? c.v_out : nullptr, c.v_out_st, krow, out_rows, "v_out");
+    const int64_t cs_bytes = mul(mul(c.max_pos, c.rot), 4);
+    for (const View* v : {&qi, &ki, &vi, &qo, &ko, &vo})
+        if (v->stride < 0 || v->len < 0 || (v->rows > 0 && mul(v->rows, v->stride) < 0))
+            return fail(MBT_ERR_BAD_SHAPE, "tensor sizes overflow");
+    if (cs_bytes < 0 || mul(c.T, c.Q + c.K) > (INT64_C(1) << 40))
+        return fail(MBT_ERR_BAD_SHAPE, "tensor sizes overflow");
+    if (c.T == 0) return ok();
+    const bool need_cache = c.rot > 0 && c.max_pos > 0;
+    if (c.Q > 0 && (!c.q_in || !c.q_out || !c.w_q))
+        return fail(MBT_ERR_NULL_POINTER, "q_in, q_out and w_q are required when Q > 0");
+    if (c.K > 0 && (!c.k_in || !c.k_out || !c.w_k))
+        return fail(MBT_ERR_NULL_POINTER, "k_in, k_out and w_k are required when K > 0");
+    if (has_v && (!c.v_in || !c.v_out))
+        return fail(MBT_ERR_NULL_POINTER, "v_in and v_out go together");
+    if (!c.pos) return fail(MBT_ERR_NULL_POINTER, "pos is required");
+    if (need_cache && !c.cos_sin)
+        return fail(MBT_ERR_NULL_POINTER, "cos_sin is required when rot_dim > 0");
+    if ((c.Q > 0 && (!aligned(c.q_in, eb) || !aligned(c.q_out, eb) || !aligned(c.w_q, eb))) ||
+        (c.K > 0 && (!aligned(c.k_in, eb) || !aligned(c.k_out, eb) || !aligned(c.w_k, eb))) ||
+        (has_v && (!aligned(c.v_in, eb) || !aligned(c.v_out, eb))) || !aligned(c.pos, 8) ||
+        (c.slot && !aligned(c.slot, 8)) || (need_cache && !aligned(c.cos_sin, 4)))
+        return fail(MBT_ERR_ALIGN, "a pointer is not aligned to its element size");
+    const int64_t w_bytes = (int64_t)c.D * eb;
+    const View wq{(const char*)(c.Q ? c.w_q : nullptr), w_bytes, w_bytes, 1, "w_q"};
+    const View wk{(const char*)(c.K ? c.w_k : nullptr), w_bytes, w_bytes, 1, "w_k"};
+    const View cs{(const char*)(need_cache ? c.cos_sin : nullptr), cs_bytes, cs_bytes, 1,
+                  "cos_sin"};
+    const View ps{(const char*)c.pos, c.T * 8, c.T * 8, 1, "pos"};
+    const View sl{(const char*)c.slot, c.T * 8, c.T * 8, 1, "slot"};
+    const View* ins[] = {&qi, &ki, &vi, &wq, &wk, &cs, &ps, &sl};
+    const View* outs[] = {&qo, &ko, &vo};
+    for (const View* o : outs) {
+        for (const View* i : ins) {
+            // the in-place form: an output exactly on the input it replaces
+            // (not through a slot table, which could move rows onto others)
+            const bool same_ok = !c.slot && ((o == &qo && i == &qi) || (o == &ko && i == &ki) ||
+                                             (o == &vo && i == &vi));
+            if (views_overlap(*o, *i) && !(same_ok && same_view(*o, *i)))
+                return fail(MBT_ERR_ALIAS, "%s overlaps %s", o->name, i->name);
+        }
+    }
+    if (views_overlap(qo, ko) || views_overlap(qo, vo) || views_overlap(ko, vo))
+        return fail(MBT_ERR_ALIAS, "the outputs overlap each other");
+
+    mbt::QkArgs a{};
+    a.q_in = c.q_in; a.k_in = c.k_in; a.q_out = c.q_out; a.k_out = c.k_out;
+    a.w_q = c.w_q; a.w_k = c.w_k; a.cos_sin = c.cos_sin; a.max_pos = c.max_pos; a.pos = c.pos;
+    a.Q = c.Q; a.K = c.K; a.T = c.T; a.head_dim = c.D; a.rot_dim = c.rot; a.eps = c.eps;
+    a.weight_offset = c.weight_offset; a.layout = c.layout; a.dtype = c.dtype;
+    a.q_in_stride = c.q_in_st; a.k_in_stride = c.k_in_st;
+    a.q_out_stride = c.q_out_st; a.k_out_stride = c.k_out_st;
+    a.round_once = (c.flags & MBT_QK_ROUND_ONCE) != 0;
+    a.slot = c.slot; a.n_slots = c.n_slots;
+    a.v_in = has_v ? c.v_in : nullptr; a.v_out = has_v ? c.v_out : nullptr;
+    a.v_in_stride = c.v_in_st; a.v_out_stride = c.v_out_st;
+    return hip_status(mbt::launch_qknorm_rope(a, (hipStream_t)stream), "qknorm_rope launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,60 +258,60 @@ mbt_status mbt_qknorm_rope(const void* q_in, const void* k_in, void* q_out, void
                            int64_t T, int32_t head_dim, int32_t rot_dim, float eps,
                            int32_t weight_offset, int32_t layout, int32_t dtype,
                            void* stream) {
+    QkCall c{};
+    c.q_in = q_in; c.k_in = k_in; c.q_out = q_out; c.k_out = k_out; c.w_q = w_q; c.w_k = w_k;
+    c.cos_sin = cos_sin; c.max_pos = max_pos; c.pos = pos; c.Q = Q; c.K = K; c.T = T;
+    c.D = head_dim; c.rot = rot_dim; c.eps = eps; c.weight_offset = weight_offset;
+    c.layout = layout; c.dtype = dtype;
+    return qk_run(c, stream);
+}
+
+mbt_status mbt_qknorm_rope_ex(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                              const void* w_q, const void* w_k, const float* cos_sin,
+                              int64_t max_pos, const int64_t* pos, int32_t Q, int32_t K,
+                              int64_t T, int32_t head_dim, int32_t rot_dim, float eps,
+                              int32_t weight_offset, int32_t layout, int32_t dtype,
+                              int64_t q_in_stride, int64_t k_in_stride, int64_t q_out_stride,
+                              int64_t k_out_stride, int32_t flags, void* stream) {
+    QkCall c{};
+    c.q_in = q_in; c.k_in = k_in; c.q_out = q_out; c.k_out = k_out; c.w_q = w_q; c.w_k = w_k;
+    c.cos_sin = cos_sin; c.max_pos = max_pos; c.pos = pos; c.Q = Q; c.K = K; c.T = T;
+    c.D = head_dim; c.rot = rot_dim; c.eps = eps; c.weight_offset = weight_offset;
+    c.layout = layout; c.dtype = dtype; c.flags = flags;
+    c.q_in_st = q_in_stride; c.k_in_st = k_in_stride;
+    c.q_out_st = q_out_stride; c.k_out_st = k_out_stride;
+    if (q_in_stride < 0 || k_in_stride < 0 || q_out_stride < 0 || k_out_stride < 0)
+        return fail(MBT_ERR_BAD_SHAPE, "negative token stride");
+    return qk_run(c, stream);
+}
+
+mbt_status mbt_qkv_norm_rope_cache(const void* qkv, void* q_out, void* k_cache, void* v_cache,
+                                   const int64_t* slot, int64_t n_slots, const void* w_q,
+                                   const void* w_k, const float* cos_sin, int64_t max_pos,
+                                   const int64_t* pos, int32_t Q, int32_t K, int64_t T,
+                                   int32_t head_dim, int32_t rot_dim, float eps,
+                                   int32_t weight_offset, int32_t layout, int32_t dtype,
+                                   int32_t flags, void* stream) {
     if (!valid_dtype(dtype)) return fail(MBT_ERR_BAD_DTYPE, "dtype %d", dtype);
-    if (layout != MBT_ROPE_ROTATE_HALF && layout != MBT_ROPE_INTERLEAVED)
-        return fail(MBT_ERR_BAD_ENUM, "layout %d", layout);
-    if (weight_offset != 0 && weight_offset != 1)
-        return fail(MBT_ERR_BAD_ENUM, "weight_offset %d", weight_offset);
-    if (Q < 0 || K < 0 || Q + K < 1) return fail(MBT_ERR_BAD_SHAPE, "Q=%d K=%d", Q, K);
-    if (T < 0) return fail(MBT_ERR_BAD_SHAPE, "T=%lld", (long long)T);
+    if (K < 1 || Q < 0) return fail(MBT_ERR_BAD_SHAPE, "Q=%d K=%d (a cache needs K >= 1)", Q, K);
     if (head_dim < 1 || head_dim > 512)
         return fail(MBT_ERR_BAD_SHAPE, "head_dim %d not in [1, 512]", head_dim);
-    if (rot_dim < 0 || rot_dim > head_dim || (rot_dim % 2) != 0)
-        return fail(MBT_ERR_BAD_SHAPE, "rot_dim %d (head_dim %d)", rot_dim, head_dim);
-    if (!finite_nonneg(eps)) return fail(MBT_ERR_BAD_SCALAR, "eps must be finite and >= 0");
-    if (max_pos < 0) return fail(MBT_ERR_BAD_SCALAR, "max_pos %lld", (long long)max_pos);
+    if (T > 0 && (!qkv || !k_cache || !v_cache || !slot))
+        return fail(MBT_ERR_NULL_POINTER, "qkv, k_cache, v_cache and slot are required");
     const int eb = elt_bytes(dtype);
-    const int64_t q_bytes = mul(mul(mul(T, Q), head_dim), eb);
-    const int64_t k_bytes = mul(mul(mul(T, K), head_dim), eb);
-    const int64_t cs_bytes = mul(mul(max_pos, rot_dim), 4);
-    if (q_bytes < 0 || k_bytes < 0 || cs_bytes < 0 || mul(T, Q + K) > (INT64_C(1) << 40))
-        return fail(MBT_ERR_BAD_SHAPE, "tensor sizes overflow");
-    if (T == 0) return ok();
-    const bool need_cache = rot_dim > 0 && max_pos > 0;
-    if (Q > 0 && (!q_in || !q_out || !w_q))
-        return fail(MBT_ERR_NULL_POINTER, "q_in, q_out and w_q are required when Q > 0");
-    if (K > 0 && (!k_in || !k_out || !w_k))
-        return fail(MBT_ERR_NULL_POINTER, "k_in, k_out and w_k are required when K > 0");
-    if (!pos) return fail(MBT_ERR_NULL_POINTER, "pos is required");
-    if (need_cache && !cos_sin)
-        return fail(MBT_ERR_NULL_POINTER, "cos_sin is required when rot_dim > 0");
-    if ((Q > 0 && (!aligned(q_in, eb) || !aligned(q_out, eb) || !aligned(w_q, eb))) ||
-        (K > 0 && (!aligned(k_in, eb) || !aligned(k_out, eb) || !aligned(w_k, eb))) ||
-        !aligned(pos, 8) || (need_cache && !aligned(cos_sin, 4)))
-        return fail(MBT_ERR_ALIGN, "a pointer is not aligned to its element size");
-    const int64_t w_bytes = (int64_t)head_dim * eb;
-    const Range qi{(const char*)(Q ? q_in : nullptr), q_bytes, "q_in"};
-    const Range ki{(const char*)(K ? k_in : nullptr), k_bytes, "k_in"};
-    const Range qo{(const char*)(Q ? q_out : nullptr), q_bytes, "q_out"};
-    const Range ko{(const char*)(K ? k_out : nullptr), k_bytes, "k_out"};
-    const Range wq{(const char*)(Q ? w_q : nullptr), w_bytes, "w_q"};
-    const Range wk{(const char*)(K ? w_k : nullptr), w_bytes, "w_k"};
-    const Range cs{(const char*)(need_cache ? cos_sin : nullptr), cs_bytes, "cos_sin"};
-    const Range ps{(const char*)pos, T * 8, "pos"};
-    const Range* ins[] = {&qi, &ki, &wq, &wk, &cs, &ps};
-    for (const Range* o : {&qo, &ko}) {
-        for (const Range* i : ins) {
-            const bool same_ok = (o == &qo && i == &qi) || (o == &ko && i == &ki);
-            mbt_status st = check_alias(*o, *i, same_ok);
-            if (st != MBT_OK) return st;
-        }
-    }
-    if (overlap(qo, ko)) return fail(MBT_ERR_ALIAS, "q_out overlaps k_out");
-
-    mbt::QkArgs a{q_in, k_in, q_out, k_out, w_q, w_k, cos_sin, max_pos, pos, Q, K, T,
-                  head_dim, rot_dim, eps, weight_offset, layout, dtype};
-    return hip_status(mbt::launch_qknorm_rope(a, (hipStream_t)stream), "qknorm_rope launch");
+    const char* base = (const char*)qkv;
+    const int64_t tok = (int64_t)(Q + 2 * K) * head_dim;        // elements per token
+    QkCall c{};
+    c.q_in = base; c.k_in = base ? base + (int64_t)Q * head_dim * eb : nullptr;
+    c.v_in = base ? base + (int64_t)(Q + K) * head_dim * eb : nullptr;
+    c.q_out = q_out; c.k_out = k_cache; c.v_out = v_cache;
+    c.w_q = w_q; c.w_k = w_k; c.cos_sin = cos_sin; c.max_pos = max_pos; c.pos = pos;
+    c.Q = Q; c.K = K; c.T = T; c.D = head_dim; c.rot = rot_dim; c.eps = eps;
+    c.weight_offset = weight_offset; c.layout = layout; c.dtype = dtype; c.flags = flags;
+    c.q_in_st = tok; c.k_in_st = tok; c.v_in_st = tok;
+    c.slot = slot; c.n_slots = n_slots;
+    if (T == 0) c.v_in = c.v_out = nullptr;
+    return qk_run(c, stream);
 }
 
 mbt_status mbt_rope(void* q, void* k, const float* cos_sin, int64_t max_pos, const int64_t* pos,

@@ -25,6 +25,17 @@ struct QkArgs {
     int32_t head_dim, rot_dim;
     float eps;
     int32_t weight_offset, layout, dtype;
+    // token strides in elements (dense: heads * head_dim)
+    int64_t q_in_stride, k_in_stride, q_out_stride, k_out_stride;
+    bool round_once;
+    // key / value rows of token t go to row slot[t] of k_out / v_out when
+    // slot is given (rows outside [0, n_slots) are not written)
+    const int64_t* slot;
+    int64_t n_slots;
+    // value rows copied unchanged (NULL v_in: none)
+    const void* v_in;
+    void* v_out;
+    int64_t v_in_stride, v_out_stride;
 };
 
 enum NormOut : int { kNormInPlace = 0, kNormFp8 = 1, kNormAmax = 2 };

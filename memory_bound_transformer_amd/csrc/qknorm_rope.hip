@@ -67,17 +67,59 @@ struct QkParams {
     int32_t layout;           // 0 rotate-half, 1 interleaved
     float inv_Q, inv_K;       // vector kernel: 1/Q, 1/K for the token index
     uint32_t q_waves;         // vector kernel: waves over the T*Q query rows
-    uint32_t total_waves;     // vector kernel: q_waves + waves over key rows
+    uint32_t qk_waves;        // vector kernel: q_waves + waves over the key rows
+    uint32_t total_waves;     // vector kernel: qk_waves + waves over the value rows
     uint32_t n_blocks;
 };
 
+// The general forms' extra arguments (token strides, slot table, value rows,
+// single rounding).  A second kernel argument, so the dense kernel keeps the
+// small argument block it measured fastest with at decode widths.
+template <bool GEN>
+struct QkGen {
+    int32_t once;             // 1: rotate the fp32 norm result, round once
+    const void* v_in;         // NULL: no value rows
+    void* v_out;
+    const int64_t* slot;      // NULL: key / value rows of token t go to row t
+    int64_t n_slots;          // rows of k_out / v_out when slot != NULL
+    int64_t q_in_st, k_in_st, v_in_st, q_out_st, k_out_st, v_out_st;   // token strides
+};
+template <>
+struct QkGen<false> {};
+
+// Output row of token t for a key or value row: slot[t] when a slot table is
+// given (-1: not written, e.g. padding), else t.
+__device__ __forceinline__ int64_t out_row(const QkGen<true>& g, bool slotted, int64_t t) {
+    if (!slotted) return t;
+    const int64_t s = g.slot[t];
+    return (s >= 0 && s < g.n_slots) ? s : -1;
+}
+
+// The V fp32 values of the rotate-half partner lane (hv lanes away).
+template <int V>
+__device__ __forceinline__ void partner_f32(const float* n, float* nb, int hv, bool is_a) {
+#pragma unroll
+    for (int h0 = 0; h0 < V; h0 += 4) {
+        const u32x4 v{__float_as_uint(n[h0]), __float_as_uint(n[h0 + 1]),
+                      __float_as_uint(n[h0 + 2]), __float_as_uint(n[h0 + 3])};
+        const u32x4 r = rot_partner(v, hv, is_a);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nb[h0 + i] = __uint_as_float(r[i]);
+    }
+}
+
 // Vector kernel.  DT: dtype; G: lanes per head-row; C: chunks per lane
-// (G * C * Vec<DT> = D); LAYOUT: rotary pairing.  Requires 16-byte aligned
-// q / k / w tensors, every rotated chunk inside chunk group 0, rows of each
-// tensor below 2^24, and for rotate-half rot/2 a multiple of Vec<DT> and a
-// 16-byte aligned cos/sin cache (interleaved reads its run element-wise).
-template <int DT, int G, int C, int LAYOUT>
-__global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
+// (G * C * Vec<DT> = D); LAYOUT: rotary pairing; GEN: false for dense q / k
+// with the contract's rounding (the hot path: none of the code below that
+// serves the other forms is compiled in), true for token strides, the slot
+// table, value rows and the single-rounding flag.  Requires 16-byte aligned
+// tensors and token strides, every rotated chunk inside chunk group 0, rows
+// of each tensor below 2^24, and for rotate-half rot/2 a multiple of
+// Vec<DT> and a 16-byte aligned cos/sin cache (interleaved reads its run
+// element-wise).  Waves cover the query rows, then the key rows, then (when
+// v_in is given) the value rows, which are copied unchanged to their slot.
+template <int DT, int G, int C, int LAYOUT, bool GEN>
+__global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g) {
     constexpr int V = Vec<DT>::n;
     constexpr int RPW = kWave / G;     // rows per wave
     constexpr int EB = EltBytes<DT>::n;
@@ -88,13 +130,23 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
     const uint32_t lb = xcd_remap(blockIdx.x, p.n_blocks);
     const uint32_t wv = (uint32_t)uniform((int)(lb * 4u + (threadIdx.x >> 6)));
     const bool wave_live = wv < p.total_waves;
-    const bool is_q = wv < p.q_waves;                       // wave-uniform tensor
+    // wave-uniform kind: 0 query rows, 1 key rows, 2 value rows (GEN only)
+    const bool is_q = wv < p.q_waves;
+    const int kind = is_q ? 0 : ((!GEN || wv < p.qk_waves) ? 1 : 2);
     const int heads = is_q ? p.Q : p.K;
     const float inv_heads = is_q ? p.inv_Q : p.inv_K;
     const int64_t nrows = wave_live ? p.T * heads : 0;
-    const int64_t row0 = (int64_t)(is_q ? wv : wv - p.q_waves) * RPW;
+    int64_t row0 = (int64_t)(is_q ? wv : wv - p.q_waves) * RPW;
+    if constexpr (GEN)
+        if (kind == 2) row0 = (int64_t)(wv - p.qk_waves) * RPW;
     const char* src = (const char*)(is_q ? p.q_in : p.k_in);
     char* dst = (char*)(is_q ? p.q_out : p.k_out);
+    if constexpr (GEN) {
+        if (kind == 2) {
+            src = (const char*)g.v_in;
+            dst = (char*)g.v_out;
+        }
+    }
     const char* wp = (const char*)(is_q ? p.w_q : p.w_k);
 
     const int lane = threadIdx.x & 63;
@@ -107,18 +159,39 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
     const bool is_b = LAYOUT == 0 && j >= hv && j < 2 * hv;
 
     // ---- issue every independent load before any arithmetic ----
-    const char* rsrc = src + row * (int64_t)p.D * EB;
-    u32x4 x[C];
-#pragma unroll
-    for (int k = 0; k < C; ++k)
-        x[k] = live ? ld16_nt(rsrc + (k * G + j) * 16) : u32x4{0u, 0u, 0u, 0u};
-    // token of the row: float reciprocal, then one correction each way
+    // The row's token t and head h come from a float reciprocal and one
+    // correction.  Dense rows are addressed as row * D, so their loads go out
+    // first and t is formed while they fly; strided and slotted rows need t
+    // and h for the address itself.
     const uint32_t r32 = live ? (uint32_t)row : 0u;
-    int32_t t = (int32_t)((float)r32 * inv_heads);
-    const int32_t rem = (int32_t)r32 - t * heads;
-    t += (rem >= heads) ? 1 : 0;
-    t -= (rem < 0) ? 1 : 0;
-    const int64_t ppos = live ? p.pos[t] : -1;
+    int32_t t = 0;
+    int64_t out_off = row * p.D, orow = 0;
+    u32x4 x[C];
+    if constexpr (!GEN) {
+        const char* rsrc = src + row * (int64_t)p.D * EB;
+#pragma unroll
+        for (int k = 0; k < C; ++k)
+            x[k] = live ? ld16_nt(rsrc + (k * G + j) * 16) : u32x4{0u, 0u, 0u, 0u};
+        t = (int32_t)((float)r32 * inv_heads);
+        const int32_t rem = (int32_t)r32 - t * heads;
+        t += (rem >= heads) ? 1 : 0;
+        t -= (rem < 0) ? 1 : 0;
+        orow = live ? t : -1;
+    } else {
+        t = (int32_t)((float)r32 * inv_heads);
+        int32_t h = (int32_t)r32 - t * heads;
+        if (h >= heads) { t += 1; h -= heads; }
+        if (h < 0) { t -= 1; h += heads; }
+        const int64_t in_st = kind == 0 ? g.q_in_st : kind == 1 ? g.k_in_st : g.v_in_st;
+        const int64_t out_st = kind == 0 ? g.q_out_st : kind == 1 ? g.k_out_st : g.v_out_st;
+        const char* rsrc = src + ((int64_t)t * in_st + (int64_t)h * p.D) * EB;
+#pragma unroll
+        for (int k = 0; k < C; ++k)
+            x[k] = live ? ld16_nt(rsrc + (k * G + j) * 16) : u32x4{0u, 0u, 0u, 0u};
+        orow = live ? out_row(g, kind != 0 && g.slot != nullptr, t) : -1;
+        out_off = (orow >= 0 ? orow : 0) * out_st + (int64_t)h * p.D;
+    }
+    const int64_t ppos = (live && kind != 2) ? p.pos[t] : -1;
     float wreg[C >= 2 ? 1 : V];
     if constexpr (C >= 2) {
         for (int i = threadIdx.x; i < p.D; i += 256) {
@@ -127,11 +200,21 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
         }
         __syncthreads();                                   // x loads already in flight
     } else {
-        unpack<DT>(wave_live ? ld16(wp + j * 16) : u32x4{0u, 0u, 0u, 0u}, wreg);
+        unpack<DT>((wave_live && kind != 2) ? ld16(wp + j * 16) : u32x4{0u, 0u, 0u, 0u}, wreg);
 #pragma unroll
         for (int i = 0; i < V; ++i) wreg[i] += p.delta;
     }
     if (!wave_live) return;
+    char* rdst = dst + out_off * EB;
+    if constexpr (GEN) {
+        if (kind == 2) {                                   // value rows: copy to the slot
+            if (orow >= 0) {
+#pragma unroll
+                for (int k = 0; k < C; ++k) st16_nt(rdst + (k * G + j) * 16, x[k]);
+            }
+            return;
+        }
+    }
     const bool rotate = (ppos >= 0) && (ppos < p.max_pos) && (p.rot > 0);
     float cs_c[V], cs_s[V];
     bool lane_rot = false;
@@ -183,7 +266,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
     const float inv = inv_rms(ss, p.inv_D, p.eps);
 
     // ---- normalise, round, rotate (group 0 only), store ----
-    char* rdst = dst + row * (int64_t)p.D * EB;
+    const bool keep = orow >= 0;
     const float* wrow = wsh[(C >= 2 && !is_q) ? 1 : 0];
 #pragma unroll
     for (int k = 0; k < C; ++k) {
@@ -199,20 +282,30 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
         }
         u32x4 out = pack<DT>(n);                            // R(n): the rounded value
         if (k == 0) {
+            // the rotation's inputs: R(n) (the contract) or n itself (once)
+            bool once = false;
+            if constexpr (GEN) once = g.once != 0;
+            float a[V], o[V];
+            if (once) {
+#pragma unroll
+                for (int i = 0; i < V; ++i) a[i] = n[i];
+            } else {
+                unpack<DT>(out, a);
+            }
             if constexpr (LAYOUT == 0) {
-                const u32x4 pb = rot_partner(out, hv, is_a);
+                float b[V];
+                if (once) {
+                    partner_f32<V>(n, b, hv, is_a);
+                } else {
+                    unpack<DT>(rot_partner(out, hv, is_a), b);
+                }
                 if (lane_rot) {
-                    float a[V], b[V], o[V];
-                    unpack<DT>(out, a);
-                    unpack<DT>(pb, b);
 #pragma unroll
                     for (int i = 0; i < V; ++i) o[i] = rot_mac(a[i], cs_c[i], b[i], cs_s[i]);
                     out = pack<DT>(o);
                 }
             } else {
                 if (lane_rot) {
-                    float a[V], o[V];
-                    unpack<DT>(out, a);
 #pragma unroll
                     for (int i = 0; i < V / 2; ++i) {
                         o[2 * i] = rot_mac(a[2 * i], cs_c[i], a[2 * i + 1], -cs_s[i]);
@@ -222,33 +315,40 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p) {
                 }
             }
         }
-        if (live) st16_nt(rdst + (k * G + j) * 16, out);
+        if (keep) st16_nt(rdst + (k * G + j) * 16, out);
     }
 }
 
-// Scalar kernel: any D <= 512, any even rot, element-aligned pointers.  One
-// wave per head-row (4 rows per 256-thread block).  Lane c owns chunk c
-// (Vec<DT> consecutive elements; lane c + 64 too for fp32 rows past 256), so
-// the sum of squares follows the vector kernels' tree (zero lanes add
-// nothing); the rounded normalised row is staged in LDS for the rotation.
+// Scalar kernel: any D <= 512, any even rot, element-aligned pointers and
+// strides.  One wave per head-row (4 rows per 256-thread block); a token's
+// rows are its Q query heads, its K key heads, then (with v_in) its K value
+// heads, which are copied to their slot.  Lane c owns chunk c (Vec<DT>
+// consecutive elements; lane c + 64 too for fp32 rows past 256), so the sum
+// of squares follows the vector kernels' tree (zero lanes add nothing); the
+// normalised row (rounded, or not for the single-rounding variant) is staged
+// in LDS for the rotation.
 template <int DT>
-__global__ __launch_bounds__(256) void qknorm_rope_scalar(QkParams p) {
+__global__ __launch_bounds__(256) void qknorm_rope_scalar(QkParams p, QkGen<true> g) {
     constexpr int V = Vec<DT>::n;
     constexpr int CPL = (512 / V + kWave - 1) / kWave;      // chunks per lane
     __shared__ float stage[4][512];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + w;
-    const int QK = p.Q + p.K;
-    const int64_t rows = p.T * QK;
+    const int per_t = p.Q + p.K + (g.v_in ? p.K : 0);
+    const int64_t rows = p.T * per_t;
     const bool live = row < rows;
-    const int64_t t = live ? row / QK : 0;
-    const int h = live ? (int)(row % QK) : 0;
-    const bool is_q = h < p.Q;
-    const void* src = is_q ? p.q_in : p.k_in;
-    void* dst = is_q ? p.q_out : p.k_out;
-    const void* wp = is_q ? p.w_q : p.w_k;
-    const int64_t base = is_q ? (t * p.Q + h) * (int64_t)p.D
-                              : (t * p.K + (h - p.Q)) * (int64_t)p.D;
+    const int64_t t = live ? row / per_t : 0;
+    const int hh = live ? (int)(row % per_t) : 0;
+    const int kind = hh < p.Q ? 0 : (hh < p.Q + p.K ? 1 : 2);
+    const int h = kind == 0 ? hh : (kind == 1 ? hh - p.Q : hh - p.Q - p.K);
+    const void* src = kind == 0 ? p.q_in : kind == 1 ? p.k_in : g.v_in;
+    void* dst = kind == 0 ? p.q_out : kind == 1 ? p.k_out : g.v_out;
+    const int64_t in_st = kind == 0 ? g.q_in_st : kind == 1 ? g.k_in_st : g.v_in_st;
+    const int64_t out_st = kind == 0 ? g.q_out_st : kind == 1 ? g.k_out_st : g.v_out_st;
+    const void* wp = kind == 0 ? p.w_q : p.w_k;
+    const int64_t ibase = t * in_st + (int64_t)h * p.D;
+    const int64_t orow = live ? out_row(g, kind != 0 && g.slot != nullptr, t) : -1;
+    const int64_t obase = (orow >= 0 ? orow : 0) * out_st + (int64_t)h * p.D;
     float f[CPL][V];
     float ss = 0.0f;
 #pragma unroll
@@ -257,24 +357,39 @@ __global__ __launch_bounds__(256) void qknorm_rope_scalar(QkParams p) {
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             const int e = c * V + i;
-            f[k][i] = (live && e < p.D) ? ld_elt<DT>(src, base + e) : 0.0f;
+            f[k][i] = (live && e < p.D) ? ld_elt<DT>(src, ibase + e) : 0.0f;
         }
         // 64-chunk groups reduce on their own, then add: the canonical tree
         const float part = seg_sum<64>(chunk_sumsq<DT>(f[k]));
         ss = (k == 0) ? part : ss + part;
     }
     const float inv = inv_rms(ss, p.inv_D, p.eps);
+    if (kind != 2) {
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
+        for (int k = 0; k < CPL; ++k) {
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-            const int e = (lane + k * kWave) * V + i;
-            if (live && e < p.D)
-                stage[w][e] = round_trip<DT>((f[k][i] * inv) * (ld_elt<DT>(wp, e) + p.delta));
+            for (int i = 0; i < V; ++i) {
+                const int e = (lane + k * kWave) * V + i;
+                if (live && e < p.D) {
+                    const float n = (f[k][i] * inv) * (ld_elt<DT>(wp, e) + p.delta);
+                    stage[w][e] = g.once ? n : round_trip<DT>(n);
+                }
+            }
         }
     }
     __syncthreads();
-    if (!live) return;
+    if (!live || orow < 0) return;
+    if (kind == 2) {                                       // value row: copy the bits
+        for (int e = lane; e < p.D; e += kWave) {
+            if constexpr (DT == kF32)
+                reinterpret_cast<uint32_t*>(dst)[obase + e] =
+                    reinterpret_cast<const uint32_t*>(src)[ibase + e];
+            else
+                reinterpret_cast<uint16_t*>(dst)[obase + e] =
+                    reinterpret_cast<const uint16_t*>(src)[ibase + e];
+        }
+        return;
+    }
     const int64_t ppos = p.pos[t];
     const bool rotate = (ppos >= 0) && (ppos < p.max_pos) && (p.rot > 0);
     const int half = p.rot >> 1;
@@ -296,7 +411,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_scalar(QkParams p) {
             o = (e == a) ? rot_mac(stage[w][a], c, stage[w][b], -s)
                          : rot_mac(stage[w][b], c, stage[w][a], s);
         }
-        st_elt<DT>(dst, base + e, o);
+        st_elt<DT>(dst, obase + e, o);
     }
 }
 
@@ -315,25 +430,30 @@ int tun_c_max() {
     return v;
 }
 
-template <int DT, int G, int C, int LAYOUT>
-hipError_t launch_vec(const QkParams& p0, hipStream_t s) {
+template <int DT, int G, int C, int LAYOUT, bool GEN>
+hipError_t launch_vec(const QkParams& p0, const QkGen<true>& g0, hipStream_t s) {
     QkParams p = p0;
     constexpr int RPW = kWave / G;
     const int64_t qw = (p.T * p.Q + RPW - 1) / RPW;
     const int64_t kw = (p.T * p.K + RPW - 1) / RPW;
+    const int64_t vw = (GEN && g0.v_in) ? kw : 0;
+    if (qw + kw + vw > 0x7FFFFFFFll) return hipErrorInvalidValue;
     p.q_waves = (uint32_t)qw;
-    p.total_waves = (uint32_t)(qw + kw);
+    p.qk_waves = (uint32_t)(qw + kw);
+    p.total_waves = (uint32_t)(qw + kw + vw);
     p.n_blocks = (p.total_waves + 3u) / 4u;
-    hipLaunchKernelGGL((qknorm_rope_vec<DT, G, C, LAYOUT>), dim3(p.n_blocks), dim3(256), 0, s,
-                       p);
+    QkGen<GEN> g{};
+    if constexpr (GEN) g = g0;
+    hipLaunchKernelGGL((qknorm_rope_vec<DT, G, C, LAYOUT, GEN>), dim3(p.n_blocks), dim3(256), 0,
+                       s, p, g);
     return hipGetLastError();
 }
 
 // (G, C) with G * C = L lanes-of-chunks per row; G a power of two >= 4.
-template <int DT, int LAYOUT>
-hipError_t launch_gc(const QkParams& p, int L, int C, hipStream_t s) {
+template <int DT, int LAYOUT, bool GEN>
+hipError_t launch_gc(const QkParams& p, const QkGen<true>& g, int L, int C, hipStream_t s) {
 #define MBT_QK_CASE(LL, CC)                                              \
-    if (L == LL && C == CC) return launch_vec<DT, LL / CC, CC, LAYOUT>(p, s);
+    if (L == LL && C == CC) return launch_vec<DT, LL / CC, CC, LAYOUT, GEN>(p, g, s);
     MBT_QK_CASE(4, 1)
     MBT_QK_CASE(8, 1) MBT_QK_CASE(8, 2)
     MBT_QK_CASE(16, 1) MBT_QK_CASE(16, 2) MBT_QK_CASE(16, 4)
@@ -346,24 +466,38 @@ hipError_t launch_gc(const QkParams& p, int L, int C, hipStream_t s) {
 template <int DT>
 hipError_t launch_dt(const QkArgs& a, hipStream_t s) {
     constexpr int V = Vec<DT>::n;
+    constexpr int EB = EltBytes<DT>::n;
     QkParams p{};
     p.q_in = a.q_in; p.k_in = a.k_in; p.q_out = a.q_out; p.k_out = a.k_out;
     p.w_q = a.w_q; p.w_k = a.w_k; p.cos_sin = a.cos_sin; p.pos = a.pos;
+    QkGen<true> g{};
+    g.v_in = a.v_in; g.v_out = a.v_out; g.slot = a.slot; g.n_slots = a.n_slots;
+    g.q_in_st = a.q_in_stride; g.k_in_st = a.k_in_stride; g.v_in_st = a.v_in_stride;
+    g.q_out_st = a.q_out_stride; g.k_out_st = a.k_out_stride; g.v_out_st = a.v_out_stride;
+    g.once = a.round_once ? 1 : 0;
     p.max_pos = a.max_pos; p.T = a.T; p.Q = a.Q; p.K = a.K; p.D = a.head_dim;
     p.rot = a.rot_dim; p.eps = a.eps; p.inv_D = 1.0f / (float)a.head_dim;
     p.delta = (float)a.weight_offset;
     p.layout = a.layout;
 
-    // Vector path conditions.
+    // Vector path conditions: 16-byte chunks everywhere, rows of each tensor
+    // below 2^24 (the token index uses a float reciprocal).
+    auto st16 = [](int64_t st) { return (st * EB) % 16 == 0; };
     const int L = a.head_dim / V;
     bool vec = (a.head_dim % V == 0) && (L == 4 || L == 8 || L == 16 || L == 32 || L == 64);
-    vec = vec && aligned16(a.q_in) && aligned16(a.k_in) && aligned16(a.q_out) &&
-          aligned16(a.k_out) && aligned16(a.w_q) && aligned16(a.w_k);
+    if (a.Q > 0)
+        vec = vec && aligned16(a.q_in) && aligned16(a.q_out) && aligned16(a.w_q) &&
+              st16(a.q_in_stride) && st16(a.q_out_stride);
+    if (a.K > 0)
+        vec = vec && aligned16(a.k_in) && aligned16(a.k_out) && aligned16(a.w_k) &&
+              st16(a.k_in_stride) && st16(a.k_out_stride);
+    if (a.v_in)
+        vec = vec && aligned16(a.v_in) && aligned16(a.v_out) && st16(a.v_in_stride) &&
+              st16(a.v_out_stride);
     if (a.rot_dim > 0 && a.max_pos > 0 && a.layout == 0)
         vec = vec && ((a.rot_dim / 2) % V == 0) && aligned16(a.cos_sin);
     const int QK = a.Q + a.K;
     const int64_t rows = a.T * (int64_t)QK;
-    // rows of each tensor below 2^24: the token index uses a float reciprocal
     vec = vec && a.T * (int64_t)(a.Q > a.K ? a.Q : a.K) < (int64_t(1) << 24);
     if (vec) {
         // Chunks per lane: 1 at decode widths; at prefill widths up to 4,
@@ -380,11 +514,21 @@ hipError_t launch_dt(const QkArgs& a, hipStream_t s) {
         }
         p.inv_Q = a.Q > 0 ? 1.0f / (float)a.Q : 0.0f;
         p.inv_K = a.K > 0 ? 1.0f / (float)a.K : 0.0f;
-        return (a.layout == 0) ? launch_gc<DT, 0>(p, L, C, s) : launch_gc<DT, 1>(p, L, C, s);
+        // the general kernel only where a stride, slot, value row or the
+        // single-rounding flag asks for it
+        const int64_t qrow = (int64_t)a.Q * a.head_dim, krow = (int64_t)a.K * a.head_dim;
+        const bool gen = a.round_once || a.slot || a.v_in ||
+                         (a.Q > 0 && (a.q_in_stride != qrow || a.q_out_stride != qrow)) ||
+                         (a.K > 0 && (a.k_in_stride != krow || a.k_out_stride != krow));
+        if (gen)
+            return (a.layout == 0) ? launch_gc<DT, 0, true>(p, g, L, C, s)
+                                   : launch_gc<DT, 1, true>(p, g, L, C, s);
+        return (a.layout == 0) ? launch_gc<DT, 0, false>(p, g, L, C, s)
+                               : launch_gc<DT, 1, false>(p, g, L, C, s);
     }
-    const int64_t blocks = (rows + 3) / 4;
+    const int64_t blocks = (a.T * (int64_t)(QK + (a.v_in ? a.K : 0)) + 3) / 4;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((qknorm_rope_scalar<DT>), dim3((uint32_t)blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((qknorm_rope_scalar<DT>), dim3((uint32_t)blocks), dim3(256), 0, s, p, g);
     return hipGetLastError();
 }
 

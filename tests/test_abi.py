@@ -35,6 +35,10 @@ def lib():
     sigs = {
         "mbt_qknorm_rope": [vp, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, i64, i32, i32, f32,
                             i32, i32, i32, vp],
+        "mbt_qknorm_rope_ex": [vp, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, i64, i32, i32,
+                               f32, i32, i32, i32, i64, i64, i64, i64, i32, vp],
+        "mbt_qkv_norm_rope_cache": [vp, vp, vp, vp, vp, i64, vp, vp, vp, i64, vp, i32, i32, i64,
+                                    i32, i32, f32, i32, i32, i32, i32, vp],
         "mbt_rope": [vp, vp, vp, i64, vp, i32, i32, i64, i32, i32, i32, i32, vp],
         "mbt_fused_add_rmsnorm": [vp, vp, vp, i64, i32, f32, i32, i32, vp],
         "mbt_fused_add_rmsnorm_fp8": [vp, vp, vp, vp, f32, i64, i32, f32, i32, i32, vp],
@@ -56,7 +60,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), f"{n} declared in mbt.h but not exported"
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
@@ -207,3 +211,81 @@ def test_rope_rejects(lib):
     assert call(k=A + 1024) == ALIAS            # k inside q
     assert call(q=CS + 64) == ALIAS             # q over the cache
     assert call(T=0, q=None, k=None, cs=None, pos=None) == OK
+
+
+def qk_ex(lib, **kw):
+    a = dict(q_in=A, k_in=B, q_out=C, k_out=D_, w_q=W1, w_k=W2, cos_sin=CS, max_pos=4096,
+             pos=POS, Q=16, K=2, T=8, head_dim=256, rot_dim=64, eps=1e-6, weight_offset=1,
+             layout=0, dtype=BF16, qis=0, kis=0, qos=0, kos=0, flags=1)
+    a.update(kw)
+    return lib.mbt_qknorm_rope_ex(a["q_in"], a["k_in"], a["q_out"], a["k_out"], a["w_q"],
+                                  a["w_k"], a["cos_sin"], a["max_pos"], a["pos"], a["Q"], a["K"],
+                                  a["T"], a["head_dim"], a["rot_dim"], a["eps"],
+                                  a["weight_offset"], a["layout"], a["dtype"], a["qis"], a["kis"],
+                                  a["qos"], a["kos"], a["flags"], None)
+
+
+# a fused QKV buffer at A: Q = 2, K = 1, D = 8 bf16, token stride 32 elements
+FQ = dict(Q=2, K=1, head_dim=8, rot_dim=8, qis=32, kis=32, qos=32, kos=32,
+          q_in=A, k_in=A + 32, q_out=A, k_out=A + 32)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=2), ENUM), (dict(flags=-1), ENUM),
+    (dict(qis=-256), SHAPE), (dict(kis=511), SHAPE),           # stride below K * D
+    (dict(qos=4095), SHAPE), (dict(kos=1 << 41), SHAPE),
+    (dict(dtype=4), DTYPE), (dict(rot_dim=3), SHAPE), (dict(eps=NAN), SCALAR),
+    (dict(q_in=A + 1), ALIGN),
+    # q_out over the key slice of the same buffer
+    (dict(FQ, q_out=A + 32), ALIAS),
+    # q_out one head into the query slice: overlaps the query input rows
+    (dict(FQ, q_out=A + 16), ALIAS),
+    # k_out over the query rows of the next token (stride 32 elements = 64 B)
+    (dict(FQ, k_out=A + 64), ALIAS),
+    # same base, different stride: not the in-place form
+    (dict(FQ, qos=16), ALIAS),
+    # the two outputs on top of each other
+    (dict(FQ, q_out=C, k_out=C), ALIAS),
+])
+def test_qknorm_rope_ex_rejects(lib, kw, status):
+    assert qk_ex(lib, **kw) == status
+    assert lib.mbt_last_error().decode() != ""
+
+
+def test_qknorm_rope_ex_empty_is_noop(lib):
+    assert qk_ex(lib, T=0, q_in=None, k_in=None, q_out=None, k_out=None, w_q=None, w_k=None,
+                 cos_sin=None, pos=None) == OK
+
+
+def qkv_cache(lib, **kw):
+    a = dict(qkv=A, q_out=B, kc=C, vc=D_, slot=POS + 4096, n_slots=64, w_q=W1, w_k=W2,
+             cos_sin=CS, max_pos=4096, pos=POS, Q=16, K=2, T=8, head_dim=256, rot_dim=64,
+             eps=1e-6, weight_offset=1, layout=0, dtype=BF16, flags=0)
+    a.update(kw)
+    return lib.mbt_qkv_norm_rope_cache(a["qkv"], a["q_out"], a["kc"], a["vc"], a["slot"],
+                                       a["n_slots"], a["w_q"], a["w_k"], a["cos_sin"],
+                                       a["max_pos"], a["pos"], a["Q"], a["K"], a["T"],
+                                       a["head_dim"], a["rot_dim"], a["eps"], a["weight_offset"],
+                                       a["layout"], a["dtype"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=0), SHAPE), (dict(Q=-1), SHAPE), (dict(head_dim=600), SHAPE),
+    (dict(dtype=7), DTYPE), (dict(flags=8), ENUM), (dict(n_slots=-1), SCALAR),
+    (dict(slot=None), NULLP), (dict(kc=None), NULLP), (dict(vc=None), NULLP),
+    (dict(qkv=None), NULLP), (dict(q_out=None), NULLP),
+    (dict(slot=POS + 4100), ALIGN), (dict(vc=D_ + 1), ALIGN),
+    (dict(kc=A + 1024), ALIAS),                 # key cache inside qkv
+    (dict(vc=C + 256), ALIAS),                  # the two caches overlap
+    (dict(q_out=C), ALIAS),                     # q_out on the key cache
+    (dict(kc=POS), ALIAS),                      # key cache over the positions
+    (dict(slot=D_ + 64), ALIAS),                # slot table inside the value cache
+])
+def test_qkv_norm_rope_cache_rejects(lib, kw, status):
+    assert qkv_cache(lib, **kw) == status
+    assert lib.mbt_last_error().decode() != ""
+
+
+def test_qkv_norm_rope_cache_empty_is_noop(lib):
+    assert qkv_cache(lib, T=0, qkv=None, q_out=None, kc=None, vc=None, slot=None, w_q=None,
+                     w_k=None, cos_sin=None, pos=None) == OK
