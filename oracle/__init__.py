@@ -47,6 +47,9 @@ _SIGS = {
     "mbt_ref_fused_add_rmsnorm": (_i32, [_vp, _vp, _vp, _i64, _i32, _f32, _i32, _i32]),
     "mbt_ref_fused_add_rmsnorm_fp8": (_i32, [_vp, _vp, _vp, _vp, _f32, _i64, _i32,
                                              _f32, _i32, _i32]),
+    "mbt_ref_adarms": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _f32, _i32]),
+    "mbt_ref_adarms_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _i64, _i32, _f32, _i32]),
+    "mbt_ref_adarms_amax": (_f32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _f32, _i32]),
     "mbt_ref_gated_act": (_i32, [_vp, _vp, _i64, _i32, _i32, _i32]),
     "mbt_ref_gated_act_fp8": (_i32, [_vp, _vp, _f32, _i64, _i32, _i32, _i32]),
     "mbt_ref_quantize_fp8": (_i32, [_vp, _vp, _i64, _f32]),
@@ -186,6 +189,37 @@ class Oracle:
         return float(self._lib.mbt_ref_fused_add_rmsnorm_amax(
             _ptr(x), _ptr(r), _ptr(_c(w, dtype)), x.size // H, H, eps,
             weight_offset, dtype))
+
+    def adarms(self, x, residual, gate, scale, shift, eps, dtype):
+        """Adaptive RMSNorm, dtype output.  Returns (x_out, residual_out)."""
+        x = _c(x, dtype)
+        H = x.shape[-1]
+        r = None if residual is None else _c(residual, dtype)
+        rc = self._lib.mbt_ref_adarms(_ptr(x), _ptr(r), _ptr(_c(gate, dtype)),
+                                      _ptr(_c(scale, dtype)), _ptr(_c(shift, dtype)),
+                                      x.size // H, H, eps, dtype)
+        self._check(rc, "adarms")
+        return x, r
+
+    def adarms_fp8(self, x, residual, gate, scale, shift, inv_scale, eps, dtype):
+        """Returns (y_codes, residual_out)."""
+        x = _c(x, dtype)
+        H = x.shape[-1]
+        r = None if residual is None else _c(residual, dtype)
+        y = np.empty(x.shape, dtype=np.uint8)
+        rc = self._lib.mbt_ref_adarms_fp8(_ptr(x), _ptr(r), _ptr(_c(gate, dtype)),
+                                          _ptr(_c(scale, dtype)), _ptr(_c(shift, dtype)), _ptr(y),
+                                          float(inv_scale), x.size // H, H, eps, dtype)
+        self._check(rc, "adarms_fp8")
+        return y, r
+
+    def adarms_amax(self, x, residual, gate, scale, shift, eps, dtype):
+        x = _c(x, dtype)
+        H = x.shape[-1]
+        r = None if residual is None else _c(residual, dtype)
+        return float(self._lib.mbt_ref_adarms_amax(
+            _ptr(x), _ptr(r), _ptr(_c(gate, dtype)), _ptr(_c(scale, dtype)),
+            _ptr(_c(shift, dtype)), x.size // H, H, eps, dtype))
 
     def gated_act(self, gate_up, act, dtype):
         gu = _c(gate_up, dtype)

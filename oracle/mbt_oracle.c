@@ -499,6 +499,92 @@ float mbt_ref_fused_add_rmsnorm_amax(const void* x, const void* residual,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Adaptive RMSNorm (FlashRT optimization details: the Pi0.5 decoder norms   */
+/* are modulated by a style vector computed once per prompt; fused kernels    */
+/* fused_adarms_fp8_static and gate_res_adarms_fp8_static).  The pages give  */
+/* no formula; the reading taken: the style vector supplies per-channel      */
+/* scale, shift and gate (each of length H) and                              */
+/*   s = R(r + g * x)      (with a residual; g = 1 when no gate is given),   */
+/*   s = x                 (without one),  r <- s,                           */
+/*   m = (s * inv) * (1 + scale) + shift,  inv = 1 / sqrt(mean s^2 + eps),  */
+/* each fp32 operation rounded as written, then R(m) or E4M3FN(m * inv_scale).*/
+/* ------------------------------------------------------------------------ */
+
+static void ada_sum(const void* x, void* residual, const void* gate, int64_t t, int32_t H,
+                    int32_t dtype, int write_res, float* s) {
+    for (int32_t i = 0; i < H; i++) {
+        int64_t k = t * H + i;
+        float xv = ld(x, k, dtype);
+        if (residual) {
+            float gx = gate ? ld(gate, i, dtype) * xv : xv;
+#if MBT_ORACLE_MUTATION == 16
+            gx = xv;                                  /* planted: gate ignored */
+#endif
+            float sum = ld(residual, k, dtype) + gx;
+            s[i] = rounded(sum, dtype);
+            if (write_res) st(residual, k, dtype, sum);
+        } else {
+            s[i] = xv;
+        }
+    }
+}
+
+static float modulate(float n, const void* scale, const void* shift, int32_t i, int32_t dtype) {
+#if MBT_ORACLE_MUTATION == 15
+    return n * ld(scale, i, dtype) + ld(shift, i, dtype); /* planted: 1 + scale lost */
+#else
+    return n * (1.0f + ld(scale, i, dtype)) + ld(shift, i, dtype);
+#endif
+}
+
+static int ada_args_ok(const void* residual, const void* gate, const void* scale,
+                       const void* shift, int64_t T, int32_t H, int32_t dtype) {
+    return dtype_ok(dtype) && T >= 0 && H > 0 && scale && shift && (residual || !gate);
+}
+
+/* mode 0: x <- R(m); mode 1: y <- E4M3FN(m * inv_scale); mode 2: amax. */
+static float adarms(void* x, void* residual, const void* gate, const void* scale,
+                    const void* shift, uint8_t* y, float inv_scale, int64_t T, int32_t H,
+                    float eps, int32_t dtype, int mode) {
+    float* s = (float*)malloc((size_t)H * sizeof(float));
+    if (!s) return -1.0f;
+    float amax = 0.0f;
+    for (int64_t t = 0; t < T; t++) {
+        ada_sum(x, residual, gate, t, H, dtype, mode != 2, s);
+        float inv = inv_rms(s, H, 0, eps);
+        for (int32_t i = 0; i < H; i++) {
+            float m = modulate(s[i] * inv, scale, shift, i, dtype);
+            if (mode == 0) st(x, t * H + i, dtype, m);
+            else if (mode == 1) y[t * H + i] = mbt_ref_f32_to_e4m3fn(m * inv_scale);
+            else if (fabsf(m) > amax) amax = fabsf(m);
+        }
+    }
+    free(s);
+    return amax;
+}
+
+int mbt_ref_adarms(void* x, void* residual, const void* gate, const void* scale,
+                   const void* shift, int64_t T, int32_t H, float eps, int32_t dtype) {
+    if (!ada_args_ok(residual, gate, scale, shift, T, H, dtype)) return -1;
+    return adarms(x, residual, gate, scale, shift, NULL, 0.0f, T, H, eps, dtype, 0) < 0 ? -1 : 0;
+}
+
+int mbt_ref_adarms_fp8(const void* x, void* residual, const void* gate, const void* scale,
+                       const void* shift, uint8_t* y, float inv_scale, int64_t T, int32_t H,
+                       float eps, int32_t dtype) {
+    if (!ada_args_ok(residual, gate, scale, shift, T, H, dtype)) return -1;
+    return adarms((void*)x, residual, gate, scale, shift, y, inv_scale, T, H, eps, dtype, 1) < 0
+               ? -1 : 0;
+}
+
+float mbt_ref_adarms_amax(const void* x, const void* residual, const void* gate,
+                          const void* scale, const void* shift, int64_t T, int32_t H,
+                          float eps, int32_t dtype) {
+    if (!ada_args_ok(residual, gate, scale, shift, T, H, dtype)) return -1.0f;
+    return adarms((void*)x, (void*)residual, gate, scale, shift, NULL, 0.0f, T, H, eps, dtype, 2);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Gated activations (P1 5.1): [g || u] in R^{2d}, out_j = act(g_j) * u_j.   */
 /* SiLU(g) = g * sigmoid(g).                                                 */
 /* GELU, tanh form: 0.5 g (1 + tanh(z)), z = sqrt(2/pi) (g + 0.044715 g^3).  */

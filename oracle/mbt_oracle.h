@@ -115,6 +115,22 @@ int mbt_ref_fused_add_rmsnorm_fp8(const void* x, void* residual, const void* w,
                                   int32_t H, float eps, int32_t weight_offset,
                                   int32_t dtype);
 
+/* Adaptive RMSNorm with a per-call style vector (FlashRT optimization
+ * details: fused_adarms_fp8_static, gate_res_adarms_fp8_static).  Reading:
+ *   s = R(r + g * x) with a residual (g = 1 when gate is NULL), else s = x;
+ *   r <- s;  m = (s * inv) * (1 + scale) + shift.
+ * scale, shift, gate: [H] in the dtype; a gate needs a residual.
+ * mbt_ref_adarms writes x <- R(m); the _fp8 form writes y = E4M3FN(m *
+ * inv_scale) and leaves x alone; _amax returns max |m| and writes nothing. */
+int mbt_ref_adarms(void* x, void* residual, const void* gate, const void* scale,
+                   const void* shift, int64_t T, int32_t H, float eps, int32_t dtype);
+int mbt_ref_adarms_fp8(const void* x, void* residual, const void* gate, const void* scale,
+                       const void* shift, uint8_t* y, float inv_scale, int64_t T, int32_t H,
+                       float eps, int32_t dtype);
+float mbt_ref_adarms_amax(const void* x, const void* residual, const void* gate,
+                          const void* scale, const void* shift, int64_t T, int32_t H,
+                          float eps, int32_t dtype);
+
 /* Gated activation on gate_up[T][2d] = [g || u] (thox-edge-ops v2, 5.1):
  * out[t][j] = R(act(g_j) * u_j). */
 int mbt_ref_gated_act(const void* gate_up, void* out, int64_t T, int32_t d,

@@ -298,6 +298,86 @@ def pin_rmsnorm_no_weight(orc):
     assert np.array_equal(y8, orc.quantize_fp8(xo32, np.float32(448.0 / amax)))
 
 
+def pin_adarms(orc):
+    """Adaptive RMSNorm (FlashRT's fused_adarms / gate_res_adarms kernels, in
+    the reading m = (s inv)(1 + scale) + shift, s = R(r + g x)).
+    * scale = shift = 0 and no residual: exactly the no-weight RMSNorm;
+    * fp32 rows against float64 torch (rms_norm without weight, then the
+      modulation), bound (D+8)/2 u on the norm plus 3 u for the modulation;
+    * the gated residual equals numpy's fp32 r + g * x (product and sum
+      rounded separately) rounded once to the dtype;
+    * every row of D = 4 over the bf16 grid against mpmath, rounded once;
+    * FP8 == quantize_fp8 of the fp32 output, amax == max |output|;
+    * a gate without a residual is refused."""
+    g = np.random.default_rng(14)
+    H = 64
+    for dtype in (BF16, F16, F32):
+        x = W.to_bits(g.standard_normal((5, H)) + 0.01, dtype)
+        zero = W.to_bits(np.zeros(H), dtype)
+        xo, _ = orc.adarms(x, None, None, zero, zero, 1e-6, dtype)
+        assert same_bits(xo, orc.rmsnorm_rows(x, None, 1e-6, 0, dtype), dtype), \
+            f"identity modulation != no-weight norm ({dtype})"
+    for D in (7, 256, 2048):
+        x = (g.standard_normal((8, D)) * 1.5).astype(np.float32)
+        sc = (g.standard_normal(D) * 0.2).astype(np.float32)
+        sh = (g.standard_normal(D) * 0.2).astype(np.float32)
+        y, _ = orc.adarms(x, None, None, sc, sh, 1e-6, F32)
+        n = F.rms_norm(torch.from_numpy(x.astype(np.float64)), (D,), weight=None,
+                       eps=float(np.float32(1e-6))).numpy()
+        a = n * (1.0 + sc.astype(np.float64))
+        ref = a + sh.astype(np.float64)
+        tol = ((D + 8) / 2.0 + 3) * U32 * np.abs(a) + 2 * U32 * np.abs(ref) + 1e-30
+        assert np.all(np.abs(y.astype(np.float64) - ref) <= tol), f"adarms vs torch D={D}"
+    for dtype in (BF16, F16, F32):
+        x = W.to_bits(g.standard_normal((6, 96)), dtype)
+        r = W.to_bits(g.standard_normal((6, 96)) * 2, dtype)
+        gt = W.to_bits(g.standard_normal(96) * 0.5 + 1, dtype)
+        sc = W.to_bits(g.standard_normal(96) * 0.1, dtype)
+        sh = W.to_bits(g.standard_normal(96) * 0.1, dtype)
+        _, ro = orc.adarms(x, r, gt, sc, sh, 1e-6, dtype)
+        want = f32(r, dtype) + f32(gt, dtype) * f32(x, dtype)        # numpy fp32, unfused
+        assert same_bits(ro, W.to_bits(want.astype(np.float64), dtype), dtype), \
+            f"gated residual ({dtype})"
+        _, ro1 = orc.adarms(x, r, None, sc, sh, 1e-6, dtype)
+        want1 = f32(r, dtype) + f32(x, dtype)
+        assert same_bits(ro1, W.to_bits(want1.astype(np.float64), dtype), dtype), "plain residual"
+    mpmath.mp.dps = 40
+    eps = float(np.float32(1e-6))
+    rows = np.array(np.meshgrid(*([_GRID] * 4), indexing="ij")).reshape(4, -1).T
+    xb = W.to_bits(rows, BF16)
+    scb = W.to_bits(np.array([0.25, -0.5, 0.0625, 1.5]), BF16)
+    shb = W.to_bits(np.array([-0.125, 0.0, 0.75, 0.03125]), BF16)
+    y = f32(orc.adarms(xb, None, None, scb, shb, eps, BF16)[0], BF16)
+    xv = f32(xb, BF16).astype(np.float64)
+    scv, shv = f32(scb, BF16).astype(np.float64), f32(shb, BF16).astype(np.float64)
+    amb = bad = 0
+    for rr in range(rows.shape[0]):
+        inv = 1 / mpmath.sqrt(mpmath.fsum(mpmath.mpf(v) ** 2 for v in xv[rr]) / 4
+                              + mpmath.mpf(eps))
+        for i in range(4):
+            exact = mpmath.mpf(xv[rr, i]) * inv * (1 + mpmath.mpf(scv[i])) + mpmath.mpf(shv[i])
+            e, a = round_exact(exact, BF16)
+            if y[rr, i] != e:
+                amb, bad = (amb + 1, bad) if a else (amb, bad + 1)
+    assert bad == 0 and amb <= rows.size // 200, f"adarms brute force: {bad} / {amb}"
+    x = g.standard_normal((8, 512)).astype(np.float32)
+    r = g.standard_normal((8, 512)).astype(np.float32)
+    gt = (g.standard_normal(512) * 0.3 + 1).astype(np.float32)
+    sc = (g.standard_normal(512) * 0.1).astype(np.float32)
+    sh = (g.standard_normal(512) * 0.1).astype(np.float32)
+    xo, ro = orc.adarms(x, r, gt, sc, sh, 1e-6, F32)
+    amax = orc.adarms_amax(x, r, gt, sc, sh, 1e-6, F32)
+    assert amax == float(np.max(np.abs(xo))), "adarms amax"
+    y8, ro8 = orc.adarms_fp8(x, r, gt, sc, sh, np.float32(448.0 / amax), 1e-6, F32)
+    assert np.array_equal(ro8, ro) and np.array_equal(y8, orc.quantize_fp8(xo, np.float32(448.0 / amax)))
+    try:
+        orc.adarms(x, None, gt, sc, sh, 1e-6, F32)
+    except Exception:
+        pass
+    else:
+        raise AssertionError("a gate without a residual must be refused")
+
+
 # ---------------------------------------------------------------------------
 # rotary embedding
 # ---------------------------------------------------------------------------
@@ -646,7 +726,7 @@ def pin_act_fp8(orc):
 ALL_PINS = [
     pin_bf16_converter, pin_f16_converter, pin_e4m3fn_converter,
     pin_rmsnorm_vs_torch, pin_rmsnorm_closed_forms, pin_rmsnorm_bruteforce,
-    pin_rmsnorm_no_weight,
+    pin_rmsnorm_no_weight, pin_adarms,
     pin_rope_complex, pin_rope_closed_forms, pin_rope_invariants,
     pin_prologue_composition, pin_prologue_constant_head, pin_prologue_round_once,
     pin_residual_add, pin_norm_fp8, pin_quantize_vs_torch,

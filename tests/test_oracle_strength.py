@@ -29,6 +29,8 @@ MUTATIONS = {
     12: "positions past the cache clamped to its last row",
     13: "a missing weight read as 1 + 1 (no-weight norm doubled)",
     14: "single-rounding prologue rounds the norm result before rotating",
+    15: "adaptive norm scales by scale instead of 1 + scale",
+    16: "adaptive norm ignores the residual gate",
 }
 
 # fast pins first: most mutations are caught within a second
