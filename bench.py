@@ -368,6 +368,31 @@ def norm_fp8_cold_us(torch, mbt, W, cell, inv_scale, launches=2000):
     return us
 
 
+def adarms_fp8_cold_us(torch, mbt, W, cell, launches=2000):
+    """Adaptive RMSNorm -> FP8 (gated residual), cold; the scale comes from
+    the GPU's own calibration pass over seed data."""
+    dev = "cuda:0"
+    i = cell.inputs()
+    t = lambda b: None if b is None else W.to_torch(b, cell.dtype, dev)
+    g, sc, sh = t(i["gate"]), t(i["scale"]), t(i["shift"])
+    cal = cell.calibration_inputs()
+    amax = mbt.adarms_amax(t(cal["x"]), t(cal["residual"]), g, sc, sh, cell.eps)
+    inv_scale = W.fp8_inv_scale(float(amax.item()))
+    R = max(8, -(-RING_BYTES // cell.bytes_algorithmic()))
+    x0, r0 = t(i["x"]), t(i["residual"])
+    ring = [(x0.clone(), r0.clone(), torch.empty(x0.shape, dtype=torch.uint8, device=dev))
+            for _ in range(R)]
+
+    def call(j):
+        x, r, y = ring[j]
+        mbt.adarms_fp8(x, r, g, sc, sh, inv_scale, cell.eps, y=y)
+
+    us = kernel_time_us(torch, call, R, launches)
+    del ring
+    torch.cuda.empty_cache()
+    return us
+
+
 def copy_ceiling_gbps(torch, nbytes, launches=1000):
     """torch's device copy of nbytes/2 -> nbytes/2 (nbytes of traffic), cold."""
     half = max(16, nbytes // 2)
@@ -591,6 +616,16 @@ def main():
                 row[key + "_us"] = round(us, 3)
                 row[key + "_GBps"] = round(c.bytes_algorithmic() / us / 1e3, 1)
             noweight.append(row)
+    # adaptive RMSNorm -> FP8 with a gated residual (style vector per call):
+    # the Pi0.5 decoder's 10-token rows and a 512-token batch, H = 2048
+    adarms = []
+    if not args.no_sweep:
+        for T in (10, 512):
+            c = W.AdaCell(name="ada", config=5, cell=70 + T, T=T, H=st.H, dtype=W.BF16, fp8=True)
+            us = adarms_fp8_cold_us(torch, mbt, W, c)
+            adarms.append({"T": T, "H": st.H, "us": round(us, 3),
+                           "GBps": round(c.bytes_algorithmic() / us / 1e3, 1),
+                           "frac_peak": round(c.bytes_algorithmic() / us / 1e3 / PEAK_HBM_GBPS, 4)})
 
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -607,6 +642,7 @@ def main():
         "kernels": per,
         "prologue": prologue,
         "norm_fp8_weight_vs_none": noweight,
+        "adarms_fp8_gated": adarms,
     }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(W, st, args.cpu_seconds)

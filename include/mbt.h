@@ -282,6 +282,45 @@ MBT_API mbt_status mbt_fused_add_rmsnorm_amax(const void* x, const void* residua
                                       int32_t weight_offset, int32_t dtype, void* stream);
 
 /*
+ * mbt_adarms, mbt_adarms_fp8, mbt_adarms_amax -- adaptive RMSNorm with a
+ * per-call style vector.
+ *
+ * P3, fused kernel table (fused_adarms_fp8_static, gate_res_adarms_fp8_static)
+ * and the style-vector paragraph: the Pi0.5 decoder norms are modulated by a
+ * vector computed once per prompt.  The pages give no formula; the library
+ * takes the style vector as per-channel scale, shift and gate and computes
+ *   s_i = R(r_i + g_i * x_i)   with a residual (g = 1 when gate is NULL;
+ *                              the product and the sum rounded in fp32, then
+ *                              once to the dtype), s = x without one
+ *   residual_i <- s_i
+ *   m_i = (s_i * inv) * (1 + scale_i) + shift_i,  inv = 1/sqrt(mean s^2 + eps)
+ * mbt_adarms:      x_i <- R(m_i)                         (in place)
+ * mbt_adarms_fp8:  y_i = E4M3FN(m_i * inv_scale)        (x read only)
+ * mbt_adarms_amax: *amax <- max(*amax, max |m_i|); nothing else written
+ *
+ *  x        [T][H] dtype
+ *  residual [T][H] dtype  may be NULL; read, then overwritten with s (not by
+ *                         the amax pass)
+ *  gate     [H]    dtype  may be NULL; needs a residual
+ *  scale, shift [H] dtype required
+ *  y        [T][H] uint8  e4m3fn codes;  amax: device float, caller-initialised
+ *  T >= 0; H >= 1; eps finite >= 0; inv_scale finite > 0; dtype mbt_dtype.
+ *  Errors: a gate without a residual, or a NULL scale / shift / y / amax
+ *  (T > 0) -> MBT_ERR_NULL_POINTER; overlaps of an output with an input ->
+ *  MBT_ERR_ALIAS.
+ */
+MBT_API mbt_status mbt_adarms(void* x, void* residual, const void* gate, const void* scale,
+                              const void* shift, int64_t T, int32_t H, float eps, int32_t dtype,
+                              void* stream);
+MBT_API mbt_status mbt_adarms_fp8(const void* x, void* residual, const void* gate,
+                                  const void* scale, const void* shift, uint8_t* y,
+                                  float inv_scale, int64_t T, int32_t H, float eps, int32_t dtype,
+                                  void* stream);
+MBT_API mbt_status mbt_adarms_amax(const void* x, const void* residual, const void* gate,
+                                   const void* scale, const void* shift, float* amax, int64_t T,
+                                   int32_t H, float eps, int32_t dtype, void* stream);
+
+/*
  * mbt_gated_act -- gated activation (P1 section 5.1: the input row is the
  * gate projection followed by the up projection, [g || u] of width 2d):
  *   out[t][j] = R(act(g) * u),  g = gate_up[t][j],  u = gate_up[t][d + j]

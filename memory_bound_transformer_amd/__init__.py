@@ -14,6 +14,9 @@ The entry points mirror include/mbt.h:
     fused_add_rmsnorm      residual add + RMSNorm, in place
     fused_add_rmsnorm_fp8  the same with static-scale e4m3fn output
     fused_add_rmsnorm_amax calibration pass (amax of the FP8 input)
+    adarms                 adaptive RMSNorm (style scale / shift / gate), in place
+    adarms_fp8             the same with static-scale e4m3fn output
+    adarms_amax            its calibration pass
     gated_act              SiLU / GELU-tanh gated activation
     gated_act_fp8          the same with static-scale e4m3fn output
     gated_act_amax         calibration pass
@@ -26,7 +29,7 @@ import torch
 
 __all__ = [
     "qknorm_rope", "qknorm_rope_ex", "qkv_norm_rope_cache", "rope", "fused_add_rmsnorm", "fused_add_rmsnorm_fp8", "fused_add_rmsnorm_amax",
-    "gated_act", "gated_act_fp8", "gated_act_amax", "quantize_fp8", "MbtError",
+    "adarms", "adarms_fp8", "adarms_amax", "gated_act", "gated_act_fp8", "gated_act_amax", "quantize_fp8", "MbtError",
     "ROTATE_HALF", "INTERLEAVED", "SILU", "GELU_TANH", "LIB_PATH", "abi_version",
 ]
 
@@ -56,6 +59,9 @@ _SIGS = {
     "mbt_fused_add_rmsnorm": [_vp, _vp, _vp, _i64, _i32, _f32, _i32, _i32, _vp],
     "mbt_fused_add_rmsnorm_fp8": [_vp, _vp, _vp, _vp, _f32, _i64, _i32, _f32, _i32, _i32, _vp],
     "mbt_fused_add_rmsnorm_amax": [_vp, _vp, _vp, _vp, _i64, _i32, _f32, _i32, _i32, _vp],
+    "mbt_adarms": [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _f32, _i32, _vp],
+    "mbt_adarms_fp8": [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _i64, _i32, _f32, _i32, _vp],
+    "mbt_adarms_amax": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _f32, _i32, _vp],
     "mbt_gated_act": [_vp, _vp, _i64, _i32, _i32, _i32, _vp],
     "mbt_gated_act_fp8": [_vp, _vp, _f32, _i64, _i32, _i32, _i32, _vp],
     "mbt_gated_act_amax": [_vp, _vp, _i64, _i32, _i32, _i32, _vp],
@@ -264,6 +270,43 @@ def fused_add_rmsnorm_amax(x, residual, w, eps=1e-6, weight_offset=0, amax=None,
     _check(_lib.mbt_fused_add_rmsnorm_amax(_ptr(x), _ptr(residual), _ptr(w), _ptr(amax),
                                            x.numel() // H, H, eps, weight_offset, _dtype(x),
                                            _stream(stream)))
+    return amax
+
+
+def adarms(x, residual, gate, scale, shift, eps=1e-6, stream=None):
+    """In place: residual <- R(residual + gate * x) (gate None: 1);
+    x <- R(RMSNorm(s) * (1 + scale) + shift).  x [T, H]; scale, shift,
+    gate [H]."""
+    _dev(x, residual, gate, scale, shift)
+    _same_dtype(x, residual, gate, scale, shift)
+    H = x.shape[-1]
+    _check(_lib.mbt_adarms(_ptr(x), _ptr(residual), _ptr(gate), _ptr(scale), _ptr(shift),
+                           x.numel() // H, H, eps, _dtype(x), _stream(stream)))
+    return x
+
+
+def adarms_fp8(x, residual, gate, scale, shift, inv_scale, eps=1e-6, y=None, stream=None):
+    """residual <- R(residual + gate * x); returns e4m3fn codes (uint8
+    [T, H]) of (RMSNorm(s) * (1 + scale) + shift) * inv_scale."""
+    _dev(x, residual, gate, scale, shift, y)
+    _same_dtype(x, residual, gate, scale, shift)
+    H = x.shape[-1]
+    if y is None:
+        y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(_lib.mbt_adarms_fp8(_ptr(x), _ptr(residual), _ptr(gate), _ptr(scale), _ptr(shift),
+                               _ptr(y), float(inv_scale), x.numel() // H, H, eps, _dtype(x),
+                               _stream(stream)))
+    return y
+
+
+def adarms_amax(x, residual, gate, scale, shift, eps=1e-6, amax=None, stream=None):
+    _dev(x, residual, gate, scale, shift, amax)
+    _same_dtype(x, residual, gate, scale, shift)
+    H = x.shape[-1]
+    if amax is None:
+        amax = torch.zeros(1, dtype=torch.float32, device=x.device)
+    _check(_lib.mbt_adarms_amax(_ptr(x), _ptr(residual), _ptr(gate), _ptr(scale), _ptr(shift),
+                                _ptr(amax), x.numel() // H, H, eps, _dtype(x), _stream(stream)))
     return amax
 
 

@@ -451,6 +451,106 @@ mbt_status mbt_fused_add_rmsnorm_amax(const void* x, const void* residual, const
 
 namespace {
 
+// Adaptive RMSNorm: the residual-norm checks with w = scale, plus shift
+// (required) and gate (optional, needs a residual).  `outs` are the ranges
+// the call writes besides residual / x.
+mbt_status ada_common(const void* x, const void* residual, const void* gate, const void* scale,
+                      const void* shift, int64_t T, int32_t H, float eps, int32_t dtype,
+                      int64_t* bytes) {
+    if (gate && !residual && T > 0)
+        return fail(MBT_ERR_NULL_POINTER, "a gate needs a residual");
+    if (T > 0 && !scale) return fail(MBT_ERR_NULL_POINTER, "scale is required");
+    mbt_status st = norm_common(x, residual, scale, T, H, eps, 1, dtype, bytes);
+    if (st != MBT_OK || T == 0) return st;
+    if (!shift) return fail(MBT_ERR_NULL_POINTER, "shift is required");
+    const int eb = elt_bytes(dtype);
+    if (!aligned(shift, eb) || (gate && !aligned(gate, eb)))
+        return fail(MBT_ERR_ALIGN, "a pointer is not aligned to its element size");
+    const Range xr{(const char*)x, *bytes, "x"};
+    const Range rr{(const char*)residual, *bytes, "residual"};
+    for (const Range& v : {Range{(const char*)shift, (int64_t)H * eb, "shift"},
+                           Range{(const char*)gate, (int64_t)H * eb, "gate"}})
+        if (overlap(v, xr) || overlap(v, rr))
+            return fail(MBT_ERR_ALIAS, "%s overlaps x or residual", v.name);
+    return MBT_OK;
+}
+
+mbt_status ada_launch(mbt::NormArgs a, const void* gate, const void* shift, void* stream,
+                      const char* what) {
+    a.ada = true;
+    a.gate = gate;
+    a.shift = shift;
+    a.weight_offset = 1;                      // w = scale: the weight path gives 1 + scale
+    return hip_status(mbt::launch_rmsnorm(a, (hipStream_t)stream), what);
+}
+
+}  // namespace
+
+mbt_status mbt_adarms(void* x, void* residual, const void* gate, const void* scale,
+                      const void* shift, int64_t T, int32_t H, float eps, int32_t dtype,
+                      void* stream) {
+    int64_t bytes = 0;
+    mbt_status st = ada_common(x, residual, gate, scale, shift, T, H, eps, dtype, &bytes);
+    if (st != MBT_OK) return st;
+    if (T == 0) return ok();
+    mbt::NormArgs a{};
+    a.x = x; a.x_out = x; a.residual = residual; a.w = scale; a.T = T; a.H = H; a.eps = eps;
+    a.dtype = dtype; a.mode = mbt::kNormInPlace;
+    return ada_launch(a, gate, shift, stream, "adarms launch");
+}
+
+mbt_status mbt_adarms_fp8(const void* x, void* residual, const void* gate, const void* scale,
+                          const void* shift, uint8_t* y, float inv_scale, int64_t T, int32_t H,
+                          float eps, int32_t dtype, void* stream) {
+    int64_t bytes = 0;
+    mbt_status st = ada_common(x, residual, gate, scale, shift, T, H, eps, dtype, &bytes);
+    if (st != MBT_OK) return st;
+    if (!finite_pos(inv_scale)) return fail(MBT_ERR_BAD_SCALAR, "inv_scale must be finite > 0");
+    if (T == 0) return ok();
+    if (!y) return fail(MBT_ERR_NULL_POINTER, "y is required");
+    const int eb = elt_bytes(dtype);
+    const Range yr{(const char*)y, mul(T, H), "y"};
+    for (const Range& in : {Range{(const char*)x, bytes, "x"},
+                            Range{(const char*)residual, bytes, "residual"},
+                            Range{(const char*)scale, (int64_t)H * eb, "scale"},
+                            Range{(const char*)shift, (int64_t)H * eb, "shift"},
+                            Range{(const char*)gate, (int64_t)H * eb, "gate"}}) {
+        st = check_alias(yr, in, false);
+        if (st != MBT_OK) return st;
+    }
+    mbt::NormArgs a{};
+    a.x = x; a.residual = residual; a.w = scale; a.y8 = y; a.inv_scale = inv_scale; a.T = T;
+    a.H = H; a.eps = eps; a.dtype = dtype; a.mode = mbt::kNormFp8;
+    return ada_launch(a, gate, shift, stream, "adarms_fp8 launch");
+}
+
+mbt_status mbt_adarms_amax(const void* x, const void* residual, const void* gate,
+                           const void* scale, const void* shift, float* amax, int64_t T,
+                           int32_t H, float eps, int32_t dtype, void* stream) {
+    int64_t bytes = 0;
+    mbt_status st = ada_common(x, residual, gate, scale, shift, T, H, eps, dtype, &bytes);
+    if (st != MBT_OK) return st;
+    if (T == 0) return ok();
+    if (!amax) return fail(MBT_ERR_NULL_POINTER, "amax is required");
+    if (!aligned(amax, 4)) return fail(MBT_ERR_ALIGN, "amax must be 4-byte aligned");
+    const int eb = elt_bytes(dtype);
+    const Range ar{(const char*)amax, 4, "amax"};
+    for (const Range& in : {Range{(const char*)x, bytes, "x"},
+                            Range{(const char*)residual, bytes, "residual"},
+                            Range{(const char*)scale, (int64_t)H * eb, "scale"},
+                            Range{(const char*)shift, (int64_t)H * eb, "shift"},
+                            Range{(const char*)gate, (int64_t)H * eb, "gate"}}) {
+        st = check_alias(ar, in, false);
+        if (st != MBT_OK) return st;
+    }
+    mbt::NormArgs a{};
+    a.x = x; a.residual = const_cast<void*>(residual); a.w = scale; a.amax = amax; a.T = T;
+    a.H = H; a.eps = eps; a.dtype = dtype; a.mode = mbt::kNormAmax;
+    return ada_launch(a, gate, shift, stream, "adarms_amax launch");
+}
+
+namespace {
+
 mbt_status act_common(const void* gate_up, int64_t T, int32_t d, int32_t act, int32_t dtype,
                       int64_t* in_bytes) {
     if (!valid_dtype(dtype)) return fail(MBT_ERR_BAD_DTYPE, "dtype %d", dtype);

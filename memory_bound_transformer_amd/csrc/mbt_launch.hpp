@@ -53,6 +53,12 @@ struct NormArgs {
     float eps;
     int32_t weight_offset, dtype;
     int mode;             // NormOut
+    // adaptive form (ada): w is the style scale (with weight_offset 1 it
+    // gives 1 + scale), `shift` is added after it and `gate` multiplies x in
+    // the residual sum (NULL: 1)
+    bool ada;
+    const void* gate;
+    const void* shift;
 };
 
 enum ActOut : int { kActDtype = 0, kActFp8 = 1, kActAmax = 2 };

@@ -9,6 +9,10 @@
 // Without a weight (w == NULL, delta 0; FlashRT optimization details, weight
 // folding) x <- R(s * inv): the weight vector becomes a register constant of
 // ones, so no weight is loaded and the multiply by exactly 1 changes nothing.
+// Adaptive form (ADA; FlashRT's fused_adarms / gate_res_adarms kernels, with
+// a style vector of per-channel scale, shift and gate): s = R(r + g * x),
+// and the output value is (s * inv) * (1 + scale) + shift -- the weight path
+// with w = scale and delta = 1, plus one add.
 // FP8 epilogue (FlashRT optimization details, fused kernel table and static
 // FP8 calibration): y = E4M3FN(((s * inv) * (w + delta)) * inv_scale) with x
 // left unchanged; the calibration pass instead folds max |(s*inv)*(w+delta)|
@@ -53,6 +57,8 @@ struct NormParams {
     float eps, inv_H, delta;
     int32_t wpr;   // wide kernel: waves per row
     int32_t rpb;   // wide kernel: rows per block
+    const void* gate;    // adaptive form: residual gate (NULL: 1)
+    const void* shift;   // adaptive form: added after the scale
 };
 
 template <int DT, int MODE>
@@ -100,22 +106,40 @@ __device__ __forceinline__ float group_tree(float* g, int n) {
 }
 
 // s = R(x + r) for one chunk (fp32 add of the decoded operands, one rounding),
-// returned packed; x alone without a residual.
-template <int DT>
-__device__ __forceinline__ u32x4 residual_sum(u32x4 xv, u32x4 rv, bool has_res) {
+// returned packed; x alone without a residual.  With a gate (adaptive form)
+// s = R(r + g * x), the product rounded to fp32 first.
+template <int DT, bool GATED>
+__device__ __forceinline__ u32x4 residual_sum(u32x4 xv, u32x4 rv, u32x4 gv, bool has_res) {
     constexpr int V = Vec<DT>::n;
     if (!has_res) return xv;
     float a[V], b[V];
     unpack<DT>(xv, a);
     unpack<DT>(rv, b);
+    if constexpr (GATED) {
+        float g[V];
+        unpack<DT>(gv, g);
+#pragma unroll
+        for (int i = 0; i < V; ++i) a[i] = g[i] * a[i];
+    }
 #pragma unroll
     for (int i = 0; i < V; ++i) a[i] += b[i];
     return pack<DT>(a);
 }
 
+// The adaptive form's shift, added to the scaled value.
+template <int DT, bool ADA>
+__device__ __forceinline__ void add_shift(const NormParams& p, int64_t e0, float* y) {
+    if constexpr (ADA) {
+        float sh[Vec<DT>::n];
+        unpack<DT>(ld16((const char*)p.shift + e0 * EltBytes<DT>::n), sh);
+#pragma unroll
+        for (int i = 0; i < Vec<DT>::n; ++i) y[i] += sh[i];
+    }
+}
+
 // Rows of at most G chunks (G in 4..64): G-lane segments, 64 / G rows per wave,
 // four waves per block, one chunk per lane.
-template <int DT, int G, int MODE>
+template <int DT, int G, int MODE, bool ADA>
 __global__ __launch_bounds__(256) void rmsnorm_small(NormParams p) {
     constexpr int V = Vec<DT>::n;
     constexpr int EB = EltBytes<DT>::n;
@@ -127,13 +151,14 @@ __global__ __launch_bounds__(256) void rmsnorm_small(NormParams p) {
     const bool have = row < p.T && j < chunks;
     const bool has_res = p.residual != nullptr;
     const int64_t off = (row * p.H + (int64_t)j * V) * EB;
-    u32x4 xv = u32x4{0u, 0u, 0u, 0u}, rv = xv, wv = ones16<DT>();
+    u32x4 xv = u32x4{0u, 0u, 0u, 0u}, rv = xv, wv = ones16<DT>(), gv = ones16<DT>();
     if (have) {
         xv = ld16_nt((const char*)p.x + off);
         if (has_res) rv = ld16_nt((const char*)p.residual + off);
         if (p.w) wv = ld16((const char*)p.w + (int64_t)j * V * EB);
+        if (ADA && p.gate) gv = ld16((const char*)p.gate + (int64_t)j * V * EB);
     }
-    const u32x4 sv = residual_sum<DT>(xv, rv, has_res);
+    const u32x4 sv = residual_sum<DT, ADA>(xv, rv, gv, has_res);
     float s[V];
     unpack<DT>(sv, s);
     const float ss = seg_sum<G>(have ? chunk_sumsq<DT>(s) : 0.0f);
@@ -145,6 +170,7 @@ __global__ __launch_bounds__(256) void rmsnorm_small(NormParams p) {
         unpack<DT>(wv, wf);
 #pragma unroll
         for (int i = 0; i < V; ++i) y[i] = (s[i] * inv) * (wf[i] + p.delta);
+        add_shift<DT, ADA>(p, (int64_t)j * V, y);
         emit<DT, MODE>(p, row, (int64_t)j * V, y, amax_acc);
     }
     if constexpr (MODE == kNormAmax) {
@@ -159,7 +185,7 @@ __global__ __launch_bounds__(256) void rmsnorm_small(NormParams p) {
 constexpr int kMaxNch = 6;
 constexpr int kMaxGroups = kMaxNch * 16;
 
-template <int DT, int NCH, int MODE>
+template <int DT, int NCH, int MODE, bool ADA>
 __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
     constexpr int V = Vec<DT>::n;
     constexpr int EB = EltBytes<DT>::n;
@@ -175,18 +201,21 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
     const bool has_res = p.residual != nullptr;
 
     // Every load of the row (x, residual, weight) is issued before any math.
-    u32x4 xv[NCH], rv[NCH], wv[NCH];
+    u32x4 xv[NCH], rv[NCH], wv[NCH], gv[ADA ? NCH : 1];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         const int ch = k * stride + wir * kWave + lane;
         xv[k] = u32x4{0u, 0u, 0u, 0u};
         rv[k] = u32x4{0u, 0u, 0u, 0u};
         wv[k] = ones16<DT>();
+        if constexpr (ADA) gv[k] = ones16<DT>();
         if (live && ch < chunks) {
             const int64_t off = (row * p.H + (int64_t)ch * V) * EB;
             xv[k] = ld16_nt((const char*)p.x + off);
             if (has_res) rv[k] = ld16_nt((const char*)p.residual + off);
             if (p.w) wv[k] = ld16((const char*)p.w + (int64_t)ch * V * EB);
+            if constexpr (ADA)
+                if (p.gate) gv[k] = ld16((const char*)p.gate + (int64_t)ch * V * EB);
         }
     }
     // group sums: chunk chains, then the 64-lane tree of each group
@@ -194,7 +223,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         const int ch = k * stride + wir * kWave + lane;
-        xv[k] = residual_sum<DT>(xv[k], rv[k], has_res);   // xv now holds s = R(x + r)
+        xv[k] = residual_sum<DT, ADA>(xv[k], rv[k], gv[ADA ? k : 0], has_res);   // s
         float s[V];
         unpack<DT>(xv[k], s);
         gs[k] = seg_sum<64>((live && ch < chunks) ? chunk_sumsq<DT>(s) : 0.0f);
@@ -230,6 +259,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
         unpack<DT>(wv[k], wf);
 #pragma unroll
         for (int i = 0; i < V; ++i) y[i] = (s[i] * inv) * (wf[i] + p.delta);
+        add_shift<DT, ADA>(p, e0, y);
         emit<DT, MODE>(p, row, e0, y, amax_acc);
     }
     if constexpr (MODE == kNormAmax) {
@@ -246,7 +276,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
 // element is read before the same thread overwrites it.
 constexpr int kScalarGroups = 1024;
 
-template <int DT, int MODE>
+template <int DT, int MODE, bool ADA>
 __global__ __launch_bounds__(256) void rmsnorm_scalar(NormParams p) {
     constexpr int V = Vec<DT>::n;
     __shared__ float gsum[kScalarGroups];
@@ -268,6 +298,7 @@ __global__ __launch_bounds__(256) void rmsnorm_scalar(NormParams p) {
                 float v = 0.0f;
                 if (e < p.H) {
                     v = ld_elt<DT>(p.x, base + e);
+                    if (ADA && p.gate) v = ld_elt<DT>(p.gate, e) * v;
                     if (has_res) v = round_trip<DT>(v + ld_elt<DT>(p.residual, base + e));
                 }
                 s[i] = v;
@@ -288,11 +319,13 @@ __global__ __launch_bounds__(256) void rmsnorm_scalar(NormParams p) {
     float amax_acc = 0.0f;
     for (int i = threadIdx.x; i < p.H; i += 256) {
         float s = ld_elt<DT>(p.x, base + i);
+        if (ADA && p.gate) s = ld_elt<DT>(p.gate, i) * s;
         if (has_res) {
             s = round_trip<DT>(s + ld_elt<DT>(p.residual, base + i));
             if (MODE != kNormAmax) st_elt<DT>(p.residual, base + i, s);
         }
-        const float y = (s * inv) * ((p.w ? ld_elt<DT>(p.w, i) : 1.0f) + p.delta);
+        float y = (s * inv) * ((p.w ? ld_elt<DT>(p.w, i) : 1.0f) + p.delta);
+        if (ADA) y += ld_elt<DT>(p.shift, i);
         if constexpr (MODE == kNormInPlace) st_elt<DT>(p.x_out, base + i, y);
         else if constexpr (MODE == kNormFp8) p.y8[base + i] = fp8x1(y * p.inv_scale);
         else amax_acc = fmaxf(amax_acc, fabsf(y));
@@ -328,71 +361,80 @@ int pick_wpr(int64_t T, int chunks) {
     return wpr;
 }
 
-template <int DT, int MODE, int NCH>
+template <int DT, int MODE, bool ADA, int NCH>
 hipError_t launch_vec_n(const NormParams& p, hipStream_t s) {
     const int64_t blocks = (p.T + p.rpb - 1) / p.rpb;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((rmsnorm_vec<DT, NCH, MODE>), dim3((uint32_t)blocks),
+    hipLaunchKernelGGL((rmsnorm_vec<DT, NCH, MODE, ADA>), dim3((uint32_t)blocks),
                        dim3(kWave * p.wpr * p.rpb), 0, s, p);
     return hipGetLastError();
 }
 
-template <int DT, int MODE, int G>
+template <int DT, int MODE, bool ADA, int G>
 hipError_t launch_small(const NormParams& p, hipStream_t s) {
     constexpr int RPB = 4 * (kWave / G);                 // rows per 256-thread block
     const int64_t blocks = (p.T + RPB - 1) / RPB;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((rmsnorm_small<DT, G, MODE>), dim3((uint32_t)blocks), dim3(256), 0, s,
-                       p);
+    hipLaunchKernelGGL((rmsnorm_small<DT, G, MODE, ADA>), dim3((uint32_t)blocks), dim3(256), 0,
+                       s, p);
     return hipGetLastError();
 }
 
-template <int DT, int MODE>
+template <int DT, int MODE, bool ADA>
 hipError_t launch_mode(const NormArgs& a, hipStream_t s) {
     constexpr int V = Vec<DT>::n;
     NormParams p{};
     p.x = a.x; p.x_out = a.x_out; p.residual = a.residual; p.w = a.w; p.y8 = a.y8;
     p.amax = a.amax; p.inv_scale = a.inv_scale; p.T = a.T; p.H = a.H; p.eps = a.eps;
     p.inv_H = 1.0f / (float)a.H; p.delta = (float)a.weight_offset;
+    p.gate = a.gate; p.shift = a.shift;
 
     const int chunks = a.H / V;
     bool vec = (a.H % V == 0) && chunks <= kMaxNch * kWave * 16 && aligned16(a.x) &&
                (a.w == nullptr || aligned16(a.w)) &&
                (a.residual == nullptr || aligned16(a.residual));
+    if (ADA) vec = vec && (a.gate == nullptr || aligned16(a.gate)) && aligned16(a.shift);
     if (MODE == kNormInPlace) vec = vec && aligned16(a.x_out);
     if (MODE == kNormFp8)
         vec = vec && ((reinterpret_cast<uintptr_t>(a.y8) & (V == 8 ? 7u : 3u)) == 0);
     if (vec && chunks <= kWave) {
-        if (chunks <= 4) return launch_small<DT, MODE, 4>(p, s);
-        if (chunks <= 8) return launch_small<DT, MODE, 8>(p, s);
-        if (chunks <= 16) return launch_small<DT, MODE, 16>(p, s);
-        if (chunks <= 32) return launch_small<DT, MODE, 32>(p, s);
-        return launch_small<DT, MODE, 64>(p, s);
+        if (chunks <= 4) return launch_small<DT, MODE, ADA, 4>(p, s);
+        if (chunks <= 8) return launch_small<DT, MODE, ADA, 8>(p, s);
+        if (chunks <= 16) return launch_small<DT, MODE, ADA, 16>(p, s);
+        if (chunks <= 32) return launch_small<DT, MODE, ADA, 32>(p, s);
+        return launch_small<DT, MODE, ADA, 64>(p, s);
     }
     if (vec) {
         p.wpr = pick_wpr(a.T, chunks);
         p.rpb = (p.wpr <= 4 && 4 % p.wpr == 0) ? 4 / p.wpr : 1;
         const int nch = (chunks + kWave * p.wpr - 1) / (kWave * p.wpr);
         switch (nch) {
-        case 1: return launch_vec_n<DT, MODE, 1>(p, s);
-        case 2: return launch_vec_n<DT, MODE, 2>(p, s);
-        case 3: return launch_vec_n<DT, MODE, 3>(p, s);
-        case 4: return launch_vec_n<DT, MODE, 4>(p, s);
-        case 5: return launch_vec_n<DT, MODE, 5>(p, s);
-        default: return launch_vec_n<DT, MODE, 6>(p, s);
+        case 1: return launch_vec_n<DT, MODE, ADA, 1>(p, s);
+        case 2: return launch_vec_n<DT, MODE, ADA, 2>(p, s);
+        case 3: return launch_vec_n<DT, MODE, ADA, 3>(p, s);
+        case 4: return launch_vec_n<DT, MODE, ADA, 4>(p, s);
+        case 5: return launch_vec_n<DT, MODE, ADA, 5>(p, s);
+        default: return launch_vec_n<DT, MODE, ADA, 6>(p, s);
         }
     }
     if (a.T > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((rmsnorm_scalar<DT, MODE>), dim3((uint32_t)a.T), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((rmsnorm_scalar<DT, MODE, ADA>), dim3((uint32_t)a.T), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_dt(const NormArgs& a, hipStream_t s) {
+    if (a.ada) {
+        switch (a.mode) {
+        case kNormInPlace: return launch_mode<DT, kNormInPlace, true>(a, s);
+        case kNormFp8: return launch_mode<DT, kNormFp8, true>(a, s);
+        default: return launch_mode<DT, kNormAmax, true>(a, s);
+        }
+    }
     switch (a.mode) {
-    case kNormInPlace: return launch_mode<DT, kNormInPlace>(a, s);
-    case kNormFp8: return launch_mode<DT, kNormFp8>(a, s);
-    default: return launch_mode<DT, kNormAmax>(a, s);
+    case kNormInPlace: return launch_mode<DT, kNormInPlace, false>(a, s);
+    case kNormFp8: return launch_mode<DT, kNormFp8, false>(a, s);
+    default: return launch_mode<DT, kNormAmax, false>(a, s);
     }
 }
 

@@ -124,6 +124,42 @@ def check_values(gpu, ora, dtype, label="", max_differ_frac=0.005):
     return dict(n=d.size, differ=differ, max_ulp=int(d.max()))
 
 
+def check_modulated(gpu, ora, a_mag, shift_mag, H, dtype, label="", max_escape_frac=None):
+    """Adaptive-norm outputs m = a + shift, a = n (1 + scale).  The rule of
+    check_values, except where a and the shift cancel: both sides' n differ
+    by at most ((H + 8)/2 + log2 H + 8) u |n| (the oracle's sequential sum of
+    squares against the kernels' tree, the square root and the products), so
+    an element may also pass within that much of |a| plus 2 u |shift| plus one
+    output step.  Such escapes are counted and bounded (fp32 outputs have no
+    output rounding to absorb the difference, so more of them lie past rel
+    1e-5: 1 % of elements there, 0.1 % for 16-bit outputs)."""
+    if max_escape_frac is None:
+        max_escape_frac = 0.01 if dtype == F32 else 0.001
+    gpu, ora = np.asarray(gpu), np.asarray(ora)
+    if ora.size == 0:
+        return dict(n=0)
+    g = W.bits_to_f32(gpu, dtype).astype(np.float64) if dtype != F32 else gpu.astype(np.float64)
+    o = W.bits_to_f32(ora, dtype).astype(np.float64) if dtype != F32 else ora.astype(np.float64)
+    u = 2.0 ** -24
+    bound = ((H + 8) / 2.0 + np.log2(H) + 8) * u * np.abs(a_mag) + 2 * u * np.abs(shift_mag)
+    if dtype == F32:
+        near = np.abs(g - o) <= 1e-5 * np.abs(o) + 1e-35
+        step = np.spacing(np.abs(o).astype(np.float32)).astype(np.float64)
+    else:
+        near = ulp16_dist(gpu, ora) <= 1
+        step = spacing16(ora, dtype)
+    esc = ~near & (np.abs(g - o) <= bound + step)
+    bad = int(np.count_nonzero(~near & ~esc))
+    assert bad == 0, f"{label}: {bad} elements beyond the cancellation bound"
+    escapes = int(np.count_nonzero(esc))
+    assert escapes <= max(4, max_escape_frac * o.size), f"{label}: {escapes} escapes"
+    differ = int(np.count_nonzero(g != o))
+    if dtype != F32:
+        assert differ <= max(4, 0.005 * o.size), \
+            f"{label}: {differ}/{o.size} elements differ (systematic rounding?)"
+    return dict(n=int(o.size), differ=differ, escapes=escapes)
+
+
 def check_bitwise(gpu, ora, label=""):
     gpu, ora = np.asarray(gpu), np.asarray(ora)
     if gpu.dtype == np.float32:

@@ -43,6 +43,9 @@ def lib():
         "mbt_fused_add_rmsnorm": [vp, vp, vp, i64, i32, f32, i32, i32, vp],
         "mbt_fused_add_rmsnorm_fp8": [vp, vp, vp, vp, f32, i64, i32, f32, i32, i32, vp],
         "mbt_fused_add_rmsnorm_amax": [vp, vp, vp, vp, i64, i32, f32, i32, i32, vp],
+        "mbt_adarms": [vp, vp, vp, vp, vp, i64, i32, f32, i32, vp],
+        "mbt_adarms_fp8": [vp, vp, vp, vp, vp, vp, f32, i64, i32, f32, i32, vp],
+        "mbt_adarms_amax": [vp, vp, vp, vp, vp, vp, i64, i32, f32, i32, vp],
         "mbt_gated_act": [vp, vp, i64, i32, i32, i32, vp],
         "mbt_gated_act_fp8": [vp, vp, f32, i64, i32, i32, i32, vp],
         "mbt_gated_act_amax": [vp, vp, i64, i32, i32, i32, vp],
@@ -60,7 +63,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 14
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), f"{n} declared in mbt.h but not exported"
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
@@ -289,3 +292,27 @@ def test_qkv_norm_rope_cache_rejects(lib, kw, status):
 def test_qkv_norm_rope_cache_empty_is_noop(lib):
     assert qkv_cache(lib, T=0, qkv=None, q_out=None, kc=None, vc=None, slot=None, w_q=None,
                      w_k=None, cos_sin=None, pos=None) == OK
+
+
+def test_adarms_rejects(lib):
+    f, g, h = lib.mbt_adarms, lib.mbt_adarms_fp8, lib.mbt_adarms_amax
+    SC, SH, GT = W1, W2, CS
+    assert f(A, B, GT, SC, SH, 4, 2048, 1e-6, 9, None) == DTYPE
+    assert f(A, B, GT, SC, SH, 4, 0, 1e-6, BF16, None) == SHAPE
+    assert f(A, B, GT, SC, SH, 4, 2048, NAN, BF16, None) == SCALAR
+    assert f(A, None, GT, SC, SH, 4, 2048, 1e-6, BF16, None) == NULLP    # gate needs residual
+    assert f(A, B, GT, None, SH, 4, 2048, 1e-6, BF16, None) == NULLP
+    assert f(A, B, GT, SC, None, 4, 2048, 1e-6, BF16, None) == NULLP
+    assert f(A, B, GT, SC, SH + 1, 4, 2048, 1e-6, BF16, None) == ALIGN
+    assert f(A, B, GT + 1, SC, SH, 4, 2048, 1e-6, BF16, None) == ALIGN
+    assert f(A, B, GT, SC, A + 64, 4, 2048, 1e-6, BF16, None) == ALIAS   # shift inside x
+    assert f(A, B, B + 64, SC, SH, 4, 2048, 1e-6, BF16, None) == ALIAS   # gate inside residual
+    assert f(A, B, GT, A + 128, SH, 4, 2048, 1e-6, BF16, None) == ALIAS  # scale inside x
+    assert f(None, None, None, None, None, 0, 2048, 1e-6, BF16, None) == OK
+    assert g(A, B, GT, SC, SH, C, 0.0, 4, 2048, 1e-6, BF16, None) == SCALAR
+    assert g(A, B, GT, SC, SH, None, 1.0, 4, 2048, 1e-6, BF16, None) == NULLP
+    assert g(A, B, GT, SC, SH, SH + 8, 1.0, 4, 2048, 1e-6, BF16, None) == ALIAS  # y over shift
+    assert g(A, B, GT, SC, SH, B + 4, 1.0, 4, 2048, 1e-6, BF16, None) == ALIAS   # y in residual
+    assert h(A, B, GT, SC, SH, None, 4, 2048, 1e-6, BF16, None) == NULLP
+    assert h(A, B, GT, SC, SH, C + 2, 4, 2048, 1e-6, BF16, None) == ALIGN
+    assert h(A, B, GT, SC, SH, GT + 4, 4, 2048, 1e-6, BF16, None) == ALIAS       # amax on gate

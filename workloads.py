@@ -224,6 +224,51 @@ class ActCell:
         return (2 * self.d * s + self.d * (1 if self.fp8 else s)) * self.T
 
 
+@dataclass
+class AdaCell:
+    """Adaptive RMSNorm inputs: rows x (and a residual stream) ~ N(0, x_std),
+    and one synthetic style vector per call -- scale, shift ~ N(0, 0.1) and a
+    residual gate ~ N(1, 0.1) -- standing in for the per-prompt modulation
+    the pages describe (no model weights exist here)."""
+    name: str
+    config: int
+    cell: int
+    T: int
+    H: int
+    dtype: int
+    residual: bool = True
+    gate: bool = True
+    fp8: bool = False
+    x_std: float = 1.0
+    eps: float = 1e-6
+
+    def inputs(self):
+        k = (self.config, self.cell)
+        shp = (self.T, self.H)
+        return dict(
+            x=normal_bits(k + (T_Q,), shp, 0.0, self.x_std, self.dtype),
+            residual=normal_bits(k + (T_K,), shp, 0.0, self.x_std, self.dtype)
+            if self.residual else None,
+            gate=normal_bits(k + (T_WK,), (self.H,), 1.0, 0.1, self.dtype)
+            if self.gate else None,
+            scale=normal_bits(k + (T_WQ,), (self.H,), 0.0, 0.1, self.dtype),
+            shift=normal_bits(k + (T_POS,), (self.H,), 0.0, 0.1, self.dtype))
+
+    def calibration_inputs(self):
+        k = (self.config, self.cell, CALIBRATION_TENSOR)
+        shp = (self.T, self.H)
+        return dict(x=normal_bits(k + (T_Q,), shp, 0.0, self.x_std, self.dtype),
+                    residual=normal_bits(k + (T_K,), shp, 0.0, self.x_std, self.dtype)
+                    if self.residual else None)
+
+    def bytes_algorithmic(self):
+        s = ELEM_BYTES[self.dtype]
+        rd = 2 if self.residual else 1                   # x (+ residual) read
+        vec = (3 if self.gate else 2) * self.H * s       # style vectors, once
+        wr = (1 if self.residual else 0) * s + (1 if self.fp8 else s)
+        return (rd * s + wr) * self.H * self.T + vec
+
+
 # Configuration 1: Qwen3-style per-head QK-norm + RoPE, head_dim 128, full
 # rotary, (Q, K) = (16, 8), four tokens, one of them at position 4096 (just
 # outside a 4096-row cache: normalised, not rotated).
