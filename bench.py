@@ -238,7 +238,7 @@ def prologue_cold_us(torch, mbt, W, cell, launches=2000):
     return us
 
 
-def route_us(torch, mbt, W, cell, cold, passes=5, samples=50, inner=32, launches=2000):
+def route_us(torch, mbt, W, cell, cold, passes=7, samples=50, inner=32, launches=6000):
     """The fused prologue against the split route it replaces -- RMSNorm of
     the q head-rows, RMSNorm of the k head-rows (mbt_fused_add_rmsnorm with
     residual NULL), then mbt_rope -- both in place, with a null arm: the

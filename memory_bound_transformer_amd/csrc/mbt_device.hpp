@@ -277,17 +277,6 @@ __device__ __forceinline__ float rot_mac(float own, float c, float other, float 
     return p + q;
 }
 
-// XCD-aware block renumbering.  MI355X dispatches workgroup b to XCD b % 8;
-// XCD x therefore runs hardware blocks x, x + 8, x + 16, ...  Map them to the
-// contiguous logical range [x q + min(x, r), ... + count(x)), q = nb / 8,
-// r = nb % 8, count(x) = q + (x < r): a bijection on [0, nb) that keeps
-// neighbouring logical blocks (and the data they share) on one XCD's L2.
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb) {
-    const uint32_t x = b & 7u, slot = b >> 3;
-    const uint32_t q = nb >> 3, r = nb & 7u;
-    return x * q + (x < r ? x : r) + slot;
-}
-
 // Sum of squares of one 16-byte chunk, as an explicit FMA chain in element
 // order.  Every kernel forms a row's sum the same way -- per-chunk chains,
 // then a balanced tree over the chunk index (DPP and lane swaps in a wave,

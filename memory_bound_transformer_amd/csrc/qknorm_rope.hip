@@ -36,8 +36,8 @@
 //    pair is rotated as written -- two rounded products, one rounded sum.
 //  * q / k chunks are streamed with nontemporal loads and stores; weights,
 //    positions and cos/sin rows use ordinary cached loads.
-//  * Workgroups are renumbered so each of the 8 XCDs (dispatched round-robin)
-//    gets a contiguous range of rows.
+//  * Workgroups run in dispatch order, round-robin over the 8 XCDs (an
+//    XCD-contiguous renumbering measured slower; see the kernel).
 //
 // A scalar kernel (one wave per head-row, LDS-staged rotation) covers every
 // shape and alignment the vector kernel does not; both give identical
@@ -67,9 +67,7 @@ struct QkParams {
     int32_t layout;           // 0 rotate-half, 1 interleaved
     float inv_Q, inv_K;       // vector kernel: 1/Q, 1/K for the token index
     uint32_t q_waves;         // vector kernel: waves over the T*Q query rows
-    uint32_t qk_waves;        // vector kernel: q_waves + waves over the key rows
-    uint32_t total_waves;     // vector kernel: qk_waves + waves over the value rows
-    uint32_t n_blocks;
+    uint32_t total_waves;     // vector kernel: q_waves + waves over the key rows
 };
 
 // The general forms' extra arguments (token strides, slot table, value rows,
@@ -116,8 +114,8 @@ __device__ __forceinline__ void partner_f32(const float* n, float* nb, int hv, b
 // tensors and token strides, every rotated chunk inside chunk group 0, rows
 // of each tensor below 2^24, and for rotate-half rot/2 a multiple of
 // Vec<DT> and a 16-byte aligned cos/sin cache (interleaved reads its run
-// element-wise).  Waves cover the query rows, then the key rows, then (when
-// v_in is given) the value rows, which are copied unchanged to their slot.
+// element-wise).  Waves cover the query rows, then the key rows; with v_in
+// a key wave also copies the value heads of its rows, unchanged, to their slot.
 template <int DT, int G, int C, int LAYOUT, bool GEN>
 __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g) {
     constexpr int V = Vec<DT>::n;
@@ -127,26 +125,21 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     // registers per lane, which keeps these kernels at 8 waves per SIMD.
     __shared__ float wsh[C >= 2 ? 2 : 1][C >= 2 ? 512 : 1];
 
-    const uint32_t lb = xcd_remap(blockIdx.x, p.n_blocks);
-    const uint32_t wv = (uint32_t)uniform((int)(lb * 4u + (threadIdx.x >> 6)));
+    // Blocks keep their dispatch order, which deals them round-robin over
+    // the 8 XCDs.  Renumbering them so that each XCD takes a contiguous range
+    // of rows was measured slower at every width, and badly so when key
+    // waves carry value heads (twice a query wave's bytes): a contiguous
+    // range put those on one XCD, whose share of the fabric then bounded the
+    // launch (15.2 us against 11.9 us, (Q, K) = (24, 4), T = 2048).
+    const uint32_t wv = (uint32_t)uniform((int)(blockIdx.x * 4u + (threadIdx.x >> 6)));
     const bool wave_live = wv < p.total_waves;
-    // wave-uniform kind: 0 query rows, 1 key rows, 2 value rows (GEN only)
-    const bool is_q = wv < p.q_waves;
-    const int kind = is_q ? 0 : ((!GEN || wv < p.qk_waves) ? 1 : 2);
+    const bool is_q = wv < p.q_waves;                       // wave-uniform tensor
     const int heads = is_q ? p.Q : p.K;
     const float inv_heads = is_q ? p.inv_Q : p.inv_K;
     const int64_t nrows = wave_live ? p.T * heads : 0;
-    int64_t row0 = (int64_t)(is_q ? wv : wv - p.q_waves) * RPW;
-    if constexpr (GEN)
-        if (kind == 2) row0 = (int64_t)(wv - p.qk_waves) * RPW;
+    const int64_t row0 = (int64_t)(is_q ? wv : wv - p.q_waves) * RPW;
     const char* src = (const char*)(is_q ? p.q_in : p.k_in);
     char* dst = (char*)(is_q ? p.q_out : p.k_out);
-    if constexpr (GEN) {
-        if (kind == 2) {
-            src = (const char*)g.v_in;
-            dst = (char*)g.v_out;
-        }
-    }
     const char* wp = (const char*)(is_q ? p.w_q : p.w_k);
 
     const int lane = threadIdx.x & 63;
@@ -167,6 +160,13 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     int32_t t = 0;
     int64_t out_off = row * p.D, orow = 0;
     u32x4 x[C];
+    // GEN with value rows: a key wave also carries the value heads of its
+    // rows (adjacent to the key heads in a fused QKV buffer), loaded beside
+    // the keys and stored to the same slot before any arithmetic.
+    u32x4 vx[GEN ? C : 1];
+    int64_t v_off = 0;
+    bool carry_v = false;
+    if constexpr (GEN) carry_v = !is_q && g.v_in != nullptr;
     if constexpr (!GEN) {
         const char* rsrc = src + row * (int64_t)p.D * EB;
 #pragma unroll
@@ -182,16 +182,24 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
         int32_t h = (int32_t)r32 - t * heads;
         if (h >= heads) { t += 1; h -= heads; }
         if (h < 0) { t -= 1; h += heads; }
-        const int64_t in_st = kind == 0 ? g.q_in_st : kind == 1 ? g.k_in_st : g.v_in_st;
-        const int64_t out_st = kind == 0 ? g.q_out_st : kind == 1 ? g.k_out_st : g.v_out_st;
+        const int64_t in_st = is_q ? g.q_in_st : g.k_in_st;
+        const int64_t out_st = is_q ? g.q_out_st : g.k_out_st;
         const char* rsrc = src + ((int64_t)t * in_st + (int64_t)h * p.D) * EB;
 #pragma unroll
         for (int k = 0; k < C; ++k)
             x[k] = live ? ld16_nt(rsrc + (k * G + j) * 16) : u32x4{0u, 0u, 0u, 0u};
-        orow = live ? out_row(g, kind != 0 && g.slot != nullptr, t) : -1;
+        if (carry_v) {
+            const char* vsrc =
+                (const char*)g.v_in + ((int64_t)t * g.v_in_st + (int64_t)h * p.D) * EB;
+#pragma unroll
+            for (int k = 0; k < C; ++k)
+                vx[k] = live ? ld16_nt(vsrc + (k * G + j) * 16) : u32x4{0u, 0u, 0u, 0u};
+        }
+        orow = live ? out_row(g, !is_q && g.slot != nullptr, t) : -1;
         out_off = (orow >= 0 ? orow : 0) * out_st + (int64_t)h * p.D;
+        v_off = (orow >= 0 ? orow : 0) * g.v_out_st + (int64_t)h * p.D;
     }
-    const int64_t ppos = (live && kind != 2) ? p.pos[t] : -1;
+    const int64_t ppos = live ? p.pos[t] : -1;
     float wreg[C >= 2 ? 1 : V];
     if constexpr (C >= 2) {
         for (int i = threadIdx.x; i < p.D; i += 256) {
@@ -200,19 +208,17 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
         }
         __syncthreads();                                   // x loads already in flight
     } else {
-        unpack<DT>((wave_live && kind != 2) ? ld16(wp + j * 16) : u32x4{0u, 0u, 0u, 0u}, wreg);
+        unpack<DT>(wave_live ? ld16(wp + j * 16) : u32x4{0u, 0u, 0u, 0u}, wreg);
 #pragma unroll
         for (int i = 0; i < V; ++i) wreg[i] += p.delta;
     }
     if (!wave_live) return;
     char* rdst = dst + out_off * EB;
     if constexpr (GEN) {
-        if (kind == 2) {                                   // value rows: copy to the slot
-            if (orow >= 0) {
+        if (carry_v && orow >= 0) {                        // value heads: copy to the slot
+            char* vdst = (char*)g.v_out + v_off * EB;
 #pragma unroll
-                for (int k = 0; k < C; ++k) st16_nt(rdst + (k * G + j) * 16, x[k]);
-            }
-            return;
+            for (int k = 0; k < C; ++k) st16_nt(vdst + (k * G + j) * 16, vx[k]);
         }
     }
     const bool rotate = (ppos >= 0) && (ppos < p.max_pos) && (p.rot > 0);
@@ -422,7 +428,7 @@ int env_int(const char* name, int dflt) {
     return e ? atoi(e) : dflt;
 }
 int tun_strided_rows() {
-    static const int v = env_int("MBT_QK_STRIDED_ROWS", 4096);
+    static const int v = env_int("MBT_QK_STRIDED_ROWS", 12288);
     return v;
 }
 int tun_c_max() {
@@ -436,16 +442,14 @@ hipError_t launch_vec(const QkParams& p0, const QkGen<true>& g0, hipStream_t s) 
     constexpr int RPW = kWave / G;
     const int64_t qw = (p.T * p.Q + RPW - 1) / RPW;
     const int64_t kw = (p.T * p.K + RPW - 1) / RPW;
-    const int64_t vw = (GEN && g0.v_in) ? kw : 0;
-    if (qw + kw + vw > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    if (qw + kw > 0x7FFFFFFFll) return hipErrorInvalidValue;
     p.q_waves = (uint32_t)qw;
-    p.qk_waves = (uint32_t)(qw + kw);
-    p.total_waves = (uint32_t)(qw + kw + vw);
-    p.n_blocks = (p.total_waves + 3u) / 4u;
+    p.total_waves = (uint32_t)(qw + kw);
+    const uint32_t n_blocks = (p.total_waves + 3u) / 4u;
     QkGen<GEN> g{};
     if constexpr (GEN) g = g0;
-    hipLaunchKernelGGL((qknorm_rope_vec<DT, G, C, LAYOUT, GEN>), dim3(p.n_blocks), dim3(256), 0,
-                       s, p, g);
+    hipLaunchKernelGGL((qknorm_rope_vec<DT, G, C, LAYOUT, GEN>), dim3(n_blocks), dim3(256), 0, s,
+                       p, g);
     return hipGetLastError();
 }
 

@@ -348,7 +348,7 @@ int env_int(const char* name, int dflt) {
 
 int pick_wpr(int64_t T, int chunks) {
     static const int forced = env_int("MBT_NORM_WPR", 0);
-    static const int wide_rows = env_int("MBT_NORM_WIDE_CHUNKS", 32768);
+    static const int wide_rows = env_int("MBT_NORM_WIDE_CHUNKS", 8192);
     const int per64 = (chunks + kWave - 1) / kWave;    // chunk groups
     const int min_wpr = (per64 + kMaxNch - 1) / kMaxNch;
     int wpr;
