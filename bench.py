@@ -31,6 +31,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -415,12 +416,23 @@ def prefill_cell(W):
 def source_digest(kernel):
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "memory_bound_transformer_amd")
-    # the compiler flags (build.py) shape the kernel as much as its source
+    # the compiler flags (build.py) shape the kernel as much as its source;
+    # comments and layout do not, so they are left out of the digest
     for path in (os.path.join(pkg, "csrc", KERNEL_SOURCES[kernel]),
                  os.path.join(pkg, "csrc", "mbt_device.hpp"), os.path.join(pkg, "build.py")):
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            h.update(_code_only(f.read(), path.endswith(".py")).encode())
     return h.hexdigest()
+
+
+def _code_only(text, python):
+    """Source text without comments and blank lines, each line stripped."""
+    if python:
+        text = re.sub(r'(?m)^\s*#.*$', "", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.strip() for l in text.splitlines() if l.strip())
 
 
 def traffic_for(key, kernel):

@@ -8,6 +8,13 @@
 // angles of the token's position (rotate-half or interleaved pairs).  Tokens
 // positioned beyond the cache get the norm only; their rotation is skipped.
 //
+// The same kernels serve the general forms: token strides (q and k as views
+// into a fused QKV buffer; "thox-edge-ops v2", section 6), the single-rounding
+// variant (ninfer PR #273, review item 1: rotate the fp32 norm result, round
+// once), and the key / value cache write (FlashRT's qkv_split_rope_kvcache;
+// "thox-edge-ops v2", section 10): key heads go to row slot[t] of the cache
+// and a key wave also copies the token's value heads there.
+//
 // MI355X design (the pages' CUDA kernel -- one block per token, one warp per
 // head, a block barrier between norm and rotation -- is prior art only):
 //
@@ -40,8 +47,8 @@
 //    XCD-contiguous renumbering measured slower; see the kernel).
 //
 // A scalar kernel (one wave per head-row, LDS-staged rotation) covers every
-// shape and alignment the vector kernel does not; both give identical
-// results up to the reduction order of the fp32 sum of squares.
+// shape and alignment the vector kernel does not; it follows the same
+// reduction tree, so both give identical bits.
 
 #include <stdlib.h>
 
