@@ -121,6 +121,16 @@ EDGE_PROLOGUE = [
     _cell(name="positions_out", T=6, outside=((0, -1), (2, 512), (3, 1 << 40), (5, -(1 << 40))),
           cell=18),
     _cell(name="long_T", T=3000, Q=3, K=1, cell=19),
+    # prefill-width launch shapes (>= 12288 head-rows): two chunks per lane
+    # (rot 96: 12 rotated chunks need 16 lanes), four with interleaved pairs,
+    # four in fp32
+    _cell(name="c2_bf16_d256_rot96", D=256, rot=96, T=1024, Q=16, K=2, max_pos=4096, cell=30),
+    _cell(name="c4_bf16_d256_inter32", D=256, rot=32, layout=W.INTERLEAVED, T=1024, Q=16,
+          K=2, max_pos=4096, cell=31),
+    _cell(name="c4_f32_d256_rot64", dtype=W.F32, D=256, rot=64, T=1024, Q=16, K=2,
+          max_pos=4096, cell=32),
+    _cell(name="c2_f16_d128_full", dtype=W.F16, D=128, rot=128, T=1024, Q=16, K=2,
+          max_pos=4096, cell=33),
 ]
 
 

@@ -92,6 +92,10 @@ ONCE_CELLS = [
           outside=(), cell=10),
     _cell(name="once_f16_prefill_16x2_inter", T=2048, Q=16, K=2, dtype=W.F16, rot=256,
           layout=W.INTERLEAVED, positions="arange", max_pos=4096, outside=(), cell=11),
+    _cell(name="once_bf16_c2_rot96", rot=96, T=1024, Q=16, K=2, max_pos=4096, cell=12),
+    _cell(name="once_bf16_c4_inter32", rot=32, layout=W.INTERLEAVED, T=1024, Q=16, K=2,
+          max_pos=4096, cell=13),
+    _cell(name="once_f32_c4_rot64", dtype=W.F32, T=1024, Q=16, K=2, max_pos=4096, cell=14),
 ]
 
 

@@ -75,6 +75,12 @@ ROUTE_CELLS = [
     _cell(name="f32_d256_rot112_hv14", dtype=W.F32, rot=112, cell=15),
     _cell(name="bf16_prefill_24x4", T=2048, Q=24, K=4, positions="arange", max_pos=4096,
           outside=(), cell=12),
+    # the other prefill launch shapes: two chunks per lane, four with
+    # interleaved pairs, four in fp32
+    _cell(name="bf16_c2_rot96", rot=96, T=1024, Q=16, K=2, max_pos=4096, cell=16),
+    _cell(name="bf16_c4_inter32", rot=32, layout=W.INTERLEAVED, T=1024, Q=16, K=2,
+          max_pos=4096, cell=17),
+    _cell(name="f32_c4_rot64", dtype=W.F32, T=1024, Q=16, K=2, max_pos=4096, cell=18),
 ]
 
 
