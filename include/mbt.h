@@ -112,7 +112,7 @@ typedef enum { MBT_ACT_SILU = 0, MBT_ACT_GELU_TANH = 1 } mbt_act;
  *  cos_sin  [max_pos][rot_dim] fp32    caller-built cache: cos in columns
  *                                      [0, rot_dim/2), sin in [rot_dim/2, rot_dim)
  *  pos    [T] int64                    position of each token
- *  Q, K   >= 0, Q + K >= 1             heads per token
+ *  Q, K   0 .. 2^20, Q + K >= 1        heads per token
  *  T      >= 0                         tokens
  *  head_dim 1..512; rot_dim even, 0..head_dim; eps finite, >= 0;
  *  max_pos >= 0; weight_offset in {0,1}; layout mbt_rope_layout; dtype mbt_dtype.
@@ -238,7 +238,7 @@ MBT_API mbt_status mbt_rope(void* q, void* k, const float* cos_sin, int64_t max_
  *                         x_i <- R(s_i * inv) (P3, weight folding: the scale
  *                         is folded into the next GEMM's weight at load
  *                         time), and then weight_offset must be 0
- *  T >= 0; H >= 1 (any width, odd included); eps finite >= 0;
+ *  T >= 0; 1 <= H <= 2^28 (any width, odd included); eps finite >= 0;
  *  weight_offset in {0,1}; dtype mbt_dtype.
  *  Errors: NULL x (T > 0), or NULL w with weight_offset 1 -> NULL_POINTER.
  */
@@ -329,7 +329,7 @@ MBT_API mbt_status mbt_adarms_amax(const void* x, const void* residual, const vo
  *
  *  gate_up [T][2d] dtype  read
  *  out     [T][d]  dtype  written; must not overlap gate_up
- *  T >= 0; d >= 1; act mbt_act; dtype mbt_dtype.
+ *  T >= 0; 1 <= d <= 2^28; act mbt_act; dtype mbt_dtype.
  */
 MBT_API mbt_status mbt_gated_act(const void* gate_up, void* out, int64_t T, int32_t d,
                          int32_t act, int32_t dtype, void* stream);

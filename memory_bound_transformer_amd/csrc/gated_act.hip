@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void gated_vec(ActParams p) {
     const uint32_t bpr = (uint32_t)p.blocks_per_row;
     const int64_t t = (int64_t)(blockIdx.x / bpr);
     const int cb = (int)(blockIdx.x % bpr);
-    const char* row = (const char*)p.gate_up + t * (int64_t)(2 * p.d) * EB;
+    const char* row = (const char*)p.gate_up + t * (2 * (int64_t)p.d) * EB;
     u32x4 gv[U], uv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void gated_scalar(ActParams p) {
     const int j = (int)(blockIdx.x % bpr) * 256 + threadIdx.x;
     float amax_acc = 0.0f;
     if (j < p.d) {
-        const int64_t gi = t * (int64_t)(2 * p.d) + j;
+        const int64_t gi = t * (2 * (int64_t)p.d) + j;
         const float y = act_mul<DT, ACT>(ld_elt<DT>(p.gate_up, gi),
                                          ld_elt<DT>(p.gate_up, gi + p.d));
         const int64_t o = t * (int64_t)p.d + j;

@@ -65,6 +65,15 @@ mbt_status check_alias(const Range& out, const Range& in, bool same_ok) {
     return fail(MBT_ERR_ALIAS, "%s overlaps %s", out.name, in.name);
 }
 
+// Heads per token (query or key) accepted by the prologue entry points: far
+// above any model's, and small enough that every sum of head counts and
+// every head index stays inside int32.
+constexpr int32_t kMaxHeads = 1 << 20;
+
+// Widest norm row (H) and activation half (d): every element and chunk index
+// inside a row, rounded up to whole blocks, stays inside int32.
+constexpr int32_t kMaxRow = 1 << 28;
+
 // Safe product of non-negative sizes, or -1 past 2^62.
 int64_t mul(int64_t a, int64_t b) {
     if (a < 0 || b < 0) return -1;
@@ -142,7 +151,8 @@ mbt_status qk_run(QkCall c, void* stream) {
     if (c.weight_offset != 0 && c.weight_offset != 1)
         return fail(MBT_ERR_BAD_ENUM, "weight_offset %d", c.weight_offset);
     if (c.flags & ~MBT_QK_ROUND_ONCE) return fail(MBT_ERR_BAD_ENUM, "flags 0x%x", c.flags);
-    if (c.Q < 0 || c.K < 0 || c.Q + c.K < 1) return fail(MBT_ERR_BAD_SHAPE, "Q=%d K=%d", c.Q, c.K);
+    if (c.Q < 0 || c.K < 0 || c.Q > kMaxHeads || c.K > kMaxHeads || c.Q + c.K < 1)
+        return fail(MBT_ERR_BAD_SHAPE, "Q=%d K=%d", c.Q, c.K);
     if (c.T < 0) return fail(MBT_ERR_BAD_SHAPE, "T=%lld", (long long)c.T);
     if (c.D < 1 || c.D > 512) return fail(MBT_ERR_BAD_SHAPE, "head_dim %d not in [1, 512]", c.D);
     if (c.rot < 0 || c.rot > c.D || (c.rot % 2) != 0)
@@ -157,7 +167,7 @@ mbt_status qk_run(QkCall c, void* stream) {
     for (int i = 0; i < 6; ++i) {
         if (*sts[i] == 0) *sts[i] = need[i];
         if (*sts[i] < need[i] || *sts[i] > (INT64_C(1) << 40))
-            return fail(MBT_ERR_BAD_SHAPE, "token stride %lld below the row width %lld",
+            return fail(MBT_ERR_BAD_SHAPE, "token stride %lld outside [%lld, 2^40]",
                         (long long)*sts[i], (long long)need[i]);
     }
     const int eb = elt_bytes(c.dtype);
@@ -293,17 +303,18 @@ mbt_status mbt_qkv_norm_rope_cache(const void* qkv, void* q_out, void* k_cache, 
                                    int32_t weight_offset, int32_t layout, int32_t dtype,
                                    int32_t flags, void* stream) {
     if (!valid_dtype(dtype)) return fail(MBT_ERR_BAD_DTYPE, "dtype %d", dtype);
-    if (K < 1 || Q < 0) return fail(MBT_ERR_BAD_SHAPE, "Q=%d K=%d (a cache needs K >= 1)", Q, K);
+    if (K < 1 || Q < 0 || Q > kMaxHeads || K > kMaxHeads)
+        return fail(MBT_ERR_BAD_SHAPE, "Q=%d K=%d (a cache needs K >= 1)", Q, K);
     if (head_dim < 1 || head_dim > 512)
         return fail(MBT_ERR_BAD_SHAPE, "head_dim %d not in [1, 512]", head_dim);
     if (T > 0 && (!qkv || !k_cache || !v_cache || !slot))
         return fail(MBT_ERR_NULL_POINTER, "qkv, k_cache, v_cache and slot are required");
     const int eb = elt_bytes(dtype);
     const char* base = (const char*)qkv;
-    const int64_t tok = (int64_t)(Q + 2 * K) * head_dim;        // elements per token
+    const int64_t tok = ((int64_t)Q + 2 * (int64_t)K) * head_dim;   // elements per token
     QkCall c{};
     c.q_in = base; c.k_in = base ? base + (int64_t)Q * head_dim * eb : nullptr;
-    c.v_in = base ? base + (int64_t)(Q + K) * head_dim * eb : nullptr;
+    c.v_in = base ? base + ((int64_t)Q + K) * head_dim * eb : nullptr;
     c.q_out = q_out; c.k_out = k_cache; c.v_out = v_cache;
     c.w_q = w_q; c.w_k = w_k; c.cos_sin = cos_sin; c.max_pos = max_pos; c.pos = pos;
     c.Q = Q; c.K = K; c.T = T; c.D = head_dim; c.rot = rot_dim; c.eps = eps;
@@ -320,7 +331,8 @@ mbt_status mbt_rope(void* q, void* k, const float* cos_sin, int64_t max_pos, con
     if (!valid_dtype(dtype)) return fail(MBT_ERR_BAD_DTYPE, "dtype %d", dtype);
     if (layout != MBT_ROPE_ROTATE_HALF && layout != MBT_ROPE_INTERLEAVED)
         return fail(MBT_ERR_BAD_ENUM, "layout %d", layout);
-    if (Q < 0 || K < 0 || Q + K < 1) return fail(MBT_ERR_BAD_SHAPE, "Q=%d K=%d", Q, K);
+    if (Q < 0 || K < 0 || Q > kMaxHeads || K > kMaxHeads || Q + K < 1)
+        return fail(MBT_ERR_BAD_SHAPE, "Q=%d K=%d", Q, K);
     if (T < 0) return fail(MBT_ERR_BAD_SHAPE, "T=%lld", (long long)T);
     if (head_dim < 1 || head_dim > 512)
         return fail(MBT_ERR_BAD_SHAPE, "head_dim %d not in [1, 512]", head_dim);
@@ -364,7 +376,8 @@ mbt_status norm_common(const void* x, const void* residual, const void* w, int64
     if (!valid_dtype(dtype)) return fail(MBT_ERR_BAD_DTYPE, "dtype %d", dtype);
     if (weight_offset != 0 && weight_offset != 1)
         return fail(MBT_ERR_BAD_ENUM, "weight_offset %d", weight_offset);
-    if (T < 0 || H < 1) return fail(MBT_ERR_BAD_SHAPE, "T=%lld H=%d", (long long)T, H);
+    if (T < 0 || H < 1 || H > kMaxRow)
+        return fail(MBT_ERR_BAD_SHAPE, "T=%lld H=%d", (long long)T, H);
     if (!finite_nonneg(eps)) return fail(MBT_ERR_BAD_SCALAR, "eps must be finite and >= 0");
     const int eb = elt_bytes(dtype);
     const int64_t bytes = mul(mul(T, H), eb);
@@ -556,7 +569,8 @@ mbt_status act_common(const void* gate_up, int64_t T, int32_t d, int32_t act, in
     if (!valid_dtype(dtype)) return fail(MBT_ERR_BAD_DTYPE, "dtype %d", dtype);
     if (act != MBT_ACT_SILU && act != MBT_ACT_GELU_TANH)
         return fail(MBT_ERR_BAD_ENUM, "act %d", act);
-    if (T < 0 || d < 1) return fail(MBT_ERR_BAD_SHAPE, "T=%lld d=%d", (long long)T, d);
+    if (T < 0 || d < 1 || d > kMaxRow)
+        return fail(MBT_ERR_BAD_SHAPE, "T=%lld d=%d", (long long)T, d);
     const int eb = elt_bytes(dtype);
     const int64_t bytes = mul(mul(T, 2 * (int64_t)d), eb);
     if (bytes < 0) return fail(MBT_ERR_BAD_SHAPE, "tensor sizes overflow");

@@ -106,6 +106,7 @@ def qk(lib, **kw):
     (dict(dtype=3), DTYPE), (dict(dtype=-1), DTYPE),
     (dict(layout=2), ENUM), (dict(weight_offset=2), ENUM),
     (dict(Q=0, K=0), SHAPE), (dict(Q=-1), SHAPE), (dict(T=-1), SHAPE),
+    (dict(Q=(1 << 20) + 1), SHAPE), (dict(Q=2**31 - 1, K=2**31 - 1), SHAPE),
     (dict(head_dim=0), SHAPE), (dict(head_dim=513), SHAPE),
     (dict(rot_dim=63), SHAPE), (dict(rot_dim=258), SHAPE), (dict(rot_dim=-2), SHAPE),
     (dict(eps=NAN), SCALAR), (dict(eps=-1e-6), SCALAR), (dict(eps=INF), SCALAR),
@@ -138,6 +139,7 @@ def test_norm_rejects(lib):
     assert f(A, B, W1, 4, 2560, 1e-6, 0, 7, None) == DTYPE
     assert f(A, B, W1, 4, 2560, 1e-6, 3, BF16, None) == ENUM
     assert f(A, B, W1, 4, 0, 1e-6, 0, BF16, None) == SHAPE
+    assert f(A, B, W1, 4, (1 << 28) + 1, 1e-6, 0, BF16, None) == SHAPE
     assert f(A, B, W1, -1, 8, 1e-6, 0, BF16, None) == SHAPE
     assert f(A, B, W1, 4, 8, NAN, 0, BF16, None) == SCALAR
     assert f(None, B, W1, 4, 8, 1e-6, 0, BF16, None) == NULLP
@@ -171,6 +173,7 @@ def test_act_rejects(lib):
     assert f(A, B, 4, 10240, 2, BF16, None) == ENUM
     assert f(A, B, 4, 10240, 0, 9, None) == DTYPE
     assert f(A, B, 4, 0, 0, BF16, None) == SHAPE
+    assert f(A, B, 4, 2**31 - 1, 0, BF16, None) == SHAPE
     assert f(A, B, -2, 16, 0, BF16, None) == SHAPE
     assert f(None, B, 4, 16, 0, BF16, None) == NULLP
     assert f(A, None, 4, 16, 0, BF16, None) == NULLP
@@ -204,6 +207,7 @@ def test_rope_rejects(lib):
     assert call(dt=5) == DTYPE
     assert call(lay=3) == ENUM
     assert call(Q=0, K=0) == SHAPE
+    assert call(Q=2**31 - 1, K=2**31 - 1) == SHAPE
     assert call(rot=65) == SHAPE
     assert call(D=600) == SHAPE
     assert call(mp=-1) == SCALAR
@@ -274,6 +278,7 @@ def qkv_cache(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(K=0), SHAPE), (dict(Q=-1), SHAPE), (dict(head_dim=600), SHAPE),
+    (dict(Q=2**31 - 1, K=2**30), SHAPE),
     (dict(dtype=7), DTYPE), (dict(flags=8), ENUM), (dict(n_slots=-1), SCALAR),
     (dict(slot=None), NULLP), (dict(kc=None), NULLP), (dict(vc=None), NULLP),
     (dict(qkv=None), NULLP), (dict(q_out=None), NULLP),
