@@ -129,6 +129,87 @@ def _same_dtype(ref, *tensors):
             raise TypeError(f"dtype mismatch: {t.dtype} vs {ref.dtype}")
 
 
+# The C ABI takes sizes on trust; these checks make every tensor handed over
+# at least as large as the sizes passed with it, so a mismatch is an error
+# here rather than an out-of-bounds access on the GPU.
+def _shape(t, shape, name):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _numel(t, n, name):
+    if t is not None and t.numel() != n:
+        raise ValueError(f"{name} must hold {n} elements, got {t.numel()}")
+
+
+def _codes(t, shape, name):
+    if t is not None:
+        _shape(t, shape, name)
+        if t.dtype != torch.uint8:
+            raise TypeError(f"{name} must be uint8 (e4m3fn codes)")
+
+
+def _amax_out(t):
+    if t is not None and (t.dtype != torch.float32 or t.numel() < 1):
+        raise TypeError("amax must be a float32 tensor of at least one element")
+
+
+def _rows(x, name="x"):
+    """(T, H) of a tensor of rows, H its last dimension."""
+    if x.dim() < 1 or x.shape[-1] < 1:
+        raise ValueError(f"{name} needs a non-empty last dimension")
+    return x.numel() // x.shape[-1], x.shape[-1]
+
+
+def _norm_args(x, residual, w):
+    T, H = _rows(x)
+    _shape(residual, x.shape, "residual")
+    _numel(w, H, "w")
+    return T, H
+
+
+def _ada_args(x, residual, gate, scale, shift):
+    T, H = _rows(x)
+    _shape(residual, x.shape, "residual")
+    for t, n in ((gate, "gate"), (scale, "scale"), (shift, "shift")):
+        _numel(t, H, n)
+    return T, H
+
+
+def _act_rows(gate_up):
+    """(T, d) of gate_up [..., 2d]."""
+    if gate_up.dim() < 1 or gate_up.shape[-1] < 2 or gate_up.shape[-1] % 2:
+        raise ValueError("gate_up must end in an even dimension 2d >= 2")
+    return gate_up.numel() // gate_up.shape[-1], gate_up.shape[-1] // 2
+
+
+def _heads3(t, name):
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [T, heads, head_dim]")
+    return t.shape
+
+
+def _rope_tables(cos_sin, pos, T, rot_dim, max_pos):
+    """pos int64 [T]; cos_sin float32 [rows, rot_dim] (cos | sin).  Returns
+    the max_pos to pass: the rows of the cache unless a smaller one is given."""
+    if pos.dtype != torch.int64:
+        raise TypeError("pos must be int64")
+    _numel(pos, T, "pos")
+    if cos_sin is None:
+        if max_pos:
+            raise ValueError("cos_sin is required when max_pos > 0")
+        return 0
+    if cos_sin.dtype != torch.float32:
+        raise TypeError("cos_sin must be float32")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != rot_dim:
+        raise ValueError(f"cos_sin must be [max_pos, rot_dim={rot_dim}], got "
+                         f"{tuple(cos_sin.shape)}")
+    mp = cos_sin.shape[0] if max_pos is None else int(max_pos)
+    if not 0 <= mp <= cos_sin.shape[0]:
+        raise ValueError(f"max_pos {mp} must lie in [0, {cos_sin.shape[0]}] (rows of cos_sin)")
+    return mp
+
+
 def qknorm_rope(q, k, w_q, w_k, cos_sin, pos, rot_dim, eps=1e-6, weight_offset=0,
                 layout=ROTATE_HALF, q_out=None, k_out=None, max_pos=None, stream=None):
     """q [T, Q, D], k [T, K, D] -> (q_out, k_out) of the same shapes.
@@ -136,15 +217,18 @@ def qknorm_rope(q, k, w_q, w_k, cos_sin, pos, rot_dim, eps=1e-6, weight_offset=0
     [max_pos, rot_dim] (cos | sin), pos int64 [T]."""
     _dev(q, k, w_q, w_k, cos_sin, pos, q_out, k_out)
     _same_dtype(q, k, w_q, w_k, q_out, k_out)
-    if pos.dtype != torch.int64 or (cos_sin is not None and cos_sin.dtype != torch.float32):
-        raise TypeError("pos must be int64 and cos_sin float32")
-    T, Q, D = q.shape
-    K = k.shape[1]
+    T, Q, D = _heads3(q, "q")
+    K = _heads3(k, "k")[1]
+    _shape(k, (T, K, D), "k")
+    _shape(q_out, q.shape, "q_out")
+    _shape(k_out, k.shape, "k_out")
+    _numel(w_q if Q else None, D, "w_q")
+    _numel(w_k if K else None, D, "w_k")
+    mp = _rope_tables(cos_sin, pos, T, rot_dim, max_pos)
     if q_out is None:
         q_out = torch.empty_like(q)
     if k_out is None:
         k_out = torch.empty_like(k)
-    mp = (cos_sin.shape[0] if cos_sin is not None else 0) if max_pos is None else max_pos
     _check(_lib.mbt_qknorm_rope(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(w_q),
                                 _ptr(w_k), _ptr(cos_sin), mp, _ptr(pos), Q, K, T, D, rot_dim,
                                 eps, weight_offset, layout, _dtype(q), _stream(stream)))
@@ -174,17 +258,20 @@ def qknorm_rope_ex(q_in, k_in, w_q, w_k, cos_sin, pos, rot_dim, eps=1e-6, weight
         if t is not None and not t.is_contiguous():
             raise ValueError("weights, cos_sin and pos must be contiguous")
     _same_dtype(q_in, k_in, w_q, w_k, q_out, k_out)
-    if pos.dtype != torch.int64 or (cos_sin is not None and cos_sin.dtype != torch.float32):
-        raise TypeError("pos must be int64 and cos_sin float32")
-    T, Q, D = q_in.shape
-    K = k_in.shape[1]
+    T, Q, D = _heads3(q_in, "q_in")
+    K = _heads3(k_in, "k_in")[1]
+    _shape(k_in, (T, K, D), "k_in")
+    _shape(q_out, (T, Q, D), "q_out")
+    _shape(k_out, (T, K, D), "k_out")
+    _numel(w_q if Q else None, D, "w_q")
+    _numel(w_k if K else None, D, "w_k")
+    mp = _rope_tables(cos_sin, pos, T, rot_dim, max_pos)
     if q_out is None:
         q_out = torch.empty((T, Q, D), dtype=q_in.dtype, device=q_in.device)
     if k_out is None:
         k_out = torch.empty((T, K, D), dtype=k_in.dtype, device=k_in.device)
     st = [_token_stride(t, n) for t, n in ((q_in, "q_in"), (k_in, "k_in"), (q_out, "q_out"),
                                            (k_out, "k_out"))]
-    mp = (cos_sin.shape[0] if cos_sin is not None else 0) if max_pos is None else max_pos
     _check(_lib.mbt_qknorm_rope_ex(_ptr(q_in), _ptr(k_in), _ptr(q_out), _ptr(k_out), _ptr(w_q),
                                    _ptr(w_k), _ptr(cos_sin), mp, _ptr(pos), Q, K, T, D, rot_dim,
                                    eps, weight_offset, layout, _dtype(q_in), *st,
@@ -200,17 +287,22 @@ def qkv_norm_rope_cache(qkv, w_q, w_k, cos_sin, pos, slot, k_cache, v_cache, Q, 
     k_cache / v_cache [n_slots, K, D] (slots outside [0, n_slots): no write)."""
     _dev(qkv, w_q, w_k, cos_sin, pos, slot, k_cache, v_cache, q_out)
     _same_dtype(qkv, w_q, w_k, k_cache, v_cache, q_out)
-    if pos.dtype != torch.int64 or slot.dtype != torch.int64:
-        raise TypeError("pos and slot must be int64")
-    T, QKV, D = qkv.shape
+    if slot.dtype != torch.int64:
+        raise TypeError("slot must be int64")
+    T, QKV, D = _heads3(qkv, "qkv")
     K = (QKV - Q) // 2
     if K < 1 or Q + 2 * K != QKV:
         raise ValueError("qkv must be [T, Q + 2K, head_dim] with K >= 1")
-    if k_cache.shape[1:] != (K, D) or v_cache.shape != k_cache.shape:
+    if k_cache.dim() != 3 or tuple(k_cache.shape[1:]) != (K, D) or \
+            v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache must be [n_slots, K, head_dim]")
+    _numel(slot, T, "slot")
+    _shape(q_out, (T, Q, D), "q_out")
+    _numel(w_q if Q else None, D, "w_q")
+    _numel(w_k, D, "w_k")
+    mp = _rope_tables(cos_sin, pos, T, rot_dim, max_pos)
     if q_out is None:
         q_out = torch.empty((T, Q, D), dtype=qkv.dtype, device=qkv.device)
-    mp = (cos_sin.shape[0] if cos_sin is not None else 0) if max_pos is None else max_pos
     _check(_lib.mbt_qkv_norm_rope_cache(_ptr(qkv), _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
                                         _ptr(slot), k_cache.shape[0], _ptr(w_q), _ptr(w_k),
                                         _ptr(cos_sin), mp, _ptr(pos), Q, K, T, D, rot_dim, eps,
@@ -224,11 +316,10 @@ def rope(q, k, cos_sin, pos, rot_dim, layout=ROTATE_HALF, max_pos=None, stream=N
     k [T, K, D] by cos_sin[pos[t]]; tokens outside the cache are untouched."""
     _dev(q, k, cos_sin, pos)
     _same_dtype(q, k)
-    if pos.dtype != torch.int64 or (cos_sin is not None and cos_sin.dtype != torch.float32):
-        raise TypeError("pos must be int64 and cos_sin float32")
-    T, Q, D = q.shape
-    K = k.shape[1]
-    mp = (cos_sin.shape[0] if cos_sin is not None else 0) if max_pos is None else max_pos
+    T, Q, D = _heads3(q, "q")
+    K = _heads3(k, "k")[1]
+    _shape(k, (T, K, D), "k")
+    mp = _rope_tables(cos_sin, pos, T, rot_dim, max_pos)
     _check(_lib.mbt_rope(_ptr(q), _ptr(k), _ptr(cos_sin), mp, _ptr(pos), Q, K, T, D, rot_dim,
                          layout, _dtype(q), _stream(stream)))
     return q, k
@@ -238,8 +329,8 @@ def fused_add_rmsnorm(x, residual, w, eps=1e-6, weight_offset=0, stream=None):
     """In place: residual <- R(x + residual); x <- RMSNorm of it.  x [T, H]."""
     _dev(x, residual, w)
     _same_dtype(x, residual, w)
-    H = x.shape[-1]
-    _check(_lib.mbt_fused_add_rmsnorm(_ptr(x), _ptr(residual), _ptr(w), x.numel() // H, H, eps,
+    T, H = _norm_args(x, residual, w)
+    _check(_lib.mbt_fused_add_rmsnorm(_ptr(x), _ptr(residual), _ptr(w), T, H, eps,
                                       weight_offset, _dtype(x), _stream(stream)))
     return x
 
@@ -249,11 +340,12 @@ def fused_add_rmsnorm_fp8(x, residual, w, inv_scale, eps=1e-6, weight_offset=0, 
     """residual <- R(x + residual); returns y = e4m3fn codes (uint8 [T, H])."""
     _dev(x, residual, w, y)
     _same_dtype(x, residual, w)
-    H = x.shape[-1]
+    T, H = _norm_args(x, residual, w)
+    _codes(y, x.shape, "y")
     if y is None:
         y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _check(_lib.mbt_fused_add_rmsnorm_fp8(_ptr(x), _ptr(residual), _ptr(w), _ptr(y),
-                                          float(inv_scale), x.numel() // H, H, eps,
+                                          float(inv_scale), T, H, eps,
                                           weight_offset, _dtype(x), _stream(stream)))
     return y
 
@@ -264,11 +356,12 @@ def fused_add_rmsnorm_amax(x, residual, w, eps=1e-6, weight_offset=0, amax=None,
     max(amax_in, max |normalised value|).  A new `amax` starts at 0."""
     _dev(x, residual, w, amax)
     _same_dtype(x, residual, w)
-    H = x.shape[-1]
+    T, H = _norm_args(x, residual, w)
+    _amax_out(amax)
     if amax is None:
         amax = torch.zeros(1, dtype=torch.float32, device=x.device)
     _check(_lib.mbt_fused_add_rmsnorm_amax(_ptr(x), _ptr(residual), _ptr(w), _ptr(amax),
-                                           x.numel() // H, H, eps, weight_offset, _dtype(x),
+                                           T, H, eps, weight_offset, _dtype(x),
                                            _stream(stream)))
     return amax
 
@@ -279,9 +372,9 @@ def adarms(x, residual, gate, scale, shift, eps=1e-6, stream=None):
     gate [H]."""
     _dev(x, residual, gate, scale, shift)
     _same_dtype(x, residual, gate, scale, shift)
-    H = x.shape[-1]
+    T, H = _ada_args(x, residual, gate, scale, shift)
     _check(_lib.mbt_adarms(_ptr(x), _ptr(residual), _ptr(gate), _ptr(scale), _ptr(shift),
-                           x.numel() // H, H, eps, _dtype(x), _stream(stream)))
+                           T, H, eps, _dtype(x), _stream(stream)))
     return x
 
 
@@ -290,11 +383,12 @@ def adarms_fp8(x, residual, gate, scale, shift, inv_scale, eps=1e-6, y=None, str
     [T, H]) of (RMSNorm(s) * (1 + scale) + shift) * inv_scale."""
     _dev(x, residual, gate, scale, shift, y)
     _same_dtype(x, residual, gate, scale, shift)
-    H = x.shape[-1]
+    T, H = _ada_args(x, residual, gate, scale, shift)
+    _codes(y, x.shape, "y")
     if y is None:
         y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _check(_lib.mbt_adarms_fp8(_ptr(x), _ptr(residual), _ptr(gate), _ptr(scale), _ptr(shift),
-                               _ptr(y), float(inv_scale), x.numel() // H, H, eps, _dtype(x),
+                               _ptr(y), float(inv_scale), T, H, eps, _dtype(x),
                                _stream(stream)))
     return y
 
@@ -302,11 +396,12 @@ def adarms_fp8(x, residual, gate, scale, shift, inv_scale, eps=1e-6, y=None, str
 def adarms_amax(x, residual, gate, scale, shift, eps=1e-6, amax=None, stream=None):
     _dev(x, residual, gate, scale, shift, amax)
     _same_dtype(x, residual, gate, scale, shift)
-    H = x.shape[-1]
+    T, H = _ada_args(x, residual, gate, scale, shift)
+    _amax_out(amax)
     if amax is None:
         amax = torch.zeros(1, dtype=torch.float32, device=x.device)
     _check(_lib.mbt_adarms_amax(_ptr(x), _ptr(residual), _ptr(gate), _ptr(scale), _ptr(shift),
-                                _ptr(amax), x.numel() // H, H, eps, _dtype(x), _stream(stream)))
+                                _ptr(amax), T, H, eps, _dtype(x), _stream(stream)))
     return amax
 
 
@@ -314,33 +409,35 @@ def gated_act(gate_up, act=SILU, out=None, stream=None):
     """gate_up [T, 2d] = [g | u] -> out [T, d] = R(act(g) * u)."""
     _dev(gate_up, out)
     _same_dtype(gate_up, out)
-    d = gate_up.shape[-1] // 2
+    T, d = _act_rows(gate_up)
+    _shape(out, gate_up.shape[:-1] + (d,), "out")
     if out is None:
         out = torch.empty(gate_up.shape[:-1] + (d,), dtype=gate_up.dtype, device=gate_up.device)
-    _check(_lib.mbt_gated_act(_ptr(gate_up), _ptr(out), gate_up.numel() // (2 * d), d, act,
-                              _dtype(gate_up), _stream(stream)))
+    _check(_lib.mbt_gated_act(_ptr(gate_up), _ptr(out), T, d, act, _dtype(gate_up),
+                              _stream(stream)))
     return out
 
 
 def gated_act_fp8(gate_up, inv_scale, act=SILU, out=None, stream=None):
     """gate_up [T, 2d] -> e4m3fn codes (uint8 [T, d]) of act(g) * u * inv_scale."""
     _dev(gate_up, out)
-    d = gate_up.shape[-1] // 2
+    T, d = _act_rows(gate_up)
+    _codes(out, gate_up.shape[:-1] + (d,), "out")
     if out is None:
         out = torch.empty(gate_up.shape[:-1] + (d,), dtype=torch.uint8, device=gate_up.device)
-    _check(_lib.mbt_gated_act_fp8(_ptr(gate_up), _ptr(out), float(inv_scale),
-                                  gate_up.numel() // (2 * d), d, act, _dtype(gate_up),
-                                  _stream(stream)))
+    _check(_lib.mbt_gated_act_fp8(_ptr(gate_up), _ptr(out), float(inv_scale), T, d, act,
+                                  _dtype(gate_up), _stream(stream)))
     return out
 
 
 def gated_act_amax(gate_up, act=SILU, amax=None, stream=None):
     _dev(gate_up, amax)
-    d = gate_up.shape[-1] // 2
+    T, d = _act_rows(gate_up)
+    _amax_out(amax)
     if amax is None:
         amax = torch.zeros(1, dtype=torch.float32, device=gate_up.device)
-    _check(_lib.mbt_gated_act_amax(_ptr(gate_up), _ptr(amax), gate_up.numel() // (2 * d), d,
-                                   act, _dtype(gate_up), _stream(stream)))
+    _check(_lib.mbt_gated_act_amax(_ptr(gate_up), _ptr(amax), T, d, act, _dtype(gate_up),
+                                   _stream(stream)))
     return amax
 
 
@@ -349,6 +446,7 @@ def quantize_fp8(x, inv_scale, y=None, stream=None):
     _dev(x, y)
     if x.dtype != torch.float32:
         raise TypeError("quantize_fp8 takes float32 input")
+    _codes(y, x.shape, "y")
     if y is None:
         y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _check(_lib.mbt_quantize_fp8(_ptr(x), _ptr(y), x.numel(), float(inv_scale),
