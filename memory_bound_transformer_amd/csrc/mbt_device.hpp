@@ -49,6 +49,19 @@ __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
 __device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
+// Raw buffer resource over [base, base + bytes): the hardware drops stores
+// at offsets outside it (the buffer range check), so lanes past the end of
+// a partial wave need no branch.  Word 3 is the gfx9-family format word
+// (32-bit data).  base and bytes must be wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+// 16-byte store through a buffer resource with the nontemporal policy (the
+// cache-policy operand's nt bit, kept by every IR pass, unlike the
+// nontemporal metadata of a plain store).
+__device__ __forceinline__ void buf_st16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 2);
+}
 __device__ __forceinline__ void st8_nt(void* p, u32x2 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
 }

@@ -123,14 +123,39 @@ __device__ __forceinline__ void partner_f32(const float* n, float* nb, int hv, b
 // Vec<DT> and a 16-byte aligned cos/sin cache (interleaved reads its run
 // element-wise).  Waves cover the query rows, then the key rows; with v_in
 // a key wave also copies the value heads of its rows, unchanged, to their slot.
-template <int DT, int G, int C, int LAYOUT, bool GEN>
+//
+// Load order.  The longest dependent chain is position -> cos/sin row, so
+// the position goes out first, then the weights, then the row's chunks, and
+// the cos/sin loads follow as soon as the position is in, while the chunks
+// are still in flight.  No load sits behind a lane-dependent branch (lanes
+// past the last row read that row again and store nothing; lanes outside
+// the rotated span read the first cos/sin pairs and ignore them), so each
+// wait the compiler places covers only the loads the next step needs.
+// Measured on MI355X, cold, (Q, K) = (24, 4), D = 256, rot_dim 64: with the
+// cos/sin loads behind a wait on the row, the gather cost 0.27 us of 3.54 us
+// at T = 256.
+//
+// THR (C >= 2 only): the order for a launch whose waves fill most of the
+// chip in one resident round.  Every wave of a block first waits for all of
+// its loads (the block's weight staging is issued last and ends in a block
+// barrier), and the cos/sin loads go out after the reduction.  There the
+// early order above measured slower -- (Q, K) = (24, 4), T = 2048: 11.7 us
+// against 10.2 us -- while below about ten waves per CU, and again once the
+// grid needs several rounds, it is the faster one (T = 512: 4.1 against
+// 4.5 us).  The host picks THR from the wave count.
+template <int DT, int G, int C, int LAYOUT, bool GEN, bool THR>
 __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g) {
+    static_assert(!THR || C >= 2, "THR stages weights in LDS: C >= 2");
     constexpr int V = Vec<DT>::n;
     constexpr int RPW = kWave / G;     // rows per wave
     constexpr int EB = EltBytes<DT>::n;
-    // C >= 2: the fp32 (w + delta) vectors live in LDS, not in 2 * C * V
-    // registers per lane, which keeps these kernels at 8 waves per SIMD.
-    __shared__ float wsh[C >= 2 ? 2 : 1][C >= 2 ? 512 : 1];
+    constexpr int L = G * C;           // 16-byte chunks per row
+    // C >= 2: the fp32 (w + delta) rows live in LDS rather than in C * V
+    // registers per lane: one row per wave (its own tensor's; each wave
+    // writes and reads only its own row, so no barrier), or with THR the
+    // q and k rows once per block, behind a block barrier.
+    constexpr int WROWS = C >= 2 ? (THR ? 2 : 4) : 1;
+    __shared__ float wsh[WROWS][C >= 2 ? L * V : 1];
 
     // Blocks keep their dispatch order, which deals them round-robin over
     // the 8 XCDs.  Renumbering them so that each XCD takes a contiguous range
@@ -139,11 +164,15 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     // range put those on one XCD, whose share of the fabric then bounded the
     // launch (15.2 us against 11.9 us, (Q, K) = (24, 4), T = 2048).
     const uint32_t wv = (uint32_t)uniform((int)(blockIdx.x * 4u + (threadIdx.x >> 6)));
+    // spare waves of the last block leave at once, or with THR after the
+    // block barrier (issuing no load of their own)
     const bool wave_live = wv < p.total_waves;
+    if constexpr (!THR)
+        if (!wave_live) return;
     const bool is_q = wv < p.q_waves;                       // wave-uniform tensor
     const int heads = is_q ? p.Q : p.K;
     const float inv_heads = is_q ? p.inv_Q : p.inv_K;
-    const int64_t nrows = wave_live ? p.T * heads : 0;
+    const int64_t nrows = p.T * heads;                      // >= 1 for a live wave
     const int64_t row0 = (int64_t)(is_q ? wv : wv - p.q_waves) * RPW;
     const char* src = (const char*)(is_q ? p.q_in : p.k_in);
     char* dst = (char*)(is_q ? p.q_out : p.k_out);
@@ -153,114 +182,157 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     const int j = lane % G;                                 // lane within the row
     const int64_t row = row0 + lane / G;
     const bool live = row < nrows;
+    const int64_t rowc = live ? row : nrows - 1;            // a row every lane may read
     const int half = p.rot >> 1;
     const int hv = half / V;                                // rotate-half: chunks per half
     const bool is_a = LAYOUT == 0 && j < hv;
     const bool is_b = LAYOUT == 0 && j >= hv && j < 2 * hv;
 
-    // ---- issue every independent load before any arithmetic ----
-    // The row's token t and head h come from a float reciprocal and one
-    // correction.  Dense rows are addressed as row * D, so their loads go out
-    // first and t is formed while they fly; strided and slotted rows need t
-    // and h for the address itself.
-    const uint32_t r32 = live ? (uint32_t)row : 0u;
-    int32_t t = 0;
-    int64_t out_off = row * p.D, orow = 0;
-    u32x4 x[C];
-    // GEN with value rows: a key wave also carries the value heads of its
-    // rows (adjacent to the key heads in a fused QKV buffer), loaded beside
-    // the keys and stored to the same slot before any arithmetic.
+    // The row's token t and head h: a float reciprocal and one correction.
+    const uint32_t r32 = (uint32_t)rowc;
+    int32_t t = (int32_t)((float)r32 * inv_heads);
+    int32_t h = (int32_t)r32 - t * heads;
+    if (h >= heads) { t += 1; h -= heads; }
+    if (h < 0) { t -= 1; h += heads; }
+
+    // ---- loads ----
+    // Order: position, weights, the row's chunks; then, once the position
+    // is in, the cos/sin row.  GEN puts its loads behind wave-uniform
+    // branches (value rows, slot) first: vmcnt retires loads in issue order,
+    // and a conditional load issued after the position would leave the
+    // compiler a conservative wait there.  A key wave that carries value
+    // rows therefore issues its cos/sin loads when those rows are in (as
+    // early as a wait on its own chunks would allow), and stores them at
+    // once, so they are not held in registers through the arithmetic.
     u32x4 vx[GEN ? C : 1];
-    int64_t v_off = 0;
-    bool carry_v = false;
-    if constexpr (GEN) carry_v = !is_q && g.v_in != nullptr;
-    if constexpr (!GEN) {
-        const char* rsrc = src + row * (int64_t)p.D * EB;
-#pragma unroll
-        for (int k = 0; k < C; ++k)
-            x[k] = live ? ld16_nt(rsrc + (k * G + j) * 16) : u32x4{0u, 0u, 0u, 0u};
-        t = (int32_t)((float)r32 * inv_heads);
-        const int32_t rem = (int32_t)r32 - t * heads;
-        t += (rem >= heads) ? 1 : 0;
-        t -= (rem < 0) ? 1 : 0;
-        orow = live ? t : -1;
-    } else {
-        t = (int32_t)((float)r32 * inv_heads);
-        int32_t h = (int32_t)r32 - t * heads;
-        if (h >= heads) { t += 1; h -= heads; }
-        if (h < 0) { t -= 1; h += heads; }
-        const int64_t in_st = is_q ? g.q_in_st : g.k_in_st;
-        const int64_t out_st = is_q ? g.q_out_st : g.k_out_st;
-        const char* rsrc = src + ((int64_t)t * in_st + (int64_t)h * p.D) * EB;
-#pragma unroll
-        for (int k = 0; k < C; ++k)
-            x[k] = live ? ld16_nt(rsrc + (k * G + j) * 16) : u32x4{0u, 0u, 0u, 0u};
+    u32x4 x[C];
+    u32x4 wraw{0u, 0u, 0u, 0u};
+    int64_t ppos = -1;
+    bool carry_v = false, slotted = false;
+    int64_t slot_raw = t;                                   // key / value output row (raw)
+    // The position-independent parts of the cos/sin addresses, formed
+    // before any load.  Without a table (rot_dim 0 or an empty cache) every
+    // lane reads the first V floats of the weight row (at least 64 bytes)
+    // instead, and nothing uses them.
+    const bool table = p.rot > 0 && p.max_pos > 0;          // wave-uniform
+    const float* cs_base = table ? p.cos_sin : (const float*)wp;
+    const int hoff = table ? half : 0;                      // sin half of the row
+    const int cs_j0 = LAYOUT == 0 ? (table ? (is_a ? j : (is_b ? j - hv : 0)) * V : 0)
+                                  : j * (V / 2);            // first pair index
+    auto issue_loads = [&]() {
+    if constexpr (GEN) {
+        // value rows: a key wave also carries the value heads of its rows
+        // (adjacent to the key heads in a fused QKV buffer)
+        carry_v = !is_q && g.v_in != nullptr;               // wave-uniform
         if (carry_v) {
             const char* vsrc =
                 (const char*)g.v_in + ((int64_t)t * g.v_in_st + (int64_t)h * p.D) * EB;
 #pragma unroll
-            for (int k = 0; k < C; ++k)
-                vx[k] = live ? ld16_nt(vsrc + (k * G + j) * 16) : u32x4{0u, 0u, 0u, 0u};
+            for (int k = 0; k < C; ++k) vx[k] = ld16_nt(vsrc + (k * G + j) * 16);
         }
-        orow = live ? out_row(g, !is_q && g.slot != nullptr, t) : -1;
-        out_off = (orow >= 0 ? orow : 0) * out_st + (int64_t)h * p.D;
-        v_off = (orow >= 0 ? orow : 0) * g.v_out_st + (int64_t)h * p.D;
+        slotted = !is_q && g.slot != nullptr;               // wave-uniform
+        if (slotted) slot_raw = g.slot[t];
     }
-    const int64_t ppos = live ? p.pos[t] : -1;
-    float wreg[C >= 2 ? 1 : V];
-    if constexpr (C >= 2) {
+    // the head of the longest chain: position -> cos/sin row
+    ppos = p.pos[t];
+    // weights: chunk (lane mod L) of the tensor's row -- for C = 1 that is
+    // the lane's own chunk, for C >= 2 the staging share of the LDS row
+    if constexpr (!THR) wraw = ld16(wp + (lane % L) * 16);
+    const char* xsrc;
+    if constexpr (GEN)
+        xsrc = src + ((int64_t)t * (is_q ? g.q_in_st : g.k_in_st) + (int64_t)h * p.D) * EB;
+    else
+        xsrc = src + rowc * (int64_t)p.D * EB;
+#pragma unroll
+    for (int k = 0; k < C; ++k) x[k] = ld16_nt(xsrc + (k * G + j) * 16);
+    };
+    if constexpr (THR) {
+        if (wave_live) issue_loads();
+    } else {
+        issue_loads();
+    }
+    // An empty asm that may touch memory: the loads above cannot be moved
+    // below it (to their first use), and it emits no instruction or wait.
+    // The sched_barrier keeps arithmetic on their results (the position
+    // test) from being hoisted above them.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // cos/sin of the position (raw bits; decoded where the rotation uses them)
+    const bool rotate = (ppos >= 0) && (ppos < p.max_pos) && (p.rot > 0);
+    constexpr int NCS = LAYOUT == 0 ? V / 4 : 1;
+    u32x4 cs_c4[NCS], cs_s4[NCS];
+    float cs_c[V / 2], cs_s[V / 2];                         // interleaved runs
+    bool lane_rot = false;
+    // (Not behind a branch, which the compiler would sink the loads into.)
+    auto load_cs = [&]() {
+        const float* crow = cs_base + (rotate ? ppos : 0) * (int64_t)p.rot;
+        if constexpr (LAYOUT == 0) {
+            lane_rot = rotate && (is_a || is_b);
+            const int j0 = cs_j0;
+#pragma unroll
+            for (int i = 0; i < NCS; ++i) {
+                cs_c4[i] = ld16(crow + j0 + 4 * i);
+                cs_s4[i] = ld16(crow + hoff + j0 + 4 * i);
+            }
+        } else {
+            // V/2 pairs per lane; a run may cross rot/2, so pairs past it
+            // read pair 0 and keep c = 1, s = 0: exactly unrotated.
+            const int j0 = cs_j0;
+            lane_rot = rotate && (j0 < half);
+#pragma unroll
+            for (int i = 0; i < V / 2; ++i) {
+                const bool ok = (j0 + i) < half;
+                const int e = (table && ok) ? j0 + i : 0;
+                const float c = crow[e], s = crow[hoff + e];
+                cs_c[i] = ok ? c : 1.0f;
+                cs_s[i] = ok ? s : 0.0f;
+            }
+        }
+    };
+    if constexpr (!THR) {
+        // sched_barrier: no arithmetic on the row is hoisted above these loads
+        __builtin_amdgcn_sched_barrier(0);
+        load_cs();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);                  // all loads issued
+    }
+
+    // ---- C >= 2: stage (w + delta) in LDS ----
+    const float* wrow = nullptr;
+    if constexpr (C >= 2 && !THR) {                         // the wave's own row
+        const int wib = threadIdx.x >> 6;
+        if (lane < L) {
+            float wf[V];
+            unpack<DT>(wraw, wf);
+#pragma unroll
+            for (int i = 0; i < V; ++i) wsh[wib][lane * V + i] = wf[i] + p.delta;
+        }
+        __builtin_amdgcn_wave_barrier();
+        wrow = wsh[wib];
+    }
+    if constexpr (THR) {                                    // both rows, block-wide
         for (int i = threadIdx.x; i < p.D; i += 256) {
             wsh[0][i] = (p.Q > 0) ? ld_elt<DT>(p.w_q, i) + p.delta : 0.0f;
             wsh[1][i] = (p.K > 0) ? ld_elt<DT>(p.w_k, i) + p.delta : 0.0f;
         }
-        __syncthreads();                                   // x loads already in flight
-    } else {
-        unpack<DT>(wave_live ? ld16(wp + j * 16) : u32x4{0u, 0u, 0u, 0u}, wreg);
-#pragma unroll
-        for (int i = 0; i < V; ++i) wreg[i] += p.delta;
+        __syncthreads();                                    // after every load of the block
+        if (!wave_live) return;
+        wrow = wsh[is_q ? 0 : 1];
     }
-    if (!wave_live) return;
-    char* rdst = dst + out_off * EB;
+
+    // ---- output rows ----
+    int64_t orow = t;
+    if constexpr (GEN)
+        if (slotted) orow = (slot_raw >= 0 && slot_raw < g.n_slots) ? slot_raw : -1;
+    const bool keep = orow >= 0;
+    int64_t out_off = rowc * p.D;
+    if constexpr (GEN)
+        out_off = (keep ? orow : 0) * (is_q ? g.q_out_st : g.k_out_st) + (int64_t)h * p.D;
     if constexpr (GEN) {
-        if (carry_v && orow >= 0) {                        // value heads: copy to the slot
-            char* vdst = (char*)g.v_out + v_off * EB;
+        if (carry_v && keep) {                              // value heads: copy to the slot
+            char* vdst = (char*)g.v_out + (orow * g.v_out_st + (int64_t)h * p.D) * EB;
 #pragma unroll
             for (int k = 0; k < C; ++k) st16_nt(vdst + (k * G + j) * 16, vx[k]);
-        }
-    }
-    const bool rotate = (ppos >= 0) && (ppos < p.max_pos) && (p.rot > 0);
-    float cs_c[V], cs_s[V];
-    bool lane_rot = false;
-    if constexpr (LAYOUT == 0) {
-        lane_rot = rotate && (is_a || is_b);
-        if (lane_rot) {
-            const int j0 = (is_a ? j : j - hv) * V;         // first pair index
-            const float* crow = p.cos_sin + ppos * (int64_t)p.rot;
-#pragma unroll
-            for (int i = 0; i < V; i += 4) {
-                const u32x4 cv = ld16(crow + j0 + i);
-                const u32x4 sv = ld16(crow + half + j0 + i);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    cs_c[i + k] = __uint_as_float(cv[k]);
-                    // sign folded in: o = own * c + partner * s'
-                    cs_s[i + k] = is_a ? -__uint_as_float(sv[k]) : __uint_as_float(sv[k]);
-                }
-            }
-        }
-    } else {
-        const int j0 = j * (V / 2);                         // first pair index
-        lane_rot = rotate && (j0 < half);
-        if (lane_rot) {
-            const float* crow = p.cos_sin + ppos * (int64_t)p.rot;
-            // V/2 pairs per lane; a run may cross rot/2, so read against the
-            // bound (pairs past it keep c = 1, s = 0: exactly unrotated).
-#pragma unroll
-            for (int i = 0; i < V / 2; ++i) {
-                const bool ok = (j0 + i) < half;
-                cs_c[i] = ok ? crow[j0 + i] : 1.0f;
-                cs_s[i] = ok ? crow[half + j0 + i] : 0.0f;
-            }
         }
     }
 
@@ -277,10 +349,21 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     else if constexpr (C == 2) ss = part[0] + part[1];
     else ss = (part[0] + part[1]) + (part[2] + part[3]);
     const float inv = inv_rms(ss, p.inv_D, p.eps);
+    if constexpr (THR) load_cs();
 
     // ---- normalise, round, rotate (group 0 only), store ----
-    const bool keep = orow >= 0;
-    const float* wrow = wsh[(C >= 2 && !is_q) ? 1 : 0];
+    float wreg[C >= 2 ? 1 : V];
+    if constexpr (C == 1) {
+        unpack<DT>(wraw, wreg);
+#pragma unroll
+        for (int i = 0; i < V; ++i) wreg[i] += p.delta;
+    }
+    char* rdst = dst + out_off * EB;
+    // dense form: the wave's rows as one buffer (its rows below nrows)
+    const int64_t wrows = (nrows - row0 < RPW) ? nrows - row0 : RPW;
+    const __amdgpu_buffer_rsrc_t wdst =
+        buf_rsrc(dst + row0 * (int64_t)p.D * EB, (uint32_t)(wrows * p.D * EB));
+    const uint32_t rofs = (uint32_t)((lane / G) * p.D * EB);
 #pragma unroll
     for (int k = 0; k < C; ++k) {
         float f[V], n[V];
@@ -312,23 +395,34 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
                 } else {
                     unpack<DT>(rot_partner(out, hv, is_a), b);
                 }
-                if (lane_rot) {
 #pragma unroll
-                    for (int i = 0; i < V; ++i) o[i] = rot_mac(a[i], cs_c[i], b[i], cs_s[i]);
-                    out = pack<DT>(o);
+                for (int i = 0; i < V; ++i) {
+                    const float c = __uint_as_float(cs_c4[i / 4][i % 4]);
+                    const float s = __uint_as_float(cs_s4[i / 4][i % 4]);
+                    // o = own * c + partner * s', s' = -s for the first half
+                    o[i] = rot_mac(a[i], c, b[i], is_a ? -s : s);
                 }
             } else {
-                if (lane_rot) {
 #pragma unroll
-                    for (int i = 0; i < V / 2; ++i) {
-                        o[2 * i] = rot_mac(a[2 * i], cs_c[i], a[2 * i + 1], -cs_s[i]);
-                        o[2 * i + 1] = rot_mac(a[2 * i + 1], cs_c[i], a[2 * i], cs_s[i]);
-                    }
-                    out = pack<DT>(o);
+                for (int i = 0; i < V / 2; ++i) {
+                    o[2 * i] = rot_mac(a[2 * i], cs_c[i], a[2 * i + 1], -cs_s[i]);
+                    o[2 * i + 1] = rot_mac(a[2 * i + 1], cs_c[i], a[2 * i], cs_s[i]);
                 }
             }
+            // every lane computes the rotation (no branch, so the cos/sin
+            // loads stay where they were issued); lanes outside the rotated
+            // span, and tokens outside the cache, keep R(n)
+            const u32x4 ro = pack<DT>(o);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) out[d] = lane_rot ? ro[d] : out[d];
         }
-        if (keep) st16_nt(rdst + (k * G + j) * 16, out);
+        if constexpr (GEN) {
+            if (keep) st16_nt(rdst + (k * G + j) * 16, out);
+        } else {
+            // through the wave's buffer: lanes past the last row fall outside
+            // it and are dropped, with no branch for the code above to sink into
+            buf_st16_nt(wdst, rofs + (uint32_t)((k * G + j) * 16), out);
+        }
     }
 }
 
@@ -443,7 +537,24 @@ int tun_c_max() {
     return v;
 }
 
-template <int DT, int G, int C, int LAYOUT, bool GEN>
+// Waves of a launch with G lanes per row.
+int64_t vec_waves(const QkParams& p, int G) {
+    const int rpw = kWave / G;
+    return (p.T * p.Q + rpw - 1) / rpw + (p.T * p.K + rpw - 1) / rpw;
+}
+
+// THR between these wave counts (C >= 2): from about ten waves per CU up to
+// one full resident round of 256 CUs x 4 SIMDs x 8 waves.
+int tun_thr_lo() {
+    static const int v = env_int("MBT_QK_THR_WAVES_LO", 2560);
+    return v;
+}
+int tun_thr_hi() {
+    static const int v = env_int("MBT_QK_THR_WAVES_HI", 8192);
+    return v;
+}
+
+template <int DT, int G, int C, int LAYOUT, bool GEN, bool THR>
 hipError_t launch_vec(const QkParams& p0, const QkGen<true>& g0, hipStream_t s) {
     QkParams p = p0;
     constexpr int RPW = kWave / G;
@@ -455,22 +566,32 @@ hipError_t launch_vec(const QkParams& p0, const QkGen<true>& g0, hipStream_t s) 
     const uint32_t n_blocks = (p.total_waves + 3u) / 4u;
     QkGen<GEN> g{};
     if constexpr (GEN) g = g0;
-    hipLaunchKernelGGL((qknorm_rope_vec<DT, G, C, LAYOUT, GEN>), dim3(n_blocks), dim3(256), 0, s,
-                       p, g);
+    hipLaunchKernelGGL((qknorm_rope_vec<DT, G, C, LAYOUT, GEN, THR>), dim3(n_blocks), dim3(256),
+                       0, s, p, g);
     return hipGetLastError();
 }
 
 // (G, C) with G * C = L lanes-of-chunks per row; G a power of two >= 4.
 template <int DT, int LAYOUT, bool GEN>
 hipError_t launch_gc(const QkParams& p, const QkGen<true>& g, int L, int C, hipStream_t s) {
+    bool thr = false;
+    if (C >= 2) {
+        const int64_t w = vec_waves(p, L / C);
+        thr = w >= tun_thr_lo() && w <= tun_thr_hi();
+    }
+#define MBT_QK_CASE1(LL)                                                 \
+    if (L == LL && C == 1) return launch_vec<DT, LL, 1, LAYOUT, GEN, false>(p, g, s);
 #define MBT_QK_CASE(LL, CC)                                              \
-    if (L == LL && C == CC) return launch_vec<DT, LL / CC, CC, LAYOUT, GEN>(p, g, s);
-    MBT_QK_CASE(4, 1)
-    MBT_QK_CASE(8, 1) MBT_QK_CASE(8, 2)
-    MBT_QK_CASE(16, 1) MBT_QK_CASE(16, 2) MBT_QK_CASE(16, 4)
-    MBT_QK_CASE(32, 1) MBT_QK_CASE(32, 2) MBT_QK_CASE(32, 4)
-    MBT_QK_CASE(64, 1) MBT_QK_CASE(64, 2) MBT_QK_CASE(64, 4)
+    if (L == LL && C == CC)                                              \
+        return thr ? launch_vec<DT, LL / CC, CC, LAYOUT, GEN, true>(p, g, s) \
+                   : launch_vec<DT, LL / CC, CC, LAYOUT, GEN, false>(p, g, s);
+    MBT_QK_CASE1(4)
+    MBT_QK_CASE1(8) MBT_QK_CASE(8, 2)
+    MBT_QK_CASE1(16) MBT_QK_CASE(16, 2) MBT_QK_CASE(16, 4)
+    MBT_QK_CASE1(32) MBT_QK_CASE(32, 2) MBT_QK_CASE(32, 4)
+    MBT_QK_CASE1(64) MBT_QK_CASE(64, 2) MBT_QK_CASE(64, 4)
 #undef MBT_QK_CASE
+#undef MBT_QK_CASE1
     return hipErrorInvalidValue;
 }
 

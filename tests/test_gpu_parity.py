@@ -131,12 +131,49 @@ EDGE_PROLOGUE = [
           max_pos=4096, cell=32),
     _cell(name="c2_f16_d128_full", dtype=W.F16, D=128, rot=128, T=1024, Q=16, K=2,
           max_pos=4096, cell=33),
+    # the two load orders of the chunked kernels (chosen by wave count: the
+    # whole-block order between about 2560 and 8192 waves, the early
+    # cos/sin order outside), each with a ragged last block -- spare waves
+    # and a partly filled last wave -- and with interleaved pairs
+    _cell(name="c4_thr_ragged_T999", D=256, rot=64, T=999, Q=24, K=4, max_pos=4096,
+          positions="arange", cell=34),
+    _cell(name="c4_lat_ragged_T501", D=256, rot=64, T=501, Q=24, K=4, max_pos=4096,
+          positions="arange", cell=35),
+    _cell(name="c4_thr_inter32", D=256, rot=32, layout=W.INTERLEAVED, T=1024, Q=24, K=4,
+          max_pos=4096, cell=36),
+    _cell(name="c2_thr_rot96", D=256, rot=96, T=1024, Q=24, K=4, max_pos=4096, cell=37),
+    _cell(name="c4_thr_f16_rot0", dtype=W.F16, D=256, rot=0, T=1024, Q=24, K=4, cell=38),
 ]
 
 
 @pytest.mark.parametrize("cell", EDGE_PROLOGUE, ids=lambda c: c.name)
 def test_prologue_edges(mbt, orc, cell):
     check_prologue_cell(mbt, orc, cell)
+
+
+@pytest.mark.parametrize("T", [1024, 2048])
+def test_prologue_width_invariant(mbt, T):
+    """A prefill-width launch (chunked rows, whole-block load order) and the
+    same tokens in 16-token launches (one chunk per lane, early cos/sin
+    order) give identical bits: the reduction tree and the rounding do not
+    depend on the launch shape."""
+    cell = [c for c in W.config3_cells()
+            if c.dtype == W.BF16 and c.Q == 24 and c.T == T and c.layout == W.ROTATE_HALF][0]
+    i = cell.inputs()
+    dt = cell.dtype
+    q, k = dev(i["q"], dt), dev(i["k"], dt)
+    wq, wk = dev(i["w_q"], dt), dev(i["w_k"], dt)
+    cs = torch.from_numpy(i["cos_sin"]).to(DEV)
+    pos = torch.from_numpy(i["pos"]).to(DEV)
+    args = (cell.rot, cell.eps, cell.weight_offset, cell.layout)
+    qo, ko = mbt.qknorm_rope(q, k, wq, wk, cs, pos, *args)
+    qs, ks = torch.empty_like(q), torch.empty_like(k)
+    for t0 in range(0, T, 16):
+        mbt.qknorm_rope(q[t0:t0 + 16], k[t0:t0 + 16], wq, wk, cs, pos[t0:t0 + 16], *args,
+                        q_out=qs[t0:t0 + 16], k_out=ks[t0:t0 + 16])
+    torch.cuda.synchronize()
+    assert torch.equal(qo.view(torch.int16), qs.view(torch.int16))
+    assert torch.equal(ko.view(torch.int16), ks.view(torch.int16))
 
 
 @pytest.mark.parametrize("dtype", [W.BF16, W.F16, W.F32])
