@@ -163,16 +163,16 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     // waves carry value heads (twice a query wave's bytes): a contiguous
     // range put those on one XCD, whose share of the fabric then bounded the
     // launch (15.2 us against 11.9 us, (Q, K) = (24, 4), T = 2048).
-    const uint32_t wv = (uint32_t)uniform((int)(blockIdx.x * 4u + (threadIdx.x >> 6)));
-    // spare waves of the last block leave at once, or with THR after the
-    // block barrier (issuing no load of their own)
-    const bool wave_live = wv < p.total_waves;
-    if constexpr (!THR)
-        if (!wave_live) return;
+    // Spare waves of the last block do not leave early (an exit test first
+    // would put a round trip for that one argument ahead of all others):
+    // they read the last wave's rows and store nothing.
+    const uint32_t wv0 = (uint32_t)uniform((int)(blockIdx.x * 4u + (threadIdx.x >> 6)));
+    const bool spare = wv0 >= p.total_waves;
+    const uint32_t wv = spare ? p.total_waves - 1 : wv0;
     const bool is_q = wv < p.q_waves;                       // wave-uniform tensor
     const int heads = is_q ? p.Q : p.K;
     const float inv_heads = is_q ? p.inv_Q : p.inv_K;
-    const int64_t nrows = p.T * heads;                      // >= 1 for a live wave
+    const int64_t nrows = p.T * heads;                      // >= 1: the wave has a row
     const int64_t row0 = (int64_t)(is_q ? wv : wv - p.q_waves) * RPW;
     const char* src = (const char*)(is_q ? p.q_in : p.k_in);
     char* dst = (char*)(is_q ? p.q_out : p.k_out);
@@ -246,11 +246,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
 #pragma unroll
     for (int k = 0; k < C; ++k) x[k] = ld16_nt(xsrc + (k * G + j) * 16);
     };
-    if constexpr (THR) {
-        if (wave_live) issue_loads();
-    } else {
-        issue_loads();
-    }
+    issue_loads();
     // An empty asm that may touch memory: the loads above cannot be moved
     // below it (to their first use), and it emits no instruction or wait.
     // The sched_barrier keeps arithmetic on their results (the position
@@ -316,7 +312,6 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
             wsh[1][i] = (p.K > 0) ? ld_elt<DT>(p.w_k, i) + p.delta : 0.0f;
         }
         __syncthreads();                                    // after every load of the block
-        if (!wave_live) return;
         wrow = wsh[is_q ? 0 : 1];
     }
 
@@ -324,7 +319,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     int64_t orow = t;
     if constexpr (GEN)
         if (slotted) orow = (slot_raw >= 0 && slot_raw < g.n_slots) ? slot_raw : -1;
-    const bool keep = orow >= 0;
+    const bool keep = !spare && orow >= 0;
     int64_t out_off = rowc * p.D;
     if constexpr (GEN)
         out_off = (keep ? orow : 0) * (is_q ? g.q_out_st : g.k_out_st) + (int64_t)h * p.D;
@@ -359,8 +354,9 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
         for (int i = 0; i < V; ++i) wreg[i] += p.delta;
     }
     char* rdst = dst + out_off * EB;
-    // dense form: the wave's rows as one buffer (its rows below nrows)
-    const int64_t wrows = (nrows - row0 < RPW) ? nrows - row0 : RPW;
+    // dense form: the wave's rows as one buffer (its rows below nrows; none
+    // for a spare wave)
+    const int64_t wrows = spare ? 0 : (nrows - row0 < RPW) ? nrows - row0 : RPW;
     const __amdgpu_buffer_rsrc_t wdst =
         buf_rsrc(dst + row0 * (int64_t)p.D * EB, (uint32_t)(wrows * p.D * EB));
     const uint32_t rofs = (uint32_t)((lane / G) * p.D * EB);
