@@ -167,6 +167,16 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     // would put a round trip for that one argument ahead of all others):
     // they read the last wave's rows and store nothing.
     const uint32_t wv0 = (uint32_t)uniform((int)(blockIdx.x * 4u + (threadIdx.x >> 6)));
+    if constexpr (GEN) {
+        // Every argument is needed up front: an empty asm that takes them
+        // makes the compiler fetch them in one batch, not in further
+        // dependent rounds inside the branches below.
+        asm volatile("" ::"s"(g.v_in), "s"(g.v_in_st), "s"(g.slot), "s"(g.n_slots),
+                     "s"(g.v_out), "s"(g.v_out_st), "s"(g.q_in_st), "s"(g.k_in_st),
+                     "s"(g.q_out_st), "s"(g.k_out_st), "s"(g.once), "s"(p.q_in), "s"(p.k_in),
+                     "s"(p.q_out), "s"(p.k_out), "s"(p.w_q), "s"(p.w_k), "s"(p.pos),
+                     "s"(p.cos_sin));
+    }
     const bool spare = wv0 >= p.total_waves;
     const uint32_t wv = spare ? p.total_waves - 1 : wv0;
     const bool is_q = wv < p.q_waves;                       // wave-uniform tensor
