@@ -176,6 +176,24 @@ def test_prologue_width_invariant(mbt, T):
     assert torch.equal(ko.view(torch.int16), ks.view(torch.int16))
 
 
+RAGGED_IN_PLACE = [
+    # spare waves in the last block (they read the last wave's rows and store
+    # nothing) and partly filled last waves, written in place: one chunk per
+    # lane, and both orders of the chunked kernel
+    _cell(name="ip_c1_T1", D=256, rot=64, T=1, Q=16, K=2, max_pos=4096, cell=40),
+    _cell(name="ip_c1_T7_q5k3", D=256, rot=64, T=7, Q=5, K=3, max_pos=4096, cell=41),
+    _cell(name="ip_c4_lat_T501", D=256, rot=64, T=501, Q=24, K=4, max_pos=4096,
+          positions="arange", cell=42),
+    _cell(name="ip_c4_thr_T999", D=256, rot=64, T=999, Q=24, K=4, max_pos=4096,
+          positions="arange", cell=43),
+]
+
+
+@pytest.mark.parametrize("cell", RAGGED_IN_PLACE, ids=lambda c: c.name)
+def test_prologue_in_place_ragged(mbt, orc, cell):
+    check_prologue_cell(mbt, orc, cell, in_place=True)
+
+
 @pytest.mark.parametrize("dtype", [W.BF16, W.F16, W.F32])
 def test_prologue_in_place_and_unaligned(mbt, orc, dtype):
     cell = _cell(name=f"inplace_{dtype}", dtype=dtype, cell=20 + dtype)
