@@ -489,6 +489,50 @@ def cpu_baseline(W, st, seconds):
                       f"host CPU: {model}, {len(os.sched_getaffinity(0))} cores visible"}
 
 
+def cpu_baseline_threads(W, st, seconds):
+    """The same oracle calls, as they stand, from several host threads at
+    once, each thread on its own contiguous slice of the step's tokens (the
+    token-parallel CPU structure of "thox-edge-ops v2", section 5.3; ctypes
+    releases the interpreter lock inside the C oracle)."""
+    import concurrent.futures as cf
+    import oracle
+    orc = oracle.default()
+    pi, ni, ai = st.pro.inputs(), st.norm.inputs(), st.act.inputs()
+    p = st.pro
+    nc, ac = st.norm.calibration_inputs(), st.act.calibration_inputs()
+    inv_n = W.fp8_inv_scale(orc.fused_add_rmsnorm_amax(nc["x"], nc["residual"], ni["w"], 1e-6,
+                                                       0, W.BF16))
+    inv_a = W.fp8_inv_scale(orc.gated_act_amax(ac["gate_up"], W.SILU, W.BF16))
+    n_thr = max(1, min(len(os.sched_getaffinity(0)), st.T, 16))
+    bounds = [(i * st.T // n_thr, (i + 1) * st.T // n_thr) for i in range(n_thr)]
+
+    def work(b):
+        a, e = b
+        orc.fused_add_rmsnorm_fp8(ni["x"][a:e], ni["residual"][a:e], ni["w"], inv_n, 1e-6, 0,
+                                  W.BF16)
+        orc.qknorm_rope(pi["q"][a:e], pi["k"][a:e], pi["w_q"], pi["w_k"], pi["cos_sin"],
+                        pi["pos"][a:e], p.rot, p.eps, p.weight_offset, p.layout, W.BF16)
+        orc.fused_add_rmsnorm_fp8(ni["x"][a:e], ni["residual"][a:e], ni["w"], inv_n, 1e-6, 0,
+                                  W.BF16)
+        orc.gated_act_fp8(ai["gate_up"][a:e], inv_a, W.SILU, W.BF16)
+
+    n = 0
+    with cf.ThreadPoolExecutor(n_thr) as ex:
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(work, bounds))
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds and n >= 2:
+                break
+    lo, hi = st.T // n_thr, -(-st.T // n_thr)
+    per = f"{lo}" if lo == hi else f"{lo}-{hi}"
+    return {"value": round(n * st.T / el, 1), "unit": "tokens/s", "cores": n_thr,
+            "kind": "oracle",
+            "sample": f"{n} full steps of T={st.T} tokens ({el:.1f} s wall), {n_thr} threads, "
+                      f"each on {per} tokens of every step"}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -659,6 +703,7 @@ def main():
     }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(W, st, args.cpu_seconds)
+        out["cpu_baseline_threads"] = cpu_baseline_threads(W, st, min(args.cpu_seconds, 5.0))
     print(json.dumps(out), flush=True)
 
 
