@@ -56,6 +56,10 @@ __device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
 }
+// 16-byte store through a buffer resource (default cache policy).
+__device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
 // 16-byte store through a buffer resource with the nontemporal policy (the
 // cache-policy operand's nt bit, kept by every IR pass, unlike the
 // nontemporal metadata of a plain store).

@@ -41,65 +41,96 @@ __device__ __forceinline__ int32_t token_of(uint32_t r, int heads, float inv_hea
 }
 
 // G lanes per row cover the rotated chunks (rotate-half: 2 * hv of them,
-// hv = rot/2 / Vec; interleaved: ceil(rot / Vec)).
+// hv = rot/2 / Vec; interleaved: ceil(rot / Vec)).  The host launches only
+// when a cache exists (rot_dim > 0 and max_pos > 0).
+//
+// Load order as in the fused prologue: the position first, the row's chunk
+// beside it, the cos/sin row as soon as the position is in; no load behind a
+// lane-dependent branch (lanes past the last row or the rotated span read a
+// valid chunk and store nothing -- their stores fall outside the wave's
+// buffer range), and an empty asm after each group of loads so the compiler
+// does not sink them to their first use.  Spare waves of the last block read
+// the last wave's rows and store nothing.
 template <int DT, int G, int LAYOUT>
 __global__ __launch_bounds__(256) void rope_vec(RopeParams p) {
     constexpr int V = Vec<DT>::n;
     constexpr int RPW = kWave / G;
     constexpr int EB = EltBytes<DT>::n;
-    const uint32_t wv = (uint32_t)uniform((int)(blockIdx.x * 4u + (threadIdx.x >> 6)));
-    if (wv >= p.total_waves) return;
+    const uint32_t wv0 = (uint32_t)uniform((int)(blockIdx.x * 4u + (threadIdx.x >> 6)));
+    const bool spare = wv0 >= p.total_waves;
+    const uint32_t wv = spare ? p.total_waves - 1 : wv0;
     const bool is_q = wv < p.q_waves;
     const int heads = is_q ? p.Q : p.K;
-    const int64_t nrows = p.T * heads;
-    const int64_t row = (int64_t)(is_q ? wv : wv - p.q_waves) * RPW + (threadIdx.x & 63) / G;
-    const int j = threadIdx.x % G;
+    const int64_t nrows = p.T * heads;                      // >= 1: the wave has a row
+    const int64_t row0 = (int64_t)(is_q ? wv : wv - p.q_waves) * RPW;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = row0 + lane / G;
+    const bool live = row < nrows;
+    const int64_t rowc = live ? row : nrows - 1;
+    const int j = lane % G;
     const int half = p.rot >> 1;
     const int hv = half / V;
     const int rc = LAYOUT == 0 ? 2 * hv : (p.rot + V - 1) / V;   // rotated chunks
-    const bool live = row < nrows;
-    const int64_t ppos =
-        live ? p.pos[token_of((uint32_t)row, heads, is_q ? p.inv_Q : p.inv_K)] : -1;
-    const bool rotate = live && ppos >= 0 && ppos < p.max_pos && j < rc;
-    char* base = (char*)(is_q ? p.q : p.k) + row * (int64_t)p.D * EB + j * 16;
-    const u32x4 xv = rotate ? ld16(base) : u32x4{0u, 0u, 0u, 0u};
-    const float* crow = p.cos_sin + (rotate ? ppos * (int64_t)p.rot : 0);
+    const int jc = j < rc ? j : 0;                          // a chunk every lane may read
+    const bool is_a = LAYOUT == 0 && jc < hv;
+    char* wbase = (char*)(is_q ? p.q : p.k) + row0 * (int64_t)p.D * EB;
+
+    const int64_t ppos = p.pos[token_of((uint32_t)rowc, heads, is_q ? p.inv_Q : p.inv_K)];
+    const u32x4 xv = ld16(wbase + (rowc - row0) * (int64_t)p.D * EB + jc * 16);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const bool in_cache = ppos >= 0 && ppos < p.max_pos;
+    const float* crow = p.cos_sin + (in_cache ? ppos : 0) * (int64_t)p.rot;
+    constexpr int NCS = LAYOUT == 0 ? V / 4 : 1;
+    u32x4 cv[NCS], sv[NCS];
+    float ci[V / 2], si[V / 2];
+    if constexpr (LAYOUT == 0) {
+        const int j0 = (is_a ? jc : jc - hv) * V;
+#pragma unroll
+        for (int i = 0; i < NCS; ++i) {
+            cv[i] = ld16(crow + j0 + 4 * i);
+            sv[i] = ld16(crow + half + j0 + 4 * i);
+        }
+    } else {
+        const int j0 = jc * (V / 2);
+#pragma unroll
+        for (int i = 0; i < V / 2; ++i) {
+            const int e = (j0 + i < half) ? j0 + i : 0;
+            ci[i] = crow[e];
+            si[i] = crow[half + e];
+        }
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
     float a[V], o[V];
     unpack<DT>(xv, a);
     if constexpr (LAYOUT == 0) {
-        const bool is_a = j < hv;
-        const u32x4 pb = rot_partner(xv, hv, is_a);      // all lanes take part
-        if (!rotate) return;
         float b[V];
-        unpack<DT>(pb, b);
-        const int j0 = (is_a ? j : j - hv) * V;
+        unpack<DT>(rot_partner(xv, hv, is_a), b);           // all lanes take part
 #pragma unroll
-        for (int i = 0; i < V; i += 4) {
-            const u32x4 cv = ld16(crow + j0 + i);
-            const u32x4 sv = ld16(crow + half + j0 + i);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float c = __uint_as_float(cv[m]);
-                const float sn = is_a ? -__uint_as_float(sv[m]) : __uint_as_float(sv[m]);
-                o[i + m] = rot_mac(a[i + m], c, b[i + m], sn);
-            }
+        for (int i = 0; i < V; ++i) {
+            const float c = __uint_as_float(cv[i / 4][i % 4]);
+            const float sn = __uint_as_float(sv[i / 4][i % 4]);
+            o[i] = rot_mac(a[i], c, b[i], is_a ? -sn : sn);
         }
     } else {
-        if (!rotate) return;
-        const int j0 = j * (V / 2);
+        const int j0 = jc * (V / 2);
 #pragma unroll
         for (int i = 0; i < V / 2; ++i) {
-            if (j0 + i < half) {
-                const float c = crow[j0 + i], sn = crow[half + j0 + i];
-                o[2 * i] = rot_mac(a[2 * i], c, a[2 * i + 1], -sn);
-                o[2 * i + 1] = rot_mac(a[2 * i + 1], c, a[2 * i], sn);
-            } else {                                      // past rot_dim: unchanged
-                o[2 * i] = a[2 * i];
-                o[2 * i + 1] = a[2 * i + 1];
-            }
+            const bool ok = j0 + i < half;                  // past rot_dim: unchanged
+            const float r0 = rot_mac(a[2 * i], ci[i], a[2 * i + 1], -si[i]);
+            const float r1 = rot_mac(a[2 * i + 1], ci[i], a[2 * i], si[i]);
+            o[2 * i] = ok ? r0 : a[2 * i];
+            o[2 * i + 1] = ok ? r1 : a[2 * i + 1];
         }
     }
-    st16(base, pack<DT>(o));
+    // written only for a live row, a rotated chunk and a position in the cache
+    const bool write = !spare && live && j < rc && in_cache;
+    const int64_t wrows = spare ? 0 : (nrows - row0 < RPW) ? nrows - row0 : RPW;
+    const __amdgpu_buffer_rsrc_t buf = buf_rsrc(wbase, (uint32_t)(wrows * p.D * EB));
+    const uint32_t off = write ? (uint32_t)((row - row0) * p.D * EB + j * 16) : 0xFFFFFFF0u;
+    buf_st16(buf, off, pack<DT>(o));
 }
 
 // Scalar kernel: one thread per rotated pair of one head-row.
