@@ -20,8 +20,10 @@
 //
 //  * A head-row of D elements is a segment of G lanes of one wavefront; each
 //    lane holds C 16-byte chunks (8 bf16 / fp16 or 4 fp32) strided by G, so
-//    chunk group 0 (channels [0, G * Vec)) contains the whole rotated span
-//    and only that chunk of each lane runs rotation code.  G * C * Vec = D.
+//    chunk group 0 (channels [0, G * Vec)) contains the whole rotate-half
+//    span and only that chunk of each lane takes part in the rotation;
+//    interleaved pairs are lane-local, so there any chunk may rotate.
+//    G * C * Vec = D.
 //    Decode widths use C = 1 (most waves, least work per wave); prefill
 //    widths use C = 4 where the rotated span allows (for D = 256, rot_dim 64
 //    bf16: 8 lanes x 4 chunks per row, 8 rows per wave).
@@ -118,10 +120,12 @@ __device__ __forceinline__ void partner_f32(const float* n, float* nb, int hv, b
 // with the contract's rounding (the hot path: none of the code below that
 // serves the other forms is compiled in), true for token strides, the slot
 // table, value rows and the single-rounding flag.  Requires 16-byte aligned
-// tensors and token strides, every rotated chunk inside chunk group 0, rows
-// of each tensor below 2^24, and for rotate-half rot/2 a multiple of
-// Vec<DT> and a 16-byte aligned cos/sin cache (interleaved reads its run
-// element-wise).  Waves cover the query rows, then the key rows; with v_in
+// tensors and token strides, for rotate-half every rotated chunk inside
+// chunk group 0, rows
+// of each tensor below 2^24, a 16-byte aligned cos/sin cache, and rot/2 a
+// multiple of Vec<DT> (rotate-half) or of Vec<DT>/2 with rot a multiple of 4
+// (interleaved: each lane's pairs are one aligned run of the cache row).
+// Waves cover the query rows, then the key rows; with v_in
 // a key wave also copies the value heads of its rows, unchanged, to their slot.
 //
 // Load order.  The longest dependent chain is position -> cos/sin row, so
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     const float* cs_base = table ? p.cos_sin : (const float*)wp;
     const int hoff = table ? half : 0;                      // sin half of the row
     const int cs_j0 = LAYOUT == 0 ? (table ? (is_a ? j : (is_b ? j - hv : 0)) * V : 0)
-                                  : j * (V / 2);            // first pair index
+                                  : j * (V / 2);            // first pair (chunk group 0)
     auto issue_loads = [&]() {
     if constexpr (GEN) {
         // value rows: a key wave also carries the value heads of its rows
@@ -267,8 +271,12 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     const bool rotate = (ppos >= 0) && (ppos < p.max_pos) && (p.rot > 0);
     constexpr int NCS = LAYOUT == 0 ? V / 4 : 1;
     u32x4 cs_c4[NCS], cs_s4[NCS];
-    float cs_c[V / 2], cs_s[V / 2];                         // interleaved runs
-    bool lane_rot = false;
+    // interleaved: every chunk group may hold rotated pairs (they are
+    // lane-local), so each of the C chunks has its own cos / sin run
+    constexpr int NCK = LAYOUT == 1 ? C : 1;
+    float cs_c[NCK][V / 2], cs_s[NCK][V / 2];
+    bool lane_rot = false;                                  // rotate-half (group 0)
+    bool rot_k[NCK];                                        // interleaved, per chunk
     // (Not behind a branch, which the compiler would sink the loads into.)
     auto load_cs = [&]() {
         const float* crow = cs_base + (rotate ? ppos : 0) * (int64_t)p.rot;
@@ -281,17 +289,31 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
                 cs_s4[i] = ld16(crow + hoff + j0 + 4 * i);
             }
         } else {
-            // V/2 pairs per lane; a run may cross rot/2, so pairs past it
-            // read pair 0 and keep c = 1, s = 0: exactly unrotated.
-            const int j0 = cs_j0;
-            lane_rot = rotate && (j0 < half);
+            // Each chunk's V/2 consecutive pairs are all below rot/2 or all
+            // past it (the host requires rot/2 to be a multiple of V/2), read
+            // as one 16-byte (8-byte for fp32) run of cos and one of sin;
+            // chunks past rot/2 read the first run and keep R(n).
 #pragma unroll
-            for (int i = 0; i < V / 2; ++i) {
-                const bool ok = (j0 + i) < half;
-                const int e = (table && ok) ? j0 + i : 0;
-                const float c = crow[e], s = crow[hoff + e];
-                cs_c[i] = ok ? c : 1.0f;
-                cs_s[i] = ok ? s : 0.0f;
+            for (int k = 0; k < NCK; ++k) {
+                const int j0 = cs_j0 + k * G * (V / 2);
+                rot_k[k] = rotate && (j0 < half);
+                const int e0 = (table && j0 < half) ? j0 : 0;
+                if constexpr (V == 8) {
+                    const u32x4 cv = ld16(crow + e0), sv = ld16(crow + hoff + e0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        cs_c[k][i] = __uint_as_float(cv[i]);
+                        cs_s[k][i] = __uint_as_float(sv[i]);
+                    }
+                } else {
+                    const u32x2 cv = *reinterpret_cast<const u32x2*>(crow + e0);
+                    const u32x2 sv = *reinterpret_cast<const u32x2*>(crow + hoff + e0);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        cs_c[k][i] = __uint_as_float(cv[i]);
+                        cs_s[k][i] = __uint_as_float(sv[i]);
+                    }
+                }
             }
         }
     };
@@ -383,7 +405,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
             for (int i = 0; i < V; ++i) n[i] = (f[i] * inv) * wreg[i];
         }
         u32x4 out = pack<DT>(n);                            // R(n): the rounded value
-        if (k == 0) {
+        if (LAYOUT == 1 || k == 0) {
             // the rotation's inputs: R(n) (the contract) or n itself (once)
             bool once = false;
             if constexpr (GEN) once = g.once != 0;
@@ -409,18 +431,20 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
                     o[i] = rot_mac(a[i], c, b[i], is_a ? -s : s);
                 }
             } else {
+                const int kk = LAYOUT == 1 ? k : 0;
 #pragma unroll
                 for (int i = 0; i < V / 2; ++i) {
-                    o[2 * i] = rot_mac(a[2 * i], cs_c[i], a[2 * i + 1], -cs_s[i]);
-                    o[2 * i + 1] = rot_mac(a[2 * i + 1], cs_c[i], a[2 * i], cs_s[i]);
+                    o[2 * i] = rot_mac(a[2 * i], cs_c[kk][i], a[2 * i + 1], -cs_s[kk][i]);
+                    o[2 * i + 1] = rot_mac(a[2 * i + 1], cs_c[kk][i], a[2 * i], cs_s[kk][i]);
                 }
             }
             // every lane computes the rotation (no branch, so the cos/sin
             // loads stay where they were issued); lanes outside the rotated
             // span, and tokens outside the cache, keep R(n)
+            const bool take = LAYOUT == 1 ? rot_k[LAYOUT == 1 ? k : 0] : lane_rot;
             const u32x4 ro = pack<DT>(o);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) out[d] = lane_rot ? ro[d] : out[d];
+            for (int d = 0; d < 4; ++d) out[d] = take ? ro[d] : out[d];
         }
         if constexpr (GEN) {
             if (keep) st16_nt(rdst + (k * G + j) * 16, out);
@@ -632,8 +656,13 @@ hipError_t launch_dt(const QkArgs& a, hipStream_t s) {
     if (a.v_in)
         vec = vec && aligned16(a.v_in) && aligned16(a.v_out) && st16(a.v_in_stride) &&
               st16(a.v_out_stride);
-    if (a.rot_dim > 0 && a.max_pos > 0 && a.layout == 0)
-        vec = vec && ((a.rot_dim / 2) % V == 0) && aligned16(a.cos_sin);
+    if (a.rot_dim > 0 && a.max_pos > 0) {
+        // rotate-half: rot/2 a multiple of Vec; interleaved: of Vec/2, with
+        // 16-byte runs of the cache (rows of a multiple of 4 floats)
+        vec = vec && aligned16(a.cos_sin);
+        if (a.layout == 0) vec = vec && ((a.rot_dim / 2) % V == 0);
+        else vec = vec && ((a.rot_dim / 2) % (V / 2) == 0) && (a.rot_dim % 4 == 0);
+    }
     const int QK = a.Q + a.K;
     const int64_t rows = a.T * (int64_t)QK;
     vec = vec && a.T * (int64_t)(a.Q > a.K ? a.Q : a.K) < (int64_t(1) << 24);
@@ -647,7 +676,13 @@ hipError_t launch_dt(const QkArgs& a, hipStream_t s) {
         if (rows >= tun_strided_rows()) {
             for (int cand : {4, 2}) {
                 const int G = L / cand;
-                if (cand <= tun_c_max() && G >= 4 && G >= rc) { C = cand; break; }
+                // rotate-half rotates chunk group 0 only (its partner
+                // permute spans G lanes); interleaved pairs are lane-local,
+                // so any chunk may rotate
+                if (cand <= tun_c_max() && G >= 4 && (a.layout == 1 || G >= rc)) {
+                    C = cand;
+                    break;
+                }
             }
         }
         p.inv_Q = a.Q > 0 ? 1.0f / (float)a.Q : 0.0f;
