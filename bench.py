@@ -627,6 +627,22 @@ def main():
                         "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
                         "tokens_per_s": round(c.T / us * 1e6, 1)})
         prologue["prefill_cold"] = pre
+        # the rest of configuration 3: fp16, and interleaved pairs with full
+        # rotary on head_dim 256
+        other = []
+        for c in W.config3_cells():
+            if c.dtype == W.BF16 and c.layout == W.ROTATE_HALF:
+                continue
+            if c.T not in (256, 2048):
+                continue
+            us = prologue_cold_us(torch, mbt, W, c)
+            gbps = c.bytes_algorithmic() / us / 1e3
+            other.append({"cell": c.name, "QK": f"{c.Q}x{c.K}", "T": c.T,
+                          "layout": "interleaved" if c.layout == W.INTERLEAVED else "rotate_half",
+                          "rot_dim": c.rot, "dtype": W.DTYPE_NAMES[c.dtype],
+                          "cold_us": round(us, 3), "GBps": round(gbps, 1),
+                          "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)})
+        prologue["prefill_cold_other"] = other
         # fused vs split route (norm q rows, norm k rows, rope), in place
         routes = {"warm": [route_us(torch, mbt, W, c, cold=False)
                            for c in W.config2_cells() if c.T in (1, 8, 32, 128)],
