@@ -24,9 +24,10 @@
 //    span and only that chunk of each lane takes part in the rotation;
 //    interleaved pairs are lane-local, so there any chunk may rotate.
 //    G * C * Vec = D.
-//    Decode widths use C = 1 (most waves, least work per wave); prefill
-//    widths use C = 4 where the rotated span allows (for D = 256, rot_dim 64
-//    bf16: 8 lanes x 4 chunks per row, 8 rows per wave).
+//    Decode widths use C = 1 (most waves, least work per wave); wider
+//    launches take the fewest chunks (2 or 4, where the layout allows) that
+//    keep them near one resident round (for D = 256, rot_dim 64 bf16, C = 4:
+//    8 lanes x 4 chunks per row, 8 rows per wave).
 //  * A wave works on rows of ONE tensor (the q heads, then the k heads, each
 //    flattened token-major), so a single set of norm weights sits in its
 //    registers and the rows it streams are contiguous in memory.  Each lane
@@ -558,8 +559,10 @@ int env_int(const char* name, int dflt) {
     const char* e = getenv(name);
     return e ? atoi(e) : dflt;
 }
-int tun_strided_rows() {
-    static const int v = env_int("MBT_QK_STRIDED_ROWS", 12288);
+// Chunks per lane: the fewest that bring the launch to at most this many
+// waves (about ten per CU: one resident round, short per-wave work).
+int tun_c_waves() {
+    static const int v = env_int("MBT_QK_C_WAVES", 2560);
     return v;
 }
 int tun_c_max() {
@@ -664,25 +667,24 @@ hipError_t launch_dt(const QkArgs& a, hipStream_t s) {
         else vec = vec && ((a.rot_dim / 2) % (V / 2) == 0) && (a.rot_dim % 4 == 0);
     }
     const int QK = a.Q + a.K;
-    const int64_t rows = a.T * (int64_t)QK;
     vec = vec && a.T * (int64_t)(a.Q > a.K ? a.Q : a.K) < (int64_t(1) << 24);
     if (vec) {
-        // Chunks per lane: 1 at decode widths; at prefill widths up to 4,
-        // as long as the rotated span stays inside chunk group 0 (G lanes).
+        // Chunks per lane: the fewest (1, 2, 4) whose launch has at most
+        // tun_c_waves() waves, else the most allowed.  Rotate-half rotates
+        // chunk group 0 only (its partner permute spans G lanes), so G must
+        // cover the rotated chunks; interleaved pairs are lane-local, so any
+        // chunk may rotate.  Measured: (24, 4) D = 256 T = 256 takes 2
+        // (3.29 us; 1 chunk 3.43, 4 chunks 3.37), T = 512 takes 4.
         const int half = a.rot_dim / 2;
         const int rc = (a.rot_dim == 0) ? 0
                        : (a.layout == 0 ? 2 * (half / V) : (a.rot_dim + V - 1) / V);
         int C = 1;
-        if (rows >= tun_strided_rows()) {
-            for (int cand : {4, 2}) {
+        if (vec_waves(p, L) > tun_c_waves()) {
+            for (int cand : {2, 4}) {
                 const int G = L / cand;
-                // rotate-half rotates chunk group 0 only (its partner
-                // permute spans G lanes); interleaved pairs are lane-local,
-                // so any chunk may rotate
-                if (cand <= tun_c_max() && G >= 4 && (a.layout == 1 || G >= rc)) {
-                    C = cand;
-                    break;
-                }
+                if (cand > tun_c_max() || G < 4 || (a.layout == 0 && G < rc)) continue;
+                C = cand;
+                if (vec_waves(p, G) <= tun_c_waves()) break;
             }
         }
         p.inv_Q = a.Q > 0 ? 1.0f / (float)a.Q : 0.0f;
