@@ -140,24 +140,30 @@ __device__ __forceinline__ void partner_f32(const float* n, float* nb, int hv, b
 // cos/sin loads behind a wait on the row, the gather cost 0.27 us of 3.54 us
 // at T = 256.
 //
-// THR (C >= 2 only): the order for a launch whose waves fill most of the
-// chip in one resident round.  Every wave of a block first waits for all of
-// its loads (the block's weight staging is issued last and ends in a block
-// barrier), and the cos/sin loads go out after the reduction.  There the
-// early order above measured slower -- (Q, K) = (24, 4), T = 2048: 11.7 us
-// against 10.2 us -- while below about ten waves per CU, and again once the
-// grid needs several rounds, it is the faster one (T = 512: 4.1 against
-// 4.5 us).  The host picks THR from the wave count.
-template <int DT, int G, int C, int LAYOUT, bool GEN, bool THR>
+// ORD, the load order (1 and 2 only with C >= 2; the host picks it from the
+// launch's wave count):
+//   0  the early order above: at most about ten waves per CU, or a grid
+//      that needs several resident rounds;
+//   2  the same loads, but the cos/sin loads wait for a block barrier after
+//      the reduction: from about ten to twenty waves per CU;
+//   1  the whole-block order: the row's chunks first, the block's weight
+//      rows staged by all 256 threads behind a block barrier that waits for
+//      every load of the block, the cos/sin loads after the reduction: from
+//      about twenty waves per CU to one full resident round.
+// Measured on MI355X, (Q, K) = (24, 4), D = 256, rot_dim 64, cold: T = 512
+// (1792 waves) 4.05 / 4.27 / - us for orders 0 / 2 / 1; T = 768 (2688) 5.05
+// / 4.97 / 5.39; T = 2048 (7168) 11.8 / 11.6 / 10.2.
+template <int DT, int G, int C, int LAYOUT, bool GEN, int ORD>
 __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g) {
-    static_assert(!THR || C >= 2, "THR stages weights in LDS: C >= 2");
+    static_assert(ORD == 0 || C >= 2, "orders 1 and 2 stage weights in LDS: C >= 2");
+    constexpr bool THR = ORD == 1;
     constexpr int V = Vec<DT>::n;
     constexpr int RPW = kWave / G;     // rows per wave
     constexpr int EB = EltBytes<DT>::n;
     constexpr int L = G * C;           // 16-byte chunks per row
     // C >= 2: the fp32 (w + delta) rows live in LDS rather than in C * V
     // registers per lane: one row per wave (its own tensor's; each wave
-    // writes and reads only its own row, so no barrier), or with THR the
+    // writes and reads only its own row, so no barrier), or with order 1 the
     // q and k rows once per block, behind a block barrier.
     constexpr int WROWS = C >= 2 ? (THR ? 2 : 4) : 1;
     __shared__ float wsh[WROWS][C >= 2 ? L * V : 1];
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
             }
         }
     };
-    if constexpr (!THR) {
+    if constexpr (ORD == 0) {
         // sched_barrier: no arithmetic on the row is hoisted above these loads
         __builtin_amdgcn_sched_barrier(0);
         load_cs();
@@ -377,7 +383,11 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     else if constexpr (C == 2) ss = part[0] + part[1];
     else ss = (part[0] + part[1]) + (part[2] + part[3]);
     const float inv = inv_rms(ss, p.inv_D, p.eps);
-    if constexpr (THR) load_cs();
+    if constexpr (ORD == 1) load_cs();
+    if constexpr (ORD == 2) {
+        __syncthreads();                                    // every row of the block summed
+        load_cs();
+    }
 
     // ---- normalise, round, rotate (group 0 only), store ----
     float wreg[C >= 2 ? 1 : V];
@@ -576,10 +586,15 @@ int64_t vec_waves(const QkParams& p, int G) {
     return (p.T * p.Q + rpw - 1) / rpw + (p.T * p.K + rpw - 1) / rpw;
 }
 
-// THR between these wave counts (C >= 2): from about ten waves per CU up to
-// one full resident round of 256 CUs x 4 SIMDs x 8 waves.
+// Load orders by wave count (C >= 2): order 2 above MID_LO waves, order 1
+// above THR_LO, both up to THR_HI (one full resident round of 256 CUs x
+// 4 SIMDs x 8 waves); order 0 elsewhere.
+int tun_mid_lo() {
+    static const int v = env_int("MBT_QK_MID_WAVES_LO", 2560);
+    return v;
+}
 int tun_thr_lo() {
-    static const int v = env_int("MBT_QK_THR_WAVES_LO", 2560);
+    static const int v = env_int("MBT_QK_THR_WAVES_LO", 5000);
     return v;
 }
 int tun_thr_hi() {
@@ -587,7 +602,7 @@ int tun_thr_hi() {
     return v;
 }
 
-template <int DT, int G, int C, int LAYOUT, bool GEN, bool THR>
+template <int DT, int G, int C, int LAYOUT, bool GEN, int ORD>
 hipError_t launch_vec(const QkParams& p0, const QkGen<true>& g0, hipStream_t s) {
     QkParams p = p0;
     constexpr int RPW = kWave / G;
@@ -599,7 +614,7 @@ hipError_t launch_vec(const QkParams& p0, const QkGen<true>& g0, hipStream_t s) 
     const uint32_t n_blocks = (p.total_waves + 3u) / 4u;
     QkGen<GEN> g{};
     if constexpr (GEN) g = g0;
-    hipLaunchKernelGGL((qknorm_rope_vec<DT, G, C, LAYOUT, GEN, THR>), dim3(n_blocks), dim3(256),
+    hipLaunchKernelGGL((qknorm_rope_vec<DT, G, C, LAYOUT, GEN, ORD>), dim3(n_blocks), dim3(256),
                        0, s, p, g);
     return hipGetLastError();
 }
@@ -607,17 +622,18 @@ hipError_t launch_vec(const QkParams& p0, const QkGen<true>& g0, hipStream_t s) 
 // (G, C) with G * C = L lanes-of-chunks per row; G a power of two >= 4.
 template <int DT, int LAYOUT, bool GEN>
 hipError_t launch_gc(const QkParams& p, const QkGen<true>& g, int L, int C, hipStream_t s) {
-    bool thr = false;
+    int ord = 0;
     if (C >= 2) {
         const int64_t w = vec_waves(p, L / C);
-        thr = w >= tun_thr_lo() && w <= tun_thr_hi();
+        if (w <= tun_thr_hi()) ord = w > tun_thr_lo() ? 1 : (w > tun_mid_lo() ? 2 : 0);
     }
 #define MBT_QK_CASE1(LL)                                                 \
-    if (L == LL && C == 1) return launch_vec<DT, LL, 1, LAYOUT, GEN, false>(p, g, s);
+    if (L == LL && C == 1) return launch_vec<DT, LL, 1, LAYOUT, GEN, 0>(p, g, s);
 #define MBT_QK_CASE(LL, CC)                                              \
     if (L == LL && C == CC)                                              \
-        return thr ? launch_vec<DT, LL / CC, CC, LAYOUT, GEN, true>(p, g, s) \
-                   : launch_vec<DT, LL / CC, CC, LAYOUT, GEN, false>(p, g, s);
+        return ord == 1   ? launch_vec<DT, LL / CC, CC, LAYOUT, GEN, 1>(p, g, s)   \
+               : ord == 2 ? launch_vec<DT, LL / CC, CC, LAYOUT, GEN, 2>(p, g, s)   \
+                          : launch_vec<DT, LL / CC, CC, LAYOUT, GEN, 0>(p, g, s);
     MBT_QK_CASE1(4)
     MBT_QK_CASE1(8) MBT_QK_CASE(8, 2)
     MBT_QK_CASE1(16) MBT_QK_CASE(16, 2) MBT_QK_CASE(16, 4)

@@ -131,12 +131,15 @@ EDGE_PROLOGUE = [
           max_pos=4096, cell=32),
     _cell(name="c2_f16_d128_full", dtype=W.F16, D=128, rot=128, T=1024, Q=16, K=2,
           max_pos=4096, cell=33),
-    # the two load orders of the chunked kernels (chosen by wave count: the
-    # whole-block order between about 2560 and 8192 waves, the early
-    # cos/sin order outside), each with a ragged last block -- spare waves
-    # and a partly filled last wave -- and with interleaved pairs
-    _cell(name="c4_thr_ragged_T999", D=256, rot=64, T=999, Q=24, K=4, max_pos=4096,
+    # the three load orders of the chunked kernels (chosen by wave count:
+    # the early cos/sin order up to 2560 waves, the barrier-after-the-sum
+    # order up to 5000, the whole-block order up to 8192), each with a ragged
+    # last block -- spare waves and a partly filled last wave -- and with
+    # interleaved pairs
+    _cell(name="c4_mid_ragged_T999", D=256, rot=64, T=999, Q=24, K=4, max_pos=4096,
           positions="arange", cell=34),
+    _cell(name="c4_thr_ragged_T1501", D=256, rot=64, T=1501, Q=24, K=4, max_pos=4096,
+          positions="arange", cell=39),
     _cell(name="c4_lat_ragged_T501", D=256, rot=64, T=501, Q=24, K=4, max_pos=4096,
           positions="arange", cell=35),
     _cell(name="c4_thr_inter32", D=256, rot=32, layout=W.INTERLEAVED, T=1024, Q=24, K=4,
@@ -179,13 +182,15 @@ def test_prologue_width_invariant(mbt, T):
 RAGGED_IN_PLACE = [
     # spare waves in the last block (they read the last wave's rows and store
     # nothing) and partly filled last waves, written in place: one chunk per
-    # lane, and both orders of the chunked kernel
+    # lane, and the three orders of the chunked kernel
     _cell(name="ip_c1_T1", D=256, rot=64, T=1, Q=16, K=2, max_pos=4096, cell=40),
     _cell(name="ip_c1_T7_q5k3", D=256, rot=64, T=7, Q=5, K=3, max_pos=4096, cell=41),
     _cell(name="ip_c4_lat_T501", D=256, rot=64, T=501, Q=24, K=4, max_pos=4096,
           positions="arange", cell=42),
-    _cell(name="ip_c4_thr_T999", D=256, rot=64, T=999, Q=24, K=4, max_pos=4096,
+    _cell(name="ip_c4_mid_T999", D=256, rot=64, T=999, Q=24, K=4, max_pos=4096,
           positions="arange", cell=43),
+    _cell(name="ip_c4_thr_T1501", D=256, rot=64, T=1501, Q=24, K=4, max_pos=4096,
+          positions="arange", cell=44),
 ]
 
 

@@ -172,7 +172,7 @@ STRIDE_CELLS = [
           outside=(), cell=41),
     _cell(name="qkv_f32_16x8_d128", dtype=W.F32, Q=16, K=8, D=128, rot=128, T=9, cell=42),
     _cell(name="qkv_f16_inter", dtype=W.F16, rot=256, layout=W.INTERLEAVED, cell=43),
-    _cell(name="qkv_bf16_thr_T999", Q=24, K=4, T=999, positions="arange", max_pos=4096,
+    _cell(name="qkv_bf16_mid_T999", Q=24, K=4, T=999, positions="arange", max_pos=4096,
           outside=(), cell=44),
 ]
 
@@ -234,10 +234,12 @@ CACHE_CELLS = [
     _cell(name="cache_f16_inter_q0", dtype=W.F16, Q=0, K=4, rot=256, layout=W.INTERLEAVED,
           T=33, cell=54),
     # spare waves and partly filled last waves (one chunk per lane; and the
-    # whole-block order of the chunked kernel)
+    # chunked kernel's other load orders)
     _cell(name="cache_bf16_ragged_q5k3", Q=5, K=3, T=7, max_pos=4096, cell=55),
-    _cell(name="cache_bf16_thr_T999", Q=24, K=4, T=999, positions="arange", max_pos=4096,
+    _cell(name="cache_bf16_mid_T999", Q=24, K=4, T=999, positions="arange", max_pos=4096,
           outside=(), cell=56),
+    _cell(name="cache_bf16_thr_T1501", Q=24, K=4, T=1501, positions="arange", max_pos=4096,
+          outside=(), cell=57),
 ]
 
 
