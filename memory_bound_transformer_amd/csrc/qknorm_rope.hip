@@ -121,13 +121,13 @@ __device__ __forceinline__ void partner_f32(const float* n, float* nb, int hv, b
 // with the contract's rounding (the hot path: none of the code below that
 // serves the other forms is compiled in), true for token strides, the slot
 // table, value rows and the single-rounding flag.  Requires 16-byte aligned
-// tensors and token strides, for rotate-half every rotated chunk inside
-// chunk group 0, rows
-// of each tensor below 2^24, a 16-byte aligned cos/sin cache, and rot/2 a
-// multiple of Vec<DT> (rotate-half) or of Vec<DT>/2 with rot a multiple of 4
-// (interleaved: each lane's pairs are one aligned run of the cache row).
-// Waves cover the query rows, then the key rows; with v_in
-// a key wave also copies the value heads of its rows, unchanged, to their slot.
+// tensors and token strides, rows of each tensor below 2^24, a 16-byte
+// aligned cos/sin cache, and rot/2 a multiple of Vec<DT> with every rotated
+// chunk inside chunk group 0 (rotate-half) or rot/2 a multiple of Vec<DT>/2
+// and rot a multiple of 4 (interleaved: each chunk's pairs are one aligned
+// run of the cache row).  Waves cover the query rows, then the key rows;
+// with v_in a key wave also copies the value heads of its rows, unchanged,
+// to their slot.
 //
 // Load order.  The longest dependent chain is position -> cos/sin row, so
 // the position goes out first, then the weights, then the row's chunks, and
@@ -146,10 +146,10 @@ __device__ __forceinline__ void partner_f32(const float* n, float* nb, int hv, b
 //      that needs several resident rounds;
 //   2  the same loads, but the cos/sin loads wait for a block barrier after
 //      the reduction: from about ten to twenty waves per CU;
-//   1  the whole-block order: the row's chunks first, the block's weight
-//      rows staged by all 256 threads behind a block barrier that waits for
-//      every load of the block, the cos/sin loads after the reduction: from
-//      about twenty waves per CU to one full resident round.
+//   1  the whole-block order: no per-lane weight load; the block's two
+//      weight rows are staged by all 256 threads behind a block barrier that
+//      waits for every load of the block, and the cos/sin loads follow the
+//      reduction: from about twenty waves per CU to one full resident round.
 // Measured on MI355X, (Q, K) = (24, 4), D = 256, rot_dim 64, cold: T = 512
 // (1792 waves) 4.05 / 4.27 / - us for orders 0 / 2 / 1; T = 768 (2688) 5.05
 // / 4.97 / 5.39; T = 2048 (7168) 11.8 / 11.6 / 10.2.
@@ -226,9 +226,6 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     // early as a wait on its own chunks would allow), and stores them at
     // once, so they are not held in registers through the arithmetic.
     u32x4 vx[GEN ? C : 1];
-    u32x4 x[C];
-    u32x4 wraw{0u, 0u, 0u, 0u};
-    int64_t ppos = -1;
     bool carry_v = false, slotted = false;
     int64_t slot_raw = t;                                   // key / value output row (raw)
     // The position-independent parts of the cos/sin addresses, formed
@@ -240,7 +237,6 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     const int hoff = table ? half : 0;                      // sin half of the row
     const int cs_j0 = LAYOUT == 0 ? (table ? (is_a ? j : (is_b ? j - hv : 0)) * V : 0)
                                   : j * (V / 2);            // first pair (chunk group 0)
-    auto issue_loads = [&]() {
     if constexpr (GEN) {
         // value rows: a key wave also carries the value heads of its rows
         // (adjacent to the key heads in a fused QKV buffer)
@@ -255,19 +251,20 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
         if (slotted) slot_raw = g.slot[t];
     }
     // the head of the longest chain: position -> cos/sin row
-    ppos = p.pos[t];
+    const int64_t ppos = p.pos[t];
     // weights: chunk (lane mod L) of the tensor's row -- for C = 1 that is
-    // the lane's own chunk, for C >= 2 the staging share of the LDS row
+    // the lane's own chunk, for C >= 2 the staging share of its LDS row;
+    // order 1 stages both rows block-wide instead
+    u32x4 wraw{0u, 0u, 0u, 0u};
     if constexpr (!THR) wraw = ld16(wp + (lane % L) * 16);
     const char* xsrc;
     if constexpr (GEN)
         xsrc = src + ((int64_t)t * (is_q ? g.q_in_st : g.k_in_st) + (int64_t)h * p.D) * EB;
     else
         xsrc = src + rowc * (int64_t)p.D * EB;
+    u32x4 x[C];
 #pragma unroll
     for (int k = 0; k < C; ++k) x[k] = ld16_nt(xsrc + (k * G + j) * 16);
-    };
-    issue_loads();
     // An empty asm that may touch memory: the loads above cannot be moved
     // below it (to their first use), and it emits no instruction or wait.
     // The sched_barrier keeps arithmetic on their results (the position
