@@ -41,6 +41,20 @@ sys.path.insert(0, ROOT)
 METRIC = "QK-norm+RoPE tokens/s & achieved HBM GB/s (% of peak); µs/call at T=1"
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
 RING_BYTES = int(1.25 * 2 ** 30)
+# Ring slots per graph: enough buffer sets to cover RING_BYTES (five times the
+# 256 MB Infinity Cache), but at most MAX_SLOTS, so a small call (a decode
+# row) does not become a graph of tens of thousands of launches.  At the
+# cap a ring still spans MAX_SLOTS distinct buffer sets.
+MAX_SLOTS = 4096
+
+
+def ring_slots(nbytes):
+    return max(8, min(MAX_SLOTS, -(-RING_BYTES // max(1, nbytes))))
+
+
+def phase(name):
+    """Progress marker on stderr (the JSON line alone goes to stdout)."""
+    print(f"bench: {name}", file=sys.stderr, flush=True)
 KERNEL_SOURCES = {
     "qknorm_rope": "qknorm_rope.hip",
     "rmsnorm": "rmsnorm.hip",
@@ -107,7 +121,7 @@ class Step:
         self.inv_a = W.fp8_inv_scale(float(amax_a.item()))
         self.slot_bytes = (self.pro.bytes_algorithmic() + 2 * self.norm.bytes_algorithmic()
                            + self.act.bytes_algorithmic())
-        self.R = max(8, -(-RING_BYTES // self.slot_bytes))
+        self.R = ring_slots(self.slot_bytes)
         base = dict(x1=t(ni["x"]), r1=t(ni["residual"]), q=t(pi["q"]), k=t(pi["k"]),
                     x2=t(ni["x"]), r2=t(ni["residual"]), gu=t(ai["gate_up"]))
         self.slots = []
@@ -223,7 +237,7 @@ def prologue_cold_us(torch, mbt, W, cell, launches=2000):
     wq, wk = t(i["w_q"]), t(i["w_k"])
     cs = torch.from_numpy(i["cos_sin"]).to(dev)
     pos = torch.from_numpy(i["pos"]).to(dev)
-    R = max(8, -(-RING_BYTES // cell.bytes_algorithmic()))
+    R = ring_slots(cell.bytes_algorithmic())
     q0, k0 = t(i["q"]), t(i["k"])
     ring = [(q0.clone(), k0.clone(), torch.empty_like(q0), torch.empty_like(k0))
             for _ in range(R)]
@@ -255,7 +269,7 @@ def route_us(torch, mbt, W, cell, cold, passes=7, samples=50, inner=32, launches
     wq, wk = t(i["w_q"]), t(i["w_k"])
     cs = torch.from_numpy(i["cos_sin"]).to(dev)
     pos = torch.from_numpy(i["pos"]).to(dev)
-    R = max(8, -(-RING_BYTES // cell.bytes_algorithmic())) if cold else 1
+    R = ring_slots(cell.bytes_algorithmic()) if cold else 1
     q0, k0 = t(i["q"]), t(i["k"])
     ring = [(q0.clone(), k0.clone()) for _ in range(R)]
 
@@ -323,7 +337,7 @@ def extended_cold_us(torch, mbt, W, cell, form, launches=2000):
     pos = torch.from_numpy(i["pos"]).to(dev)
     T, Q, K, D = cell.T, cell.Q, cell.K, cell.D
     nbytes = cell.bytes_algorithmic() if form == "once" else qkv_cache_bytes(cell)
-    R = max(8, -(-RING_BYTES // nbytes))
+    R = ring_slots(nbytes)
     q0, k0 = t(i["q"]), t(i["k"])
     if form == "once":
         ring = [(q0.clone(), k0.clone(), torch.empty_like(q0), torch.empty_like(k0))
@@ -355,7 +369,7 @@ def norm_fp8_cold_us(torch, mbt, W, cell, inv_scale, launches=2000):
     i = cell.inputs()
     t = lambda b: W.to_torch(b, cell.dtype, dev)
     w = None if i["w"] is None else t(i["w"])
-    R = max(8, -(-RING_BYTES // cell.bytes_algorithmic()))
+    R = ring_slots(cell.bytes_algorithmic())
     x0, r0 = t(i["x"]), t(i["residual"])
     ring = [(x0.clone(), r0.clone(), torch.empty(x0.shape, dtype=torch.uint8, device=dev))
             for _ in range(R)]
@@ -380,7 +394,7 @@ def adarms_fp8_cold_us(torch, mbt, W, cell, launches=2000):
     cal = cell.calibration_inputs()
     amax = mbt.adarms_amax(t(cal["x"]), t(cal["residual"]), g, sc, sh, cell.eps)
     inv_scale = W.fp8_inv_scale(float(amax.item()))
-    R = max(8, -(-RING_BYTES // cell.bytes_algorithmic()))
+    R = ring_slots(cell.bytes_algorithmic())
     x0, r0 = t(i["x"]), t(i["residual"])
     ring = [(x0.clone(), r0.clone(), torch.empty(x0.shape, dtype=torch.uint8, device=dev))
             for _ in range(R)]
@@ -395,10 +409,53 @@ def adarms_fp8_cold_us(torch, mbt, W, cell, launches=2000):
     return us
 
 
+def norm_cold_us(torch, mbt, W, cell, launches=1500):
+    """Residual RMSNorm in place (dtype output), cold: each launch uses its
+    own ring slot."""
+    dev = "cuda:0"
+    i = cell.inputs()
+    t = lambda b: W.to_torch(b, cell.dtype, dev)
+    w = t(i["w"])
+    R = ring_slots(cell.bytes_algorithmic())
+    x0, r0 = t(i["x"]), t(i["residual"])
+    ring = [(x0.clone(), r0.clone()) for _ in range(R)]
+
+    def call(j):
+        x, r = ring[j]
+        mbt.fused_add_rmsnorm(x, r, w, cell.eps, cell.weight_offset)
+
+    us = kernel_time_us(torch, call, R, launches)
+    del ring
+    torch.cuda.empty_cache()
+    return us
+
+
+def act_cold_us(torch, mbt, W, cell, inv_scale=1.0, launches=1500):
+    """Gated activation, dtype or FP8 output, cold."""
+    dev = "cuda:0"
+    gu0 = W.to_torch(cell.inputs()["gate_up"], cell.dtype, dev)
+    R = ring_slots(cell.bytes_algorithmic())
+    odt = torch.uint8 if cell.fp8 else gu0.dtype
+    ring = [(gu0.clone(), torch.empty((cell.T, cell.d), dtype=odt, device=dev))
+            for _ in range(R)]
+
+    def call(j):
+        gu, out = ring[j]
+        if cell.fp8:
+            mbt.gated_act_fp8(gu, inv_scale, cell.act, out=out)
+        else:
+            mbt.gated_act(gu, cell.act, out=out)
+
+    us = kernel_time_us(torch, call, R, launches)
+    del ring
+    torch.cuda.empty_cache()
+    return us
+
+
 def copy_ceiling_gbps(torch, nbytes, launches=1000):
     """torch's device copy of nbytes/2 -> nbytes/2 (nbytes of traffic), cold."""
     half = max(16, nbytes // 2)
-    R = max(8, -(-RING_BYTES // nbytes))
+    R = ring_slots(nbytes)
     src = [torch.empty(half, dtype=torch.uint8, device="cuda:0") for _ in range(R)]
     dst = [torch.empty(half, dtype=torch.uint8, device="cuda:0") for _ in range(R)]
     us = kernel_time_us(torch, lambda j: dst[j].copy_(src[j]), R, launches)
@@ -558,6 +615,7 @@ def main():
         print(json.dumps({"copy_probe_bytes_moved": 2 * (args.copy_probe // 2)}))
         return
 
+    phase("step buffers")
     st = Step(torch, mbt, W, args.tokens)
     kernels = {"norm_fp8": (st.norm1, st.norm.bytes_algorithmic(), "rmsnorm"),
                "prologue": (st.prologue, st.pro.bytes_algorithmic(), "qknorm_rope"),
@@ -596,6 +654,7 @@ def main():
     dom = max(share, key=share.get)
     dom_fn, dom_bytes, dom_src = kernels[dom]
     achieved = dom_bytes / per[dom]["us"] / 1e3
+    phase("roofline")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                 "traffic": traffic_for(f"{dom}_T{args.tokens}", dom_src), "kernel": dom,
@@ -603,6 +662,7 @@ def main():
                 "copy_ceiling_GBps": round(copy_ceiling_gbps(torch, dom_bytes), 1)}
 
     # the prologue's own figures (the headline metric's parts)
+    out_extra = {}
     prologue = {"step_T": args.tokens,
                 "tokens_per_s": round(args.tokens / per["prologue"]["us"] * 1e6, 1),
                 "GBps": per["prologue"]["GBps"], "frac_peak": per["prologue"]["frac_peak"]}
@@ -610,6 +670,7 @@ def main():
         t1 = [c for c in W.config2_cells() if c.T == 1][0]
         w1 = prologue_warm_us(torch, mbt, W, t1)
         prologue["us_per_call_T1"] = {k: round(v, 3) for k, v in w1.items()}
+        phase("decode sweep")
         sweep = []
         for c in W.config2_cells():
             w = prologue_warm_us(torch, mbt, W, c, samples=50)
@@ -627,6 +688,7 @@ def main():
                         "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
                         "tokens_per_s": round(c.T / us * 1e6, 1)})
         prologue["prefill_cold"] = pre
+        phase("prefill, other cells")
         # the rest of configuration 3: fp16, and interleaved pairs with full
         # rotary on head_dim 256
         other = []
@@ -643,7 +705,33 @@ def main():
                           "cold_us": round(us, 3), "GBps": round(gbps, 1),
                           "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)})
         prologue["prefill_cold_other"] = other
+        # the residual norm (configuration 4, bf16 and fp32, both weight
+        # conventions folded: delta 0) and the gated activation
+        # (configuration 5), as rows/s and GB/s
+        phase("norm sweep (configuration 4)")
+        nsweep = []
+        for c in W.config4_cells():
+            if c.weight_offset != 0 or c.dtype == W.F16:
+                continue
+            us = norm_cold_us(torch, mbt, W, c)
+            gbps = c.bytes_algorithmic() / us / 1e3
+            nsweep.append({"dtype": W.DTYPE_NAMES[c.dtype], "H": c.H, "T": c.T,
+                           "cold_us": round(us, 3), "rows_per_s": round(c.T / us * 1e6, 1),
+                           "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)})
+        phase("activation sweep (configuration 5)")
+        asweep = []
+        for c in W.config5_cells():
+            if not isinstance(c, W.ActCell):
+                continue
+            us = act_cold_us(torch, mbt, W, c)
+            gbps = c.bytes_algorithmic() / us / 1e3
+            asweep.append({"act": "silu" if c.act == W.SILU else "gelu_tanh", "T": c.T,
+                           "out": "fp8" if c.fp8 else "bf16", "d": c.d, "cold_us": round(us, 3),
+                           "rows_per_s": round(c.T / us * 1e6, 1), "GBps": round(gbps, 1),
+                           "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)})
+        out_extra = {"norm_sweep_config4": nsweep, "act_sweep_config5": asweep}
         # fused vs split route (norm q rows, norm k rows, rope), in place
+        phase("routes")
         routes = {"warm": [route_us(torch, mbt, W, c, cold=False)
                            for c in W.config2_cells() if c.T in (1, 8, 32, 128)],
                   "cold": [route_us(torch, mbt, W, c, cold=True)
@@ -676,6 +764,7 @@ def main():
 
     # RMSNorm -> FP8 with the weight against the no-weight form (the scale
     # folded into the next GEMM), H = 2048, bf16, cold
+    phase("no-weight norm")
     noweight = []
     if not args.no_sweep:
         for T in (args.tokens, 512):
@@ -691,6 +780,7 @@ def main():
             noweight.append(row)
     # adaptive RMSNorm -> FP8 with a gated residual (style vector per call):
     # the Pi0.5 decoder's 10-token rows and a 512-token batch, H = 2048
+    phase("adaptive norm")
     adarms = []
     if not args.no_sweep:
         for T in (10, 512):
@@ -716,6 +806,7 @@ def main():
         "prologue": prologue,
         "norm_fp8_weight_vs_none": noweight,
         "adarms_fp8_gated": adarms,
+        **out_extra,
     }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(W, st, args.cpu_seconds)
