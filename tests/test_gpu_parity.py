@@ -448,12 +448,16 @@ def test_act_unaligned(mbt, orc, dtype):
                    offset=1)
 
 
-def test_act_exhaustive_bf16_gate(mbt, orc):
-    """Every finite bf16 gate value with up = 1: GPU vs oracle, <= 1 ulp."""
+@pytest.mark.parametrize("rows", [1, 50], ids=["one_chunk_per_lane", "two_chunks_per_lane"])
+def test_act_exhaustive_bf16_gate(mbt, orc, rows):
+    """Every finite bf16 gate value with up = 1: GPU vs oracle, <= 1 ulp.
+    50 copies of the row make the launch wide enough for two chunks per
+    lane, whose exponent rescue is taken per wave."""
     bits = np.arange(65536, dtype=np.uint16)
     keep = np.isfinite(W.bits_to_f32(bits, W.BF16))
     bits = bits[keep]
     gu = np.concatenate([bits, W.to_bits(np.ones(bits.size), W.BF16)])[None, :]
+    gu = np.repeat(gu, rows, axis=0)
     for act in (W.SILU, W.GELU_TANH):
         out = host(mbt.gated_act(dev(gu, W.BF16), act), W.BF16)
         C.check_values(out, orc.gated_act(gu, act, W.BF16), W.BF16, label=f"act {act}")
