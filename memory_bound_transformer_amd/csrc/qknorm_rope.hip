@@ -282,8 +282,43 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     bool lane_rot = false;                                  // rotate-half (group 0)
     bool rot_k[NCK];                                        // interleaved, per chunk
     // (Not behind a branch, which the compiler would sink the loads into.)
+    const float* crow = cs_base + (rotate ? ppos : 0) * (int64_t)p.rot;
+    // Interleaved, chunk k: its V/2 consecutive pairs are all below rot/2 or
+    // all past it (the host requires rot/2 to be a multiple of V/2), read as
+    // one 16-byte (8-byte for fp32) run of cos and one of sin; chunks past
+    // rot/2 read the first run and keep R(n).
+    auto load_cs_chunk = [&](int k) {
+        const int j0 = cs_j0 + k * G * (V / 2);
+        rot_k[k] = rotate && (j0 < half);
+        const int e0 = (table && j0 < half) ? j0 : 0;
+        if constexpr (V == 8) {
+            const u32x4 cv = ld16(crow + e0), sv = ld16(crow + hoff + e0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cs_c[k][i] = __uint_as_float(cv[i]);
+                cs_s[k][i] = __uint_as_float(sv[i]);
+            }
+        } else {
+            const u32x2 cv = *reinterpret_cast<const u32x2*>(crow + e0);
+            const u32x2 sv = *reinterpret_cast<const u32x2*>(crow + hoff + e0);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                cs_c[k][i] = __uint_as_float(cv[i]);
+                cs_s[k][i] = __uint_as_float(sv[i]);
+            }
+        }
+    };
+    // Interleaved rows in order 1 issue a chunk's runs two chunks ahead of
+    // its rotation, not all C up front: with C = 4 that is 16 live registers
+    // of cos/sin instead of 32, which keeps the kernel at eight waves per
+    // SIMD (63 VGPRs for bf16, against 83 and five waves up front).  Order 1
+    // serves launches of up to one round at eight waves per SIMD, so at five
+    // its last waves waited for a second round: (Q, K) = (24, 4), T = 2048,
+    // rot_dim 256, cold, 13.07 -> 10.72 us on MI355X.  The lower orders fit
+    // in one round at five waves per SIMD and keep every run up front (2 %
+    // faster at (16, 2), T = 2048).
+    constexpr int PIPE = (LAYOUT == 1 && ORD == 1) ? 2 : C;   // runs issued up front
     auto load_cs = [&]() {
-        const float* crow = cs_base + (rotate ? ppos : 0) * (int64_t)p.rot;
         if constexpr (LAYOUT == 0) {
             lane_rot = rotate && (is_a || is_b);
             const int j0 = cs_j0;
@@ -293,32 +328,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
                 cs_s4[i] = ld16(crow + hoff + j0 + 4 * i);
             }
         } else {
-            // Each chunk's V/2 consecutive pairs are all below rot/2 or all
-            // past it (the host requires rot/2 to be a multiple of V/2), read
-            // as one 16-byte (8-byte for fp32) run of cos and one of sin;
-            // chunks past rot/2 read the first run and keep R(n).
 #pragma unroll
-            for (int k = 0; k < NCK; ++k) {
-                const int j0 = cs_j0 + k * G * (V / 2);
-                rot_k[k] = rotate && (j0 < half);
-                const int e0 = (table && j0 < half) ? j0 : 0;
-                if constexpr (V == 8) {
-                    const u32x4 cv = ld16(crow + e0), sv = ld16(crow + hoff + e0);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        cs_c[k][i] = __uint_as_float(cv[i]);
-                        cs_s[k][i] = __uint_as_float(sv[i]);
-                    }
-                } else {
-                    const u32x2 cv = *reinterpret_cast<const u32x2*>(crow + e0);
-                    const u32x2 sv = *reinterpret_cast<const u32x2*>(crow + hoff + e0);
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        cs_c[k][i] = __uint_as_float(cv[i]);
-                        cs_s[k][i] = __uint_as_float(sv[i]);
-                    }
-                }
-            }
+            for (int k = 0; k < NCK && k < PIPE; ++k) load_cs_chunk(k);
         }
     };
     if constexpr (ORD == 0) {
@@ -453,6 +464,14 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
             const u32x4 ro = pack<DT>(o);
 #pragma unroll
             for (int d = 0; d < 4; ++d) out[d] = take ? ro[d] : out[d];
+        }
+        if constexpr (PIPE < C) {
+            // the runs PIPE chunks on, issued once this chunk's are used
+            if (k + PIPE < C) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_cs_chunk(k + PIPE);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         if constexpr (GEN) {
             if (keep) st16_nt(rdst + (k * G + j) * 16, out);
