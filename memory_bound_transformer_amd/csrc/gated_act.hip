@@ -108,30 +108,43 @@ __device__ __forceinline__ void act_mul_vec(const float* g, const float* u, floa
 }
 
 // Vector kernel: d a multiple of Vec<DT>; gate_up and out 16-byte aligned,
-// out8 aligned to its 8- (16-bit) or 4-byte (fp32) store.
+// out8 aligned to its 8- (16-bit) or 4-byte (fp32) store; a half row below
+// 2^31 bytes.  All arguments come in one batch of scalar loads, and every
+// access goes through a buffer resource over the token's gate half, up half
+// or output row: chunks past d read zeros (act(0) * 0 = 0, so they leave
+// amax alone) and their stores are dropped, with no branch around a load or
+// store.
 template <int DT, int ACT, int MODE, int U>
 __global__ __launch_bounds__(256) void gated_vec(ActParams p) {
     constexpr int V = Vec<DT>::n;
     constexpr int EB = EltBytes<DT>::n;
+    asm volatile("" ::"s"(p.gate_up), "s"(p.d), "s"(p.blocks_per_row));
+    if constexpr (MODE == kActDtype) asm volatile("" ::"s"(p.out));
+    if constexpr (MODE == kActFp8) asm volatile("" ::"s"(p.out8), "s"(p.inv_scale));
+    if constexpr (MODE == kActAmax) asm volatile("" ::"s"(p.amax));
     const uint32_t bpr = (uint32_t)p.blocks_per_row;
-    const int64_t t = (int64_t)(blockIdx.x / bpr);
-    const int cb = (int)(blockIdx.x % bpr);
-    const char* row = (const char*)p.gate_up + t * (2 * (int64_t)p.d) * EB;
+    const uint32_t tu = blockIdx.x / bpr;
+    const int64_t t = tu;
+    const int cb = (int)(blockIdx.x - tu * bpr);
+    const uint32_t hb = (uint32_t)p.d * EB;                 // bytes of a half row
+    const char* row = (const char*)p.gate_up + t * 2 * (int64_t)hb;
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc((void*)row, hb);
+    const __amdgpu_buffer_rsrc_t ru = buf_rsrc((void*)(row + hb), hb);
     u32x4 gv[U], uv[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const int ch = (cb * U + k) * 256 + threadIdx.x;
-        gv[k] = u32x4{0u, 0u, 0u, 0u};
-        uv[k] = u32x4{0u, 0u, 0u, 0u};
-        if (ch < p.chunks) {
-            gv[k] = ld16_nt(row + (int64_t)ch * 16);
-            uv[k] = ld16_nt(row + (int64_t)p.d * EB + (int64_t)ch * 16);
-        }
+        const uint32_t off = (uint32_t)((cb * U + k) * 256 + threadIdx.x) * 16u;
+        gv[k] = buf_ld16_nt(rg, off);
+        uv[k] = buf_ld16_nt(ru, off);
     }
+    asm volatile("" ::: "memory");
+    __amdgpu_buffer_rsrc_t ro = rg;
+    if constexpr (MODE == kActDtype) ro = buf_rsrc((char*)p.out + t * (int64_t)hb, hb);
+    if constexpr (MODE == kActFp8) ro = buf_rsrc(p.out8 + t * (int64_t)p.d, (uint32_t)p.d);
     float amax_acc = 0.0f;
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        const int ch = (cb * U + k) * 256 + threadIdx.x;
+        const uint32_t ch = (uint32_t)((cb * U + k) * 256 + threadIdx.x);
         float g[V], u[V], y[V];
         unpack<DT>(gv[k], g);
         unpack<DT>(uv[k], u);
@@ -141,10 +154,8 @@ __global__ __launch_bounds__(256) void gated_vec(ActParams p) {
 #pragma unroll
             for (int i = 0; i < V; ++i) y[i] = act_mul<DT, ACT>(g[i], u[i]);
         }
-        if (ch >= p.chunks) continue;
-        const int64_t e0 = t * (int64_t)p.d + (int64_t)ch * V;
         if constexpr (MODE == kActDtype) {
-            st16_nt((char*)p.out + e0 * EB, pack<DT>(y));
+            buf_st16_nt(ro, ch * 16u, pack<DT>(y));
         } else if constexpr (MODE == kActFp8) {
             if constexpr (V == 8) {
                 u32x2 c;
@@ -152,10 +163,10 @@ __global__ __launch_bounds__(256) void gated_vec(ActParams p) {
                              y[3] * p.inv_scale);
                 c[1] = fp8x4(y[4] * p.inv_scale, y[5] * p.inv_scale, y[6] * p.inv_scale,
                              y[7] * p.inv_scale);
-                st8_nt(p.out8 + e0, c);
+                buf_st8_nt(ro, ch * 8u, c);
             } else {
-                st4_nt(p.out8 + e0, fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale,
-                                          y[2] * p.inv_scale, y[3] * p.inv_scale));
+                buf_st4_nt(ro, ch * 4u, fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale,
+                                              y[2] * p.inv_scale, y[3] * p.inv_scale));
             }
         } else {
 #pragma unroll
@@ -212,7 +223,8 @@ hipError_t launch_mode(const ActArgs& a, hipStream_t s) {
     ActParams p{};
     p.gate_up = a.gate_up; p.out = a.out; p.out8 = a.out8; p.amax = a.amax;
     p.inv_scale = a.inv_scale; p.T = a.T; p.d = a.d;
-    bool vec = (a.d % V == 0) && aligned16(a.gate_up);
+    bool vec = (a.d % V == 0) && aligned16(a.gate_up) &&
+               (int64_t)a.d * EltBytes<DT>::n < (int64_t(1) << 31);
     if (MODE == kActDtype) vec = vec && aligned16(a.out);
     if (MODE == kActFp8)
         vec = vec && ((reinterpret_cast<uintptr_t>(a.out8) & (V == 8 ? 7u : 3u)) == 0);

@@ -66,6 +66,22 @@ __device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off,
 __device__ __forceinline__ void buf_st16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 2);
 }
+// 16-byte loads through a buffer resource: offsets outside the range read
+// zeros (the same range check), so a partial wave needs no branch around
+// its loads either.  Default and nontemporal policies.
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+}
+// 8- and 4-byte nontemporal stores through a buffer resource (packed FP8).
+__device__ __forceinline__ void buf_st8_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 2);
+}
+__device__ __forceinline__ void buf_st4_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 2);
+}
 __device__ __forceinline__ void st8_nt(void* p, u32x2 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
 }

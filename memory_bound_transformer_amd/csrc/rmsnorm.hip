@@ -57,6 +57,7 @@ struct NormParams {
     float eps, inv_H, delta;
     int32_t wpr;   // wide kernel: waves per row
     int32_t rpb;   // wide kernel: rows per block
+    int32_t wsh;   // wide kernel: wave -> row in block is wave >> wsh
     const void* gate;    // adaptive form: residual gate (NULL: 1)
     const void* shift;   // adaptive form: added after the scale
 };
@@ -127,6 +128,29 @@ __device__ __forceinline__ u32x4 residual_sum(u32x4 xv, u32x4 rv, u32x4 gv, bool
 }
 
 // The adaptive form's shift, added to the scaled value.
+// The same sum with no branch: formed always, and x itself selected when
+// there is no residual (x + 0 would turn -0 into +0).
+template <int DT, bool GATED>
+__device__ __forceinline__ u32x4 residual_sum_sel(u32x4 xv, u32x4 rv, u32x4 gv, bool has_res) {
+    constexpr int V = Vec<DT>::n;
+    float a[V], b[V];
+    unpack<DT>(xv, a);
+    unpack<DT>(rv, b);
+    if constexpr (GATED) {
+        float g[V];
+        unpack<DT>(gv, g);
+#pragma unroll
+        for (int i = 0; i < V; ++i) a[i] = g[i] * a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) a[i] += b[i];
+    const u32x4 sv = pack<DT>(a);
+    u32x4 out;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) out[d] = has_res ? sv[d] : xv[d];
+    return out;
+}
+
 template <int DT, bool ADA>
 __device__ __forceinline__ void add_shift(const NormParams& p, int64_t e0, float* y) {
     if constexpr (ADA) {
@@ -182,6 +206,18 @@ __global__ __launch_bounds__(256) void rmsnorm_small(NormParams p) {
 // Rows of more than 64 chunks: WPR waves per row (RPB rows per block when
 // WPR divides 4), NCH chunks per lane.  Chunk ch = k * 64 * WPR + wave * 64
 // + lane, so chunk group g = k * WPR + wave holds 64 consecutive chunks.
+//
+// Every access goes through a buffer resource over the wave's row (range 0
+// for a row past T, and for a residual that is NULL): chunks past the row
+// read zeros and their stores are dropped, so no load or store sits behind
+// a branch and the loads go out back to back.  All arguments come in one
+// batch of scalar loads, and the wave's row in the block is a shift, not a
+// division.  Measured on MI355X, cold, bf16, against the branched form with
+// two argument rounds: residual norm H = 2560 T = 1 / 128 / 512 2.37 / 2.86
+// / 3.69 -> 2.09 / 2.60 / 3.40 us; norm -> FP8 H = 2048 T = 128 / 2048 2.75
+// / 6.67 -> 2.62 / 6.00 us.  Storing the residual sum before the reduction
+// (to overlap the barrier) gained nothing at one chunk per lane and cost 17 %
+// at four (T = 2048), so it is stored with the output.
 constexpr int kMaxNch = 6;
 constexpr int kMaxGroups = kMaxNch * 16;
 
@@ -190,43 +226,64 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
     constexpr int V = Vec<DT>::n;
     constexpr int EB = EltBytes<DT>::n;
     __shared__ float gsum[4][kMaxGroups];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    asm volatile("" ::"s"(p.x), "s"(p.residual), "s"(p.w), "s"(p.T), "s"(p.H), "s"(p.eps),
+                 "s"(p.inv_H), "s"(p.delta), "s"(p.wpr), "s"(p.rpb), "s"(p.wsh));
+    if constexpr (MODE == kNormInPlace) asm volatile("" ::"s"(p.x_out));
+    if constexpr (MODE == kNormFp8) asm volatile("" ::"s"(p.y8), "s"(p.inv_scale));
+    if constexpr (MODE == kNormAmax) asm volatile("" ::"s"(p.amax));
+    if constexpr (ADA) asm volatile("" ::"s"(p.gate), "s"(p.shift));
+    const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
     const int wpr = p.wpr;
-    const int rib = wave / wpr, wir = wave % wpr;
+    const int rib = wave >> p.wsh, wir = wave - rib * wpr;   // row in block, wave in row
     const int64_t row = (int64_t)blockIdx.x * p.rpb + rib;
-    const bool live = row < p.T;
+    const bool live = row < p.T;                               // wave-uniform
     const int chunks = p.H / V;
     const int ngroups = (chunks + kWave - 1) / kWave;
     const int stride = kWave * wpr;
     const bool has_res = p.residual != nullptr;
+    const uint32_t hb = (uint32_t)p.H * EB;                   // bytes of a row
+    const uint32_t rb = live ? hb : 0u;
+    const int64_t ro = live ? row * (int64_t)hb : 0;
+    const __amdgpu_buffer_rsrc_t rx = buf_rsrc((char*)p.x + ro, rb);
+    const __amdgpu_buffer_rsrc_t rr =
+        buf_rsrc(has_res ? (char*)p.residual + ro : (char*)p.x, has_res ? rb : 0u);
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc((void*)p.w, p.w ? hb : 0u);
+    __amdgpu_buffer_rsrc_t rg = rw;
+    if constexpr (ADA) rg = buf_rsrc((void*)p.gate, p.gate ? hb : 0u);
 
-    // Every load of the row (x, residual, weight) is issued before any math.
+    // Every load of the row (x, residual, weight, gate) before any math.
     u32x4 xv[NCH], rv[NCH], wv[NCH], gv[ADA ? NCH : 1];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-        const int ch = k * stride + wir * kWave + lane;
-        xv[k] = u32x4{0u, 0u, 0u, 0u};
-        rv[k] = u32x4{0u, 0u, 0u, 0u};
-        wv[k] = ones16<DT>();
-        if constexpr (ADA) gv[k] = ones16<DT>();
-        if (live && ch < chunks) {
-            const int64_t off = (row * p.H + (int64_t)ch * V) * EB;
-            xv[k] = ld16_nt((const char*)p.x + off);
-            if (has_res) rv[k] = ld16_nt((const char*)p.residual + off);
-            if (p.w) wv[k] = ld16((const char*)p.w + (int64_t)ch * V * EB);
-            if constexpr (ADA)
-                if (p.gate) gv[k] = ld16((const char*)p.gate + (int64_t)ch * V * EB);
-        }
+        const uint32_t off = (uint32_t)(k * stride + wir * kWave + lane) * 16u;
+        xv[k] = buf_ld16_nt(rx, off);
+        rv[k] = buf_ld16_nt(rr, off);
+        wv[k] = buf_ld16(rw, off);
+        if constexpr (ADA) gv[k] = buf_ld16(rg, off);
     }
-    // group sums: chunk chains, then the 64-lane tree of each group
+    asm volatile("" ::: "memory");
+    const bool has_w = p.w != nullptr;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) wv[k][d] = has_w ? wv[k][d] : ones16<DT>()[d];
+    if constexpr (ADA) {
+        const bool has_g = p.gate != nullptr;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) gv[k][d] = has_g ? gv[k][d] : ones16<DT>()[d];
+    }
+
+    // s = R(x + r); group sums: chunk chains, then the 64-lane tree of each
+    // group (chunks past the row are zeros)
     float gs[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-        const int ch = k * stride + wir * kWave + lane;
-        xv[k] = residual_sum<DT, ADA>(xv[k], rv[k], gv[ADA ? k : 0], has_res);   // s
+        xv[k] = residual_sum_sel<DT, ADA>(xv[k], rv[k], gv[ADA ? k : 0], has_res);   // s
         float s[V];
         unpack<DT>(xv[k], s);
-        gs[k] = seg_sum<64>((live && ch < chunks) ? chunk_sumsq<DT>(s) : 0.0f);
+        gs[k] = seg_sum<64>(chunk_sumsq<DT>(s));
     }
     float ss;
     if (wpr == 1) {
@@ -246,21 +303,50 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
         if (ngroups > kWave) ss += seg_sum<64>(hi);
     }
     const float inv = inv_rms(ss, p.inv_H, p.eps);
+
+    __amdgpu_buffer_rsrc_t ro_ = rx, rsh = rx;
+    if constexpr (MODE == kNormInPlace) ro_ = buf_rsrc((char*)p.x_out + ro, rb);
+    if constexpr (MODE == kNormFp8)
+        ro_ = buf_rsrc(p.y8 + (live ? row * (int64_t)p.H : 0), live ? (uint32_t)p.H : 0u);
+    if constexpr (ADA) rsh = buf_rsrc((void*)p.shift, hb);
     float amax_acc = 0.0f;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         const int ch = k * stride + wir * kWave + lane;
-        if (!(live && ch < chunks)) continue;
-        const int64_t e0 = (int64_t)ch * V;
-        if (has_res && MODE != kNormAmax)
-            st16_nt((char*)p.residual + (row * p.H + e0) * EB, xv[k]);
+        const uint32_t off = (uint32_t)ch * 16u;
+        // (no residual: rr has range 0 and the store is dropped)
+        if constexpr (MODE != kNormAmax) buf_st16_nt(rr, off, xv[k]);
         float s[V], wf[V], y[V];
         unpack<DT>(xv[k], s);
         unpack<DT>(wv[k], wf);
 #pragma unroll
         for (int i = 0; i < V; ++i) y[i] = (s[i] * inv) * (wf[i] + p.delta);
-        add_shift<DT, ADA>(p, e0, y);
-        emit<DT, MODE>(p, row, e0, y, amax_acc);
+        if constexpr (ADA) {
+            float sh[V];
+            unpack<DT>(buf_ld16(rsh, off), sh);
+#pragma unroll
+            for (int i = 0; i < V; ++i) y[i] += sh[i];
+        }
+        if constexpr (MODE == kNormInPlace) {
+            buf_st16_nt(ro_, off, pack<DT>(y));
+        } else if constexpr (MODE == kNormFp8) {
+            if constexpr (V == 8) {
+                u32x2 c;
+                c[0] = fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
+                             y[3] * p.inv_scale);
+                c[1] = fp8x4(y[4] * p.inv_scale, y[5] * p.inv_scale, y[6] * p.inv_scale,
+                             y[7] * p.inv_scale);
+                buf_st8_nt(ro_, (uint32_t)ch * 8u, c);
+            } else {
+                buf_st4_nt(ro_, (uint32_t)ch * 4u,
+                           fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
+                                 y[3] * p.inv_scale));
+            }
+        } else {
+            const bool valid = live && ch < chunks;
+#pragma unroll
+            for (int i = 0; i < V; ++i) amax_acc = fmaxf(amax_acc, valid ? fabsf(y[i]) : 0.0f);
+        }
     }
     if constexpr (MODE == kNormAmax) {
         amax_acc = seg_max<64>(amax_acc);
@@ -407,6 +493,9 @@ hipError_t launch_mode(const NormArgs& a, hipStream_t s) {
     if (vec) {
         p.wpr = pick_wpr(a.T, chunks);
         p.rpb = (p.wpr <= 4 && 4 % p.wpr == 0) ? 4 / p.wpr : 1;
+        // several rows per block only for wpr 1, 2 or 4; one row: every
+        // wave (at most 16) maps to row 0
+        p.wsh = p.rpb > 1 ? (p.wpr == 1 ? 0 : (p.wpr == 2 ? 1 : 2)) : 5;
         const int nch = (chunks + kWave * p.wpr - 1) / (kWave * p.wpr);
         switch (nch) {
         case 1: return launch_vec_n<DT, MODE, ADA, 1>(p, s);

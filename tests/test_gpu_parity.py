@@ -349,6 +349,16 @@ EDGE_NORM = [
     _ncell(name="noweight_no_residual", weight=False, residual=False, cell=18),
     _ncell(name="noweight_fp8_H2048_T512", weight=False, fp8=True, H=2048, T=512, cell=19),
     _ncell(name="noweight_fp8_odd", weight=False, fp8=True, H=333, cell=20),
+    # the wide kernel's buffer ranges: four rows per block with the last
+    # block partly past T, two rows per block likewise, and rows whose last
+    # wave (or last chunk of a lane) lies partly past H
+    _ncell(name="wide_rpb4_T2049", H=2048, T=2049, cell=21),
+    _ncell(name="wide_rpb4_T2049_fp8", H=2048, T=2049, fp8=True, cell=22),
+    _ncell(name="wide_rpb2_H4096_T1025", H=4096, T=1025, cell=23),
+    _ncell(name="partial_wave_H2504", H=2504, cell=24),
+    _ncell(name="partial_chunks_H2504_T2001", H=2504, T=2001, cell=25),
+    _ncell(name="partial_fp8_f32_H2500_T3001", dtype=W.F32, H=2500, T=3001, fp8=True, cell=26),
+    _ncell(name="wide_no_residual_T2049", residual=False, H=2048, T=2049, cell=27),
 ]
 
 
