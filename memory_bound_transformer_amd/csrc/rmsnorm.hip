@@ -62,36 +62,6 @@ struct NormParams {
     const void* shift;   // adaptive form: added after the scale
 };
 
-template <int DT, int MODE>
-__device__ __forceinline__ void emit(const NormParams& p, int64_t row, int64_t e0,
-                                     const float* y, float& amax_acc) {
-    constexpr int V = Vec<DT>::n;
-    constexpr int EB = EltBytes<DT>::n;
-    if constexpr (MODE == kNormInPlace) {
-        st16_nt((char*)p.x_out + (row * p.H + e0) * EB, pack<DT>(y));
-    } else if constexpr (MODE == kNormFp8) {
-        uint8_t* dst = p.y8 + row * p.H + e0;
-        if constexpr (V == 8) {
-            u32x2 c;
-            c[0] = fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
-                         y[3] * p.inv_scale);
-            c[1] = fp8x4(y[4] * p.inv_scale, y[5] * p.inv_scale, y[6] * p.inv_scale,
-                         y[7] * p.inv_scale);
-            st8_nt(dst, c);
-        } else {
-            st4_nt(dst, fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
-                              y[3] * p.inv_scale));
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < V; ++i) amax_acc = fmaxf(amax_acc, fabsf(y[i]));
-    }
-}
-
-// Balanced tree over g[0 .. n-1] padded with zeros to a power of two (a
-// missing right operand adds nothing).  Leaves the total in g[0].  Padding to
-// a larger power of two only adds +0 at the top, so N may exceed the count of
-// non-zero entries.
 template <int N>
 __device__ __forceinline__ float fixed_tree(float* g) {
 #pragma unroll
@@ -109,29 +79,10 @@ __device__ __forceinline__ float group_tree(float* g, int n) {
 // s = R(x + r) for one chunk (fp32 add of the decoded operands, one rounding),
 // returned packed; x alone without a residual.  With a gate (adaptive form)
 // s = R(r + g * x), the product rounded to fp32 first.
+// s = R(x + r) (with the gate: R(g * x + r)), formed with no branch, and x
+// itself selected when there is no residual (x + 0 would turn -0 into +0).
 template <int DT, bool GATED>
 __device__ __forceinline__ u32x4 residual_sum(u32x4 xv, u32x4 rv, u32x4 gv, bool has_res) {
-    constexpr int V = Vec<DT>::n;
-    if (!has_res) return xv;
-    float a[V], b[V];
-    unpack<DT>(xv, a);
-    unpack<DT>(rv, b);
-    if constexpr (GATED) {
-        float g[V];
-        unpack<DT>(gv, g);
-#pragma unroll
-        for (int i = 0; i < V; ++i) a[i] = g[i] * a[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V; ++i) a[i] += b[i];
-    return pack<DT>(a);
-}
-
-// The adaptive form's shift, added to the scaled value.
-// The same sum with no branch: formed always, and x itself selected when
-// there is no residual (x + 0 would turn -0 into +0).
-template <int DT, bool GATED>
-__device__ __forceinline__ u32x4 residual_sum_sel(u32x4 xv, u32x4 rv, u32x4 gv, bool has_res) {
     constexpr int V = Vec<DT>::n;
     float a[V], b[V];
     unpack<DT>(xv, a);
@@ -151,53 +102,86 @@ __device__ __forceinline__ u32x4 residual_sum_sel(u32x4 xv, u32x4 rv, u32x4 gv, 
     return out;
 }
 
-template <int DT, bool ADA>
-__device__ __forceinline__ void add_shift(const NormParams& p, int64_t e0, float* y) {
-    if constexpr (ADA) {
-        float sh[Vec<DT>::n];
-        unpack<DT>(ld16((const char*)p.shift + e0 * EltBytes<DT>::n), sh);
-#pragma unroll
-        for (int i = 0; i < Vec<DT>::n; ++i) y[i] += sh[i];
-    }
-}
-
 // Rows of at most G chunks (G in 4..64): G-lane segments, 64 / G rows per wave,
-// four waves per block, one chunk per lane.
+// four waves per block, one chunk per lane.  As in the wide kernel below,
+// every access goes through a buffer resource over the wave's rows (its rows
+// below T), and a lane past the row's last chunk takes an offset outside
+// every range: it reads zeros and its stores are dropped, with no branch;
+// the arguments come in one batch of scalar loads.
 template <int DT, int G, int MODE, bool ADA>
 __global__ __launch_bounds__(256) void rmsnorm_small(NormParams p) {
     constexpr int V = Vec<DT>::n;
     constexpr int EB = EltBytes<DT>::n;
     constexpr int RPW = kWave / G;
+    asm volatile("" ::"s"(p.x), "s"(p.residual), "s"(p.w), "s"(p.T), "s"(p.H), "s"(p.eps),
+                 "s"(p.inv_H), "s"(p.delta));
+    if constexpr (MODE == kNormInPlace) asm volatile("" ::"s"(p.x_out));
+    if constexpr (MODE == kNormFp8) asm volatile("" ::"s"(p.y8), "s"(p.inv_scale));
+    if constexpr (MODE == kNormAmax) asm volatile("" ::"s"(p.amax));
+    if constexpr (ADA) asm volatile("" ::"s"(p.gate), "s"(p.shift));
     const int lane = threadIdx.x & 63;
     const int j = lane % G;
-    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / G;
+    const int64_t row0 = (int64_t)uniform((int)(blockIdx.x * 4u + (threadIdx.x >> 6))) * RPW;
+    const int64_t row = row0 + lane / G;
     const int chunks = p.H / V;
     const bool have = row < p.T && j < chunks;
     const bool has_res = p.residual != nullptr;
-    const int64_t off = (row * p.H + (int64_t)j * V) * EB;
-    u32x4 xv = u32x4{0u, 0u, 0u, 0u}, rv = xv, wv = ones16<DT>(), gv = ones16<DT>();
-    if (have) {
-        xv = ld16_nt((const char*)p.x + off);
-        if (has_res) rv = ld16_nt((const char*)p.residual + off);
-        if (p.w) wv = ld16((const char*)p.w + (int64_t)j * V * EB);
-        if (ADA && p.gate) gv = ld16((const char*)p.gate + (int64_t)j * V * EB);
-    }
+    const int64_t nr = p.T - row0 < RPW ? (p.T - row0 > 0 ? p.T - row0 : 0) : RPW;
+    const uint32_t hb = (uint32_t)p.H * EB;
+    const uint32_t wb = (uint32_t)nr * hb;                 // bytes of the wave's rows
+    const int64_t base = row0 * (int64_t)hb;
+    const uint32_t off = j < chunks ? (uint32_t)((lane / G) * hb + j * 16) : 0xFFFFFFF0u;
+    const __amdgpu_buffer_rsrc_t rx = buf_rsrc((char*)p.x + base, wb);
+    const __amdgpu_buffer_rsrc_t rr =
+        buf_rsrc(has_res ? (char*)p.residual + base : (char*)p.x, has_res ? wb : 0u);
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc((void*)p.w, p.w ? hb : 0u);
+    const u32x4 xv = buf_ld16_nt(rx, off);
+    const u32x4 rv = buf_ld16_nt(rr, off);
+    u32x4 wv = buf_ld16(rw, (uint32_t)j * 16u), gv = ones16<DT>();
+    if constexpr (ADA) gv = buf_ld16(buf_rsrc((void*)p.gate, p.gate ? hb : 0u), (uint32_t)j * 16u);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int d = 0; d < 4; ++d) wv[d] = p.w ? wv[d] : ones16<DT>()[d];
+    if constexpr (ADA)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) gv[d] = p.gate ? gv[d] : ones16<DT>()[d];
     const u32x4 sv = residual_sum<DT, ADA>(xv, rv, gv, has_res);
     float s[V];
     unpack<DT>(sv, s);
-    const float ss = seg_sum<G>(have ? chunk_sumsq<DT>(s) : 0.0f);
+    const float ss = seg_sum<G>(chunk_sumsq<DT>(s));        // lanes past the row add 0
     const float inv = inv_rms(ss, p.inv_H, p.eps);
-    float amax_acc = 0.0f;
-    if (have) {
-        if (has_res && MODE != kNormAmax) st16_nt((char*)p.residual + off, sv);
-        float wf[V], y[V];
-        unpack<DT>(wv, wf);
+    // (no residual: rr has range 0 and the store is dropped)
+    if constexpr (MODE != kNormAmax) buf_st16_nt(rr, off, sv);
+    float wf[V], y[V];
+    unpack<DT>(wv, wf);
 #pragma unroll
-        for (int i = 0; i < V; ++i) y[i] = (s[i] * inv) * (wf[i] + p.delta);
-        add_shift<DT, ADA>(p, (int64_t)j * V, y);
-        emit<DT, MODE>(p, row, (int64_t)j * V, y, amax_acc);
+    for (int i = 0; i < V; ++i) y[i] = (s[i] * inv) * (wf[i] + p.delta);
+    if constexpr (ADA) {
+        float sh[V];
+        unpack<DT>(buf_ld16(buf_rsrc((void*)p.shift, hb), (uint32_t)j * 16u), sh);
+#pragma unroll
+        for (int i = 0; i < V; ++i) y[i] += sh[i];
     }
-    if constexpr (MODE == kNormAmax) {
+    float amax_acc = 0.0f;
+    if constexpr (MODE == kNormInPlace) {
+        buf_st16_nt(buf_rsrc((char*)p.x_out + base, wb), off, pack<DT>(y));
+    } else if constexpr (MODE == kNormFp8) {
+        const __amdgpu_buffer_rsrc_t ry = buf_rsrc(p.y8 + row0 * (int64_t)p.H, (uint32_t)nr * (uint32_t)p.H);
+        const uint32_t o8 = j < chunks ? (uint32_t)((lane / G) * p.H + j * V) : 0xFFFFFFF0u;
+        if constexpr (V == 8) {
+            u32x2 c;
+            c[0] = fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
+                         y[3] * p.inv_scale);
+            c[1] = fp8x4(y[4] * p.inv_scale, y[5] * p.inv_scale, y[6] * p.inv_scale,
+                         y[7] * p.inv_scale);
+            buf_st8_nt(ry, o8, c);
+        } else {
+            buf_st4_nt(ry, o8, fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale,
+                                     y[2] * p.inv_scale, y[3] * p.inv_scale));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) amax_acc = fmaxf(amax_acc, have ? fabsf(y[i]) : 0.0f);
         amax_acc = seg_max<64>(amax_acc);
         if (lane == 0) atomic_max_nonneg(p.amax, amax_acc);
     }
@@ -280,7 +264,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
     float gs[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-        xv[k] = residual_sum_sel<DT, ADA>(xv[k], rv[k], gv[ADA ? k : 0], has_res);   // s
+        xv[k] = residual_sum<DT, ADA>(xv[k], rv[k], gv[ADA ? k : 0], has_res);   // s
         float s[V];
         unpack<DT>(xv[k], s);
         gs[k] = seg_sum<64>(chunk_sumsq<DT>(s));

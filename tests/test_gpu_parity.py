@@ -359,6 +359,14 @@ EDGE_NORM = [
     _ncell(name="partial_chunks_H2504_T2001", H=2504, T=2001, cell=25),
     _ncell(name="partial_fp8_f32_H2500_T3001", dtype=W.F32, H=2500, T=3001, fp8=True, cell=26),
     _ncell(name="wide_no_residual_T2049", residual=False, H=2048, T=2049, cell=27),
+    # the small kernel's buffer ranges: rows past T inside a wave, and lanes
+    # past the row's last chunk (25 chunks on 32 lanes; 3 on 4)
+    _ncell(name="small_H256_T33", H=256, T=33, cell=28),
+    _ncell(name="small_H200_T9", H=200, T=9, cell=29),
+    _ncell(name="small_fp8_H200_T9", H=200, T=9, fp8=True, cell=30),
+    _ncell(name="small_fp8_f32_H12_T7", dtype=W.F32, H=12, T=7, fp8=True, cell=31),
+    _ncell(name="small_no_residual_H200_T9", residual=False, H=200, T=9, cell=32),
+    _ncell(name="small_f16_H24_T65", dtype=W.F16, H=24, T=65, cell=33),
 ]
 
 
