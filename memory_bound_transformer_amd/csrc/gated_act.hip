@@ -40,13 +40,15 @@ struct ActParams {
 
 // e^-a for a >= 0 on the hardware exp2 (v_exp_f32).  v_exp_f32 returns 0
 // for results below the smallest normal float, yet e.g. SiLU(-90) =
-// -90 e^-90 ~ -7e-38 is still a normal bf16; so exponents below -126 are
-// raised by 32 and the result scaled back by the exact power 2^-32.
+// -90 e^-90 ~ -7e-38 is still a normal bf16; so the exponent is halved
+// (exactly: the constant is -log2(e) / 2) and the result squared, which
+// reaches the fp32 subnormals (e^-a for a up to 174 has its square root in
+// the normal range) with no compare or select: two VALU slots beside the
+// exp2, against five for a rescue of exponents below -126 by a select.
+// Error: about twice v_exp_f32's (1 ulp) plus the square's rounding.
 __device__ __forceinline__ float exp_neg(float a) {
-    const float t = a * -1.4426950408889634f;          // -a log2(e)
-    const bool tiny = t < -126.0f;
-    const float e = __builtin_amdgcn_exp2f(tiny ? t + 32.0f : t);
-    return tiny ? e * 2.3283064365386963e-10f : e;
+    const float h = __builtin_amdgcn_exp2f(a * -0.72134752044448170f);
+    return h * h;
 }
 
 template <int DT>
@@ -69,42 +71,6 @@ __device__ __forceinline__ float act_mul(float g, float u) {
         a = g * sigmoid<DT>(2.0f * z);
     }
     return a * u;
-}
-
-// act_mul on the V elements of a chunk, value for value, with exp_neg's
-// rescue of exponents below -126 taken only when some lane of the wave needs
-// it (a wave-uniform branch): the common case costs one compare per element
-// instead of a compare, an add, a multiply and two selects.  Used with two
-// chunks per lane, where it measured 0.1-0.2 us faster at T = 512 (d =
-// 10240); with one chunk per lane the branch cost more than it saved.
-template <int DT, int ACT, int V>
-__device__ __forceinline__ void act_mul_vec(const float* g, const float* u, float* y) {
-    float x[V], t[V], e[V];
-    bool tiny = false;
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-        if constexpr (ACT == 0) {
-            x[i] = g[i];
-        } else {
-            const float z = 0.7978845608f * (g[i] + 0.044715f * g[i] * g[i] * g[i]);
-            x[i] = 2.0f * z;
-        }
-        t[i] = fabsf(x[i]) * -1.4426950408889634f;          // -|x| log2(e)
-        e[i] = __builtin_amdgcn_exp2f(t[i]);
-        tiny = tiny || t[i] < -126.0f;
-    }
-    if (__builtin_amdgcn_ballot_w64(tiny) != 0) {
-#pragma unroll
-        for (int i = 0; i < V; ++i)
-            if (t[i] < -126.0f)
-                e[i] = __builtin_amdgcn_exp2f(t[i] + 32.0f) * 2.3283064365386963e-10f;
-    }
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-        const float r = __builtin_amdgcn_rcpf(1.0f + e[i]);
-        const float sg = x[i] >= 0.0f ? r : e[i] * r;
-        y[i] = (g[i] * sg) * u[i];
-    }
 }
 
 // Vector kernel: d a multiple of Vec<DT>; gate_up and out 16-byte aligned,
@@ -148,12 +114,8 @@ __global__ __launch_bounds__(256) void gated_vec(ActParams p) {
         float g[V], u[V], y[V];
         unpack<DT>(gv[k], g);
         unpack<DT>(uv[k], u);
-        if constexpr (U == 2 && DT != kF32) {
-            act_mul_vec<DT, ACT, V>(g, u, y);
-        } else {
 #pragma unroll
-            for (int i = 0; i < V; ++i) y[i] = act_mul<DT, ACT>(g[i], u[i]);
-        }
+        for (int i = 0; i < V; ++i) y[i] = act_mul<DT, ACT>(g[i], u[i]);
         if constexpr (MODE == kActDtype) {
             buf_st16_nt(ro, ch * 16u, pack<DT>(y));
         } else if constexpr (MODE == kActFp8) {
