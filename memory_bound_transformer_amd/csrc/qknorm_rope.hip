@@ -130,15 +130,18 @@ __device__ __forceinline__ void partner_f32(const float* n, float* nb, int hv, b
 // to their slot.
 //
 // Load order.  The longest dependent chain is position -> cos/sin row, so
-// the position goes out first, then the weights, then the row's chunks, and
+// the weights and the position go out first, then the row's chunks, and
 // the cos/sin loads follow as soon as the position is in, while the chunks
 // are still in flight.  No load sits behind a lane-dependent branch (lanes
-// past the last row read that row again and store nothing; lanes outside
-// the rotated span read the first cos/sin pairs and ignore them), so each
-// wait the compiler places covers only the loads the next step needs.
-// Measured on MI355X, cold, (Q, K) = (24, 4), D = 256, rot_dim 64: with the
-// cos/sin loads behind a wait on the row, the gather cost 0.27 us of 3.54 us
-// at T = 256.
+// past the last row read zeros (dense form) or that row again (general
+// form) and store nothing; lanes outside the rotated span read the first
+// cos/sin pairs and ignore them), so each wait the compiler places covers
+// only the loads the next step needs.  Measured on MI355X, cold, (Q, K) =
+// (24, 4), D = 256, rot_dim 64: with the cos/sin loads behind a wait on the
+// row, the gather cost 0.27 us of 3.54 us at T = 256.  The compiler issues
+// the weight load ahead of the position; a position read through a buffer
+// resource, which it issued ahead of the weights, measured 0.5-0.7 us
+// slower at four chunks per lane ((24, 4) T = 512, (16, 2) T = 1024).
 //
 // ORD, the load order (1 and 2 only with C >= 2; the host picks it from the
 // launch's wave count):
@@ -257,14 +260,24 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     // order 1 stages both rows block-wide instead
     u32x4 wraw{0u, 0u, 0u, 0u};
     if constexpr (!THR) wraw = ld16(wp + (lane % L) * 16);
-    const char* xsrc;
-    if constexpr (GEN)
-        xsrc = src + ((int64_t)t * (is_q ? g.q_in_st : g.k_in_st) + (int64_t)h * p.D) * EB;
-    else
-        xsrc = src + rowc * (int64_t)p.D * EB;
+    // the row's chunks: dense rows through a buffer over the wave's rows (a
+    // scalar base and 32-bit lane offsets, no per-lane 64-bit address
+    // arithmetic; lanes past the last row read zeros, and their results are
+    // not stored); the general form at its own token and head strides
     u32x4 x[C];
+    const uint32_t rofs = (uint32_t)((lane / G) * p.D * EB);   // the lane's row in the wave
+    if constexpr (GEN) {
+        const char* xsrc =
+            src + ((int64_t)t * (is_q ? g.q_in_st : g.k_in_st) + (int64_t)h * p.D) * EB;
 #pragma unroll
-    for (int k = 0; k < C; ++k) x[k] = ld16_nt(xsrc + (k * G + j) * 16);
+        for (int k = 0; k < C; ++k) x[k] = ld16_nt(xsrc + (k * G + j) * 16);
+    } else {
+        const int64_t lrows = (nrows - row0 < RPW) ? nrows - row0 : RPW;   // >= 1
+        const __amdgpu_buffer_rsrc_t wsrc =
+            buf_rsrc((void*)(src + row0 * (int64_t)p.D * EB), (uint32_t)(lrows * p.D * EB));
+#pragma unroll
+        for (int k = 0; k < C; ++k) x[k] = buf_ld16_nt(wsrc, rofs + (uint32_t)((k * G + j) * 16));
+    }
     // An empty asm that may touch memory: the loads above cannot be moved
     // below it (to their first use), and it emits no instruction or wait.
     // The sched_barrier keeps arithmetic on their results (the position
@@ -410,7 +423,6 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
     const int64_t wrows = spare ? 0 : (nrows - row0 < RPW) ? nrows - row0 : RPW;
     const __amdgpu_buffer_rsrc_t wdst =
         buf_rsrc(dst + row0 * (int64_t)p.D * EB, (uint32_t)(wrows * p.D * EB));
-    const uint32_t rofs = (uint32_t)((lane / G) * p.D * EB);
 #pragma unroll
     for (int k = 0; k < C; ++k) {
         float f[V], n[V];
