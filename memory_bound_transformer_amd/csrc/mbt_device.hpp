@@ -197,7 +197,10 @@ __device__ __forceinline__ float round_trip(float v) {
 // NaN; the hardware conversion then rounds to nearest-even (subnormals
 // included).  Two values -> 16 bits; `hi` selects the upper half of `old`.
 __device__ __forceinline__ float fp8_clamp(float v) {
-    return (v != v) ? v : __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+    // IEEE 754-2019 minimum / maximum propagate a NaN (gfx950's
+    // v_minimum3_f32 / v_maximum3_f32): two instructions, against a v_med3
+    // (which does not return a NaN operand) plus a compare and a select
+    return __builtin_elementwise_maximum(__builtin_elementwise_minimum(v, 448.0f), -448.0f);
 }
 __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(a), fp8_clamp(b), 0, false);

@@ -495,13 +495,20 @@ def test_quantize_fp8_exhaustive(mbt, orc):
                         np.nextafter(mids, np.float32(-np.inf)),
                         np.float32([448.0, 449.0, 464.0, 480.0, 1e30, np.inf, -np.inf,
                                     -1e30, 0.0, -0.0, 2 ** -10, 2 ** -11, 1e-40, np.nan]),
+                        # NaNs of both signs, quiet and signalling payloads
+                        np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF800001, 0x7FFFFFFF,
+                                  0xFFFFFFFF], dtype=np.uint32).view(np.float32),
                         rnd]).astype(np.float32)
     for inv_scale in (1.0, 3.0):
         y = mbt.quantize_fp8(torch.from_numpy(x).to(DEV), inv_scale).cpu().numpy()
         yo = orc.quantize_fp8(x, inv_scale)
         nan = np.isnan(x)
         C.check_bitwise(y[~nan], yo[~nan], label=f"quantize inv_scale={inv_scale}")
-        assert np.all((y[nan] & 0x7F) == 0x7F)
+        # NaN stays NaN.  Both e4m3fn NaN codes (0x7F, 0xFF) denote NaN and a
+        # NaN's sign carries no information: the oracle keeps the input's
+        # sign, gfx950's conversion gives 0xFF for every NaN, and either is
+        # accepted
+        assert np.all((y[nan] & 0x7F) == 0x7F) and np.all((yo[nan] & 0x7F) == 0x7F)
     # odd length at a 4-byte offset: the scalar path
     xt = torch.from_numpy(x[:1002].copy()).to(DEV)
     y = mbt.quantize_fp8(xt[1:1002], 1.0).cpu().numpy()
