@@ -254,7 +254,8 @@ MBT_API mbt_status mbt_fused_add_rmsnorm(void* x, void* residual, const void* w,
  * in the same pass with a scale fixed ahead of time, instead of an amax
  * reduction and a separate quantize kernel.
  *   y_i = E4M3FN(((s_i * inv) * (w_i + weight_offset)) * inv_scale)
- * E4M3FN rounds to nearest-even and saturates to +-448 (NaN stays NaN).
+ * E4M3FN rounds to nearest-even and saturates to +-448; a NaN gives a NaN
+ * code (0xFF on gfx950, whatever the input NaN's sign).
  *
  *  x        [T][H] dtype  read only
  *  residual [T][H] dtype  read, then overwritten with s; may be NULL
