@@ -75,6 +75,13 @@ __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off
 __device__ __forceinline__ u32x4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
 }
+// 8-byte loads through a buffer resource (same range rule).
+__device__ __forceinline__ u32x2 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_ld8_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 2);
+}
 // 8- and 4-byte nontemporal stores through a buffer resource (packed FP8).
 __device__ __forceinline__ void buf_st8_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 2);
@@ -219,6 +226,7 @@ constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror: lane i <- 7 - i (in 8)
 constexpr int kDppMirror = 0x140;     // row_mirror: lane i <- 15 - i (in 16)
+constexpr int kDppQuadEven = 0xA0;    // quad_perm [0,0,2,2]: odd lanes take the even lane
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

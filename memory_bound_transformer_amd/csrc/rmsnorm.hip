@@ -338,6 +338,104 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
     }
 }
 
+// Half-chunk lanes: 16-bit rows of 65 to 256 chunks at decode widths.  With
+// few rows most SIMDs are idle and a wave's arithmetic is its latency (each
+// VALU instruction issues over 4 cycles), so each lane takes half a 16-byte
+// chunk (8 bytes, 4 elements) and a row takes twice the waves: at most 8,
+// two per SIMD of the row's CU (101 VALU instructions per wave against 168
+// for norm -> FP8).  Measured on MI355X, cold, bf16: norm -> FP8 H = 2048
+// T = 1 / 128 2.09 / 2.57 -> 2.00 / 2.46 us; residual norm H = 1024 T = 1 /
+// 128 1.97 / 2.39 -> 1.78 / 2.16 us.  At H = 2560 (ten waves on one CU) it
+// measured no faster, so wider rows keep one chunk per lane.  The sums are
+// the same bits as the other kernels': a chunk's FMA chain runs through its
+// even lane (first four elements) and continues in the odd lane from the
+// even lane's partial (one DPP move); with even lanes contributing zeros, a
+// wave's 64-lane tree is the balanced tree over its 32 chunks, and the group
+// tree's last level (a group's two 32-chunk halves) and the tree over groups
+// are the tree over the waves' sums.  One row per block, one wave per 32
+// chunks (p.wpr waves, at most 8).
+template <int DT, int MODE>
+__global__ __launch_bounds__(1024) void rmsnorm_half(NormParams p) {
+    static_assert(DT != kF32, "16-bit dtypes");
+    constexpr int EB = 2;
+    __shared__ float hsum[8];
+    asm volatile("" ::"s"(p.x), "s"(p.residual), "s"(p.w), "s"(p.H), "s"(p.eps), "s"(p.inv_H),
+                 "s"(p.delta), "s"(p.wpr));
+    if constexpr (MODE == kNormInPlace) asm volatile("" ::"s"(p.x_out));
+    if constexpr (MODE == kNormFp8) asm volatile("" ::"s"(p.y8), "s"(p.inv_scale));
+    if constexpr (MODE == kNormAmax) asm volatile("" ::"s"(p.amax));
+    const int wave = uniform((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+    const int64_t row = blockIdx.x;
+    const int chunks = p.H / 8;
+    const bool has_res = p.residual != nullptr, has_w = p.w != nullptr;
+    const uint32_t hb = (uint32_t)p.H * EB;
+    const int64_t ro = row * (int64_t)hb;
+    const __amdgpu_buffer_rsrc_t rx = buf_rsrc((char*)p.x + ro, hb);
+    const __amdgpu_buffer_rsrc_t rr =
+        buf_rsrc(has_res ? (char*)p.residual + ro : (char*)p.x, has_res ? hb : 0u);
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc((void*)p.w, has_w ? hb : 0u);
+    const uint32_t hc = (uint32_t)(wave * kWave + lane);     // half-chunk index
+    const uint32_t off = hc * 8u;
+    const u32x2 xv = buf_ld8_nt(rx, off);
+    const u32x2 rv = buf_ld8_nt(rr, off);
+    u32x2 wv = buf_ld8(rw, off);
+    asm volatile("" ::: "memory");
+    const uint32_t one = ones16<DT>()[0];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) wv[d] = has_w ? wv[d] : one;
+
+    // s = R(x + r), or x itself without a residual
+    u32x2 sv;
+    {
+        u32x4 x4{xv[0], xv[1], 0u, 0u}, r4{rv[0], rv[1], 0u, 0u};
+        float a[8], b[8];
+        unpack<DT>(x4, a);
+        unpack<DT>(r4, b);
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const uint32_t sum = pack2<DT>(a[2 * d] + b[2 * d], a[2 * d + 1] + b[2 * d + 1]);
+            sv[d] = has_res ? sum : xv[d];
+        }
+    }
+    float s[8];
+    unpack<DT>(u32x4{sv[0], sv[1], 0u, 0u}, s);
+    // the chunk's chain: even lanes the first four elements, odd lanes the
+    // last four from their partner's partial
+    float pch = s[0] * s[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) pch = __builtin_fmaf(s[i], s[i], pch);
+    float q = dpp<kDppQuadEven>(pch);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q = __builtin_fmaf(s[i], s[i], q);
+    const float hs = seg_sum<64>((lane & 1) ? q : 0.0f);     // the wave's 32 chunks
+    if (lane == 0) hsum[wave] = hs;
+    __syncthreads();
+    const float ss = seg_sum<64>(lane < p.wpr ? hsum[lane] : 0.0f);
+    const float inv = inv_rms(ss, p.inv_H, p.eps);
+
+    // (no residual: rr has range 0 and the store is dropped)
+    if constexpr (MODE != kNormAmax) buf_st8_nt(rr, off, sv);
+    float wf[8], y[4];
+    unpack<DT>(u32x4{wv[0], wv[1], 0u, 0u}, wf);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = (s[i] * inv) * (wf[i] + p.delta);
+    if constexpr (MODE == kNormInPlace) {
+        const u32x2 o{pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3])};
+        buf_st8_nt(buf_rsrc((char*)p.x_out + ro, hb), off, o);
+    } else if constexpr (MODE == kNormFp8) {
+        buf_st4_nt(buf_rsrc(p.y8 + row * (int64_t)p.H, (uint32_t)p.H), hc * 4u,
+                   fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
+                         y[3] * p.inv_scale));
+    } else {
+        const bool valid = (int)(hc >> 1) < chunks;
+        float amax_acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) amax_acc = fmaxf(amax_acc, valid ? fabsf(y[i]) : 0.0f);
+        amax_acc = seg_max<64>(amax_acc);
+        if (lane == 0) atomic_max_nonneg(p.amax, amax_acc);
+    }
+}
+
 // Scalar kernel: any H and element-aligned pointers; one 256-thread block per
 // row.  Pass 1: wave (g % 4) forms group g's chunk chains (Vec<DT> elements
 // each, scalar loads) and its 64-lane tree; the group sums meet in LDS (up to
@@ -416,6 +514,13 @@ int env_int(const char* name, int dflt) {
     return e ? atoi(e) : dflt;
 }
 
+// Half-chunk lanes (rows of at most four 64-chunk groups) while the launch
+// has at most this many waves (one per SIMD of 256 CUs).
+int tun_half_waves() {
+    static const int v = env_int("MBT_NORM_HALF_WAVES", 1024);
+    return v;
+}
+
 int pick_wpr(int64_t T, int chunks) {
     static const int forced = env_int("MBT_NORM_WPR", 0);
     static const int wide_rows = env_int("MBT_NORM_WIDE_CHUNKS", 8192);
@@ -473,6 +578,15 @@ hipError_t launch_mode(const NormArgs& a, hipStream_t s) {
         if (chunks <= 16) return launch_small<DT, MODE, ADA, 16>(p, s);
         if (chunks <= 32) return launch_small<DT, MODE, ADA, 32>(p, s);
         return launch_small<DT, MODE, ADA, 64>(p, s);
+    }
+    if (vec && DT != kF32 && !ADA) {
+        const int per64 = (chunks + kWave - 1) / kWave;
+        if (per64 <= 4 && a.T * 2 * per64 <= tun_half_waves()) {
+            p.wpr = 2 * per64;
+            hipLaunchKernelGGL((rmsnorm_half<DT == kF32 ? kBF16 : DT, MODE>), dim3((uint32_t)a.T),
+                               dim3(kWave * p.wpr), 0, s, p);
+            return hipGetLastError();
+        }
     }
     if (vec) {
         p.wpr = pick_wpr(a.T, chunks);

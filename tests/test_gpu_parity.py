@@ -367,6 +367,13 @@ EDGE_NORM = [
     _ncell(name="small_fp8_f32_H12_T7", dtype=W.F32, H=12, T=7, fp8=True, cell=31),
     _ncell(name="small_no_residual_H200_T9", residual=False, H=200, T=9, cell=32),
     _ncell(name="small_f16_H24_T65", dtype=W.F16, H=24, T=65, cell=33),
+    # half-chunk lanes: a last wave partly past the row (250 chunks on 256
+    # half-chunk pairs), three groups (six waves), and no residual
+    _ncell(name="half_H2000_T5", H=2000, T=5, cell=34),
+    _ncell(name="half_fp8_H1032_T3", H=1032, T=3, fp8=True, cell=35),
+    _ncell(name="half_f16_no_residual_H2048_T64", dtype=W.F16, residual=False, H=2048, T=64,
+           cell=36),
+    _ncell(name="half_noweight_fp8_H2048_T128", weight=False, fp8=True, H=2048, T=128, cell=37),
 ]
 
 

@@ -154,11 +154,11 @@ def test_prologue_alignment_invariant(mbt, cell):
 
 
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
-@pytest.mark.parametrize("H", [256, 1024, 2560, 6144])
+@pytest.mark.parametrize("H", [256, 1024, 2048, 2560, 6144])
 def test_norm_shape_invariant(mbt, dtype, H):
-    """A row's output does not depend on how many rows share the launch (one
-    chunk per lane at small widths, up to six at large ones) or on alignment
-    (vector vs scalar kernel)."""
+    """A row's output does not depend on how many rows share the launch (half
+    a chunk or one chunk per lane at small widths, up to six at large ones)
+    or on alignment (vector vs scalar kernel)."""
     big_T = max(64, (1 << 16) // max(1, H * (4 if dtype == W.F32 else 2) // 1024))
     c = W.NormCell(name="inv", config=94, cell=H, T=big_T, H=H, dtype=dtype, weight_offset=1,
                    w_mean=0.0, w_std=0.05)
