@@ -154,14 +154,15 @@ def test_prologue_edges(mbt, orc, cell):
     check_prologue_cell(mbt, orc, cell)
 
 
-@pytest.mark.parametrize("T", [1024, 2048])
-def test_prologue_width_invariant(mbt, T):
+@pytest.mark.parametrize("T,layout", [(1024, W.ROTATE_HALF), (2048, W.ROTATE_HALF),
+                                      (2048, W.INTERLEAVED)])
+def test_prologue_width_invariant(mbt, T, layout):
     """A prefill-width launch (chunked rows, whole-block load order) and the
     same tokens in 16-token launches (one chunk per lane, early cos/sin
     order) give identical bits: the reduction tree and the rounding do not
     depend on the launch shape."""
     cell = [c for c in W.config3_cells()
-            if c.dtype == W.BF16 and c.Q == 24 and c.T == T and c.layout == W.ROTATE_HALF][0]
+            if c.dtype == W.BF16 and c.Q == 24 and c.T == T and c.layout == layout][0]
     i = cell.inputs()
     dt = cell.dtype
     q, k = dev(i["q"], dt), dev(i["k"], dt)
