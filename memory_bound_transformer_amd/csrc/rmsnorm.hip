@@ -27,7 +27,9 @@
 //    per lane: no barrier.
 //  * Wider rows are spread over WPR waves of NCH chunks per lane (one chunk
 //    per lane at decode widths, measured best); each 64-chunk group reduces
-//    inside a wave with DPP and the group sums combine through LDS.
+//    inside a wave with DPP and the group sums combine through LDS.  16-bit
+//    rows of up to 256 chunks at decode widths take half a chunk per lane
+//    (twice the waves, half the arithmetic per wave, the same bits).
 //  * The sum of squares is the same fixed tree in every kernel: an FMA chain
 //    inside each chunk, then a balanced tree over the chunk index padded with
 //    zeros to a power of two.  The result therefore does not depend on the
