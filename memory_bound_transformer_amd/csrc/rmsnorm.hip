@@ -28,7 +28,7 @@
 //  * Wider rows are spread over WPR waves of NCH chunks per lane (one chunk
 //    per lane at decode widths, measured best); each 64-chunk group reduces
 //    inside a wave with DPP and the group sums combine through LDS.  16-bit
-//    rows of up to 256 chunks at decode widths take half a chunk per lane
+//    rows of up to 256 chunks take half a chunk per lane up to 4096 waves
 //    (twice the waves, half the arithmetic per wave, the same bits).
 //  * The sum of squares is the same fixed tree in every kernel: an FMA chain
 //    inside each chunk, then a balanced tree over the chunk index padded with
@@ -340,12 +340,12 @@ __global__ __launch_bounds__(1024) void rmsnorm_vec(NormParams p) {
     }
 }
 
-// Half-chunk lanes: 16-bit rows of 65 to 256 chunks at decode widths.  With
-// few rows most SIMDs are idle and a wave's arithmetic is its latency (each
-// VALU instruction issues over 4 cycles), so each lane takes half a 16-byte
-// chunk (8 bytes, 4 elements) and a row takes twice the waves: at most 8,
-// two per SIMD of the row's CU (101 VALU instructions per wave against 168
-// for norm -> FP8).  Measured on MI355X, cold, bf16: norm -> FP8 H = 2048
+// Half-chunk lanes: 16-bit rows of 65 to 256 chunks up to a few thousand
+// waves.  With few rows most SIMDs are idle and a wave's arithmetic is its
+// latency (each VALU instruction issues over 4 cycles), so each lane takes
+// half a 16-byte chunk (8 bytes, 4 elements) and a row takes twice the
+// waves: at most 8, two per SIMD of the row's CU (101 VALU instructions per
+// wave against 168 for norm -> FP8).  Measured on MI355X, cold, bf16: norm -> FP8 H = 2048
 // T = 1 / 128 2.09 / 2.57 -> 2.00 / 2.46 us; residual norm H = 1024 T = 1 /
 // 128 1.97 / 2.39 -> 1.78 / 2.16 us.  At H = 2560 (ten waves on one CU) it
 // measured no faster, so wider rows keep one chunk per lane.  The sums are
@@ -517,9 +517,13 @@ int env_int(const char* name, int dflt) {
 }
 
 // Half-chunk lanes (rows of at most four 64-chunk groups) while the launch
-// has at most this many waves (one per SIMD of 256 CUs).
+// has at most this many waves (four per SIMD of 256 CUs).  Measured on
+// MI355X, cold, bf16: up to this bound half-chunk lanes were faster at every
+// width tried (norm -> FP8 H = 2048 T = 256 / 512 2.74 / 3.15 -> 2.61 / 3.07
+// us; H = 1024 T = 1024 3.16 -> 2.96 us), above it slower (H = 2048 T = 1024
+// 4.03 -> 4.13 us).
 int tun_half_waves() {
-    static const int v = env_int("MBT_NORM_HALF_WAVES", 1024);
+    static const int v = env_int("MBT_NORM_HALF_WAVES", 4096);
     return v;
 }
 
