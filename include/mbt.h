@@ -43,7 +43,8 @@
  *    process, override the thresholds for sweeps (MBT_QK_C_WAVES,
  *    MBT_QK_C_MAX, MBT_QK_MID_WAVES_LO, MBT_QK_THR_WAVES_LO,
  *    MBT_QK_THR_WAVES_HI, MBT_NORM_WPR, MBT_NORM_WIDE_CHUNKS,
- *    MBT_NORM_HALF_WAVES, MBT_ACT_U, MBT_ACT_U2_CHUNKS); every shape gives
+ *    MBT_NORM_HALF_WAVES, MBT_ACT_U, MBT_ACT_U2_CHUNKS,
+ *    MBT_ACT_HALF_WAVES); every shape gives
  *    the same bits, so they change timing only.
  */
 #ifndef MBT_H

@@ -460,6 +460,10 @@ EDGE_ACT = [
     _acell(name="odd_fp8", d=333, fp8=True, cell=6),
     _acell(name="wide_std", x_std=8.0, act=W.GELU_TANH, cell=7),
     _acell(name="T600", T=600, d=4096, cell=8),
+    # half-chunk lanes: a last block partly past d, fp16, and the
+    # calibration amax of a narrow launch
+    _acell(name="half_partial_d1000", d=1000, T=3, cell=9),
+    _acell(name="half_f16_d2056", dtype=W.F16, d=2056, T=7, act=W.GELU_TANH, cell=10),
 ]
 
 
@@ -474,11 +478,12 @@ def test_act_unaligned(mbt, orc, dtype):
                    offset=1)
 
 
-@pytest.mark.parametrize("rows", [1, 50], ids=["one_chunk_per_lane", "two_chunks_per_lane"])
+@pytest.mark.parametrize("rows", [1, 20, 50],
+                         ids=["half_chunk_per_lane", "one_chunk_per_lane", "two_chunks_per_lane"])
 def test_act_exhaustive_bf16_gate(mbt, orc, rows):
     """Every finite bf16 gate value with up = 1: GPU vs oracle, <= 1 ulp.
-    50 copies of the row make the launch wide enough for two chunks per
-    lane, whose exponent rescue is taken per wave."""
+    One row is a narrow launch (half a chunk per lane); 20 and 50 copies of
+    the row make it wide enough for one and two chunks per lane."""
     bits = np.arange(65536, dtype=np.uint16)
     keep = np.isfinite(W.bits_to_f32(bits, W.BF16))
     bits = bits[keep]
