@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle on one
 MI355X: every configuration cell at its full size, plus edge cases.
 
-Marked `gpu`; run on the GPU machine with
+Marked `gpu`; run on a machine with an MI355X with
     python -u -m pytest tests -m gpu -x -v --timeout 120 --timeout-method thread
 """
 import numpy as np
