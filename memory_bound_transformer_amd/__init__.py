@@ -242,7 +242,16 @@ def _token_stride(t, name):
         raise ValueError(f"{name} must be [T, heads, head_dim]")
     if t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != t.shape[2]):
         raise ValueError(f"{name}: the heads of one token must be contiguous")
-    return t.stride(0) if t.shape[0] > 1 else t.shape[1] * t.shape[2]
+    row = t.shape[1] * t.shape[2]
+    if t.shape[0] <= 1:
+        return row
+    # A broadcast (expand()ed) view has token stride 0, and the C ABI reads
+    # 0 as "dense": it would then address T rows where the allocation holds
+    # one.  Any stride below a token's row would make tokens overlap.
+    if row and t.stride(0) < row:
+        raise ValueError(f"{name}: token stride {t.stride(0)} is below one token's "
+                         f"{row} elements (a broadcast or overlapping view)")
+    return t.stride(0)
 
 
 def qknorm_rope_ex(q_in, k_in, w_q, w_k, cos_sin, pos, rot_dim, eps=1e-6, weight_offset=0,

@@ -68,3 +68,24 @@ def test_heads_and_strides():
         mbt._heads3(torch.zeros(4, 8), "q")
     with pytest.raises(ValueError):
         mbt._token_stride(qkv[:, :, :4], "q")           # heads not contiguous
+
+
+def test_broadcast_and_overlapping_views_refused():
+    """A broadcast (expand()ed) [T, heads, D] view has token stride 0, which
+    the C ABI reads as "dense": it would address T rows of an allocation
+    holding one.  Overlapping tokens are refused the same way."""
+    one = torch.zeros(1, 6, 8)
+    wide = one.expand(5, 6, 8)
+    assert wide.stride(0) == 0
+    with pytest.raises(ValueError, match="token stride"):
+        mbt._token_stride(wide, "q_in")
+    base = torch.zeros(200)
+    overlap = base.as_strided((4, 6, 8), (40, 8, 1))     # tokens 40 apart, rows of 48
+    with pytest.raises(ValueError, match="token stride"):
+        mbt._token_stride(overlap, "q_out")
+    # a single token needs no stride; a padded one keeps its own
+    assert mbt._token_stride(one.expand(1, 6, 8), "q") == 48
+    assert mbt._token_stride(base.as_strided((3, 6, 8), (50, 8, 1)), "q") == 50
+    # no heads: nothing is addressed, so any stride passes
+    mbt._token_stride(torch.zeros(4, 0, 8), "k")
+    mbt._token_stride(torch.zeros(1, 0, 8).expand(4, 0, 8), "k")

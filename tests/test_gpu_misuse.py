@@ -40,6 +40,11 @@ def test_prologue_refusals(mbt):
         mbt.qkv_norm_rope_cache(qkv, w, w, cs, pos, pos[:2], z(8, 2, 128), z(8, 2, 128), 6, 64)
     with pytest.raises(ValueError):
         mbt.qkv_norm_rope_cache(qkv, w, w, cs, pos, pos, z(8, 2, 128), z(7, 2, 128), 6, 64)
+    # broadcast views: token stride 0 would address T rows of one
+    with pytest.raises(ValueError, match="token stride"):
+        mbt.qknorm_rope_ex(z(1, 6, 128).expand(4, 6, 128), k, w, w, cs, pos, 64)
+    with pytest.raises(ValueError, match="token stride"):
+        mbt.qknorm_rope_ex(q, k, w, w, cs, pos, 64, k_out=z(1, 2, 128).expand(4, 2, 128))
     # still healthy
     qo, ko = mbt.qknorm_rope(q, k, w, w, cs, pos, 64)
     torch.cuda.synchronize()
