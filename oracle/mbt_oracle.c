@@ -232,6 +232,19 @@ static float apply_weight(float xn, const void* w, int64_t i, int32_t dtype, int
 #endif
 }
 
+/* The value an FP8 epilogue (or its calibration pass) consumes: the fp32
+ * result itself, quantized once (FlashRT optimization details, static FP8:
+ * the fused kernels go from the fp32 value straight to the 8-bit code), never
+ * its copy already rounded to the I/O dtype.  `site` names the epilogue for
+ * the planted-mistake switch. */
+static float fp8_source(float v, int32_t dtype, int site) {
+#if MBT_ORACLE_MUTATION >= 17 && MBT_ORACLE_MUTATION <= 22
+    if (site == MBT_ORACLE_MUTATION) return rounded(v, dtype); /* planted: double rounding */
+#endif
+    (void)dtype; (void)site;
+    return v;
+}
+
 int mbt_ref_rmsnorm_rows(const void* x, void* y, const void* w, int64_t rows,
                          int32_t D, float eps, int32_t weight_offset,
                          int32_t dtype) {
@@ -470,7 +483,7 @@ int mbt_ref_fused_add_rmsnorm_fp8(const void* x, void* residual, const void* w,
         residual_sum(x, residual, t, H, dtype, 1, s);
         float inv = inv_rms(s, H, 0, eps);
         for (int32_t i = 0; i < H; i++) {
-            float v = apply_weight(s[i] * inv, w, i, dtype, weight_offset);
+            float v = fp8_source(apply_weight(s[i] * inv, w, i, dtype, weight_offset), dtype, 17);
             y[t * H + i] = mbt_ref_f32_to_e4m3fn(v * inv_scale);
         }
     }
@@ -490,7 +503,8 @@ float mbt_ref_fused_add_rmsnorm_amax(const void* x, const void* residual,
         residual_sum(x, (void*)residual, t, H, dtype, 0, s);
         float inv = inv_rms(s, H, 0, eps);
         for (int32_t i = 0; i < H; i++) {
-            float v = fabsf(apply_weight(s[i] * inv, w, i, dtype, weight_offset));
+            float v = fabsf(fp8_source(apply_weight(s[i] * inv, w, i, dtype, weight_offset),
+                                       dtype, 18));
             if (v > amax) amax = v;
         }
     }
@@ -555,8 +569,10 @@ static float adarms(void* x, void* residual, const void* gate, const void* scale
         for (int32_t i = 0; i < H; i++) {
             float m = modulate(s[i] * inv, scale, shift, i, dtype);
             if (mode == 0) st(x, t * H + i, dtype, m);
-            else if (mode == 1) y[t * H + i] = mbt_ref_f32_to_e4m3fn(m * inv_scale);
-            else if (fabsf(m) > amax) amax = fabsf(m);
+            else if (mode == 1)
+                y[t * H + i] = mbt_ref_f32_to_e4m3fn(fp8_source(m, dtype, 19) * inv_scale);
+            else if (fabsf(fp8_source(m, dtype, 20)) > amax)
+                amax = fabsf(fp8_source(m, dtype, 20));
         }
     }
     free(s);
@@ -635,7 +651,8 @@ int mbt_ref_gated_act_fp8(const void* gate_up, uint8_t* out, float inv_scale,
         for (int32_t j = 0; j < d; j++) {
             float g = ld(gate_up, t * 2 * (int64_t)d + j, dtype);
             float u = ld(gate_up, t * 2 * (int64_t)d + d + j, dtype);
-            out[t * (int64_t)d + j] = mbt_ref_f32_to_e4m3fn((act_value(g, act) * u) * inv_scale);
+            float v = fp8_source(act_value(g, act) * u, dtype, 21);
+            out[t * (int64_t)d + j] = mbt_ref_f32_to_e4m3fn(v * inv_scale);
         }
     return 0;
 }
@@ -648,7 +665,7 @@ float mbt_ref_gated_act_amax(const void* gate_up, int64_t T, int32_t d,
         for (int32_t j = 0; j < d; j++) {
             float g = ld(gate_up, t * 2 * (int64_t)d + j, dtype);
             float u = ld(gate_up, t * 2 * (int64_t)d + d + j, dtype);
-            float v = fabsf(act_value(g, act) * u);
+            float v = fabsf(fp8_source(act_value(g, act) * u, dtype, 22));
             if (v > amax) amax = v;
         }
     return amax;

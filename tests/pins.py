@@ -723,6 +723,126 @@ def pin_act_fp8(orc):
             assert np.array_equal(y, orc.quantize_fp8(out, np.float32(inv_scale))), "act fp8"
 
 
+# ---------------------------------------------------------------------------
+# FP8 epilogues at 16-bit I/O: one rounding, from the fp32 value
+# ---------------------------------------------------------------------------
+
+def _e4m3_order(codes):
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+def _torch_e4m3(v64, inv_scale):
+    """torch's float8_e4m3fn cast of float64 values times inv_scale, after
+    the saturation to +-448 the epilogues apply (torch's cast does not
+    saturate); a library reference independent of the oracle's encoder."""
+    v = np.clip(v64 * float(inv_scale), -448.0, 448.0)
+    return torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _check_fp8_once(orc, y, amax, v32, v64, inv_scales, codes_for, what):
+    """y: codes at the calibrated scale (inv_scales[0]); v32: the oracle's
+    fp32 value the epilogue must quantize; v64: a float64 library value of
+    the same; codes_for(inv): the epilogue's codes at another scale."""
+    assert amax == float(np.max(np.abs(v32))), f"{what}: amax != max |fp32 value|"
+    for k, inv in enumerate(inv_scales):
+        yk = y if k == 0 else codes_for(inv)
+        assert np.array_equal(yk, orc.quantize_fp8(v32, inv)), \
+            f"{what}: codes != E4M3FN(fp32 value * inv_scale) at inv_scale {inv}"
+        lib = _torch_e4m3(v64, inv)
+        step = np.abs(_e4m3_order(yk) - _e4m3_order(lib))
+        assert step.max() <= 1, f"{what}: codes more than one step from torch's cast"
+        assert np.mean(step > 0) <= 0.01, f"{what}: {np.mean(step > 0):.4f} differ from torch"
+
+
+def pin_fp8_epilogues_16bit(orc):
+    """At bf16 and fp16 I/O the FP8 epilogues quantize the fp32 value of the
+    op once (FlashRT optimization details: the static-FP8 kernels go from the
+    fp32 result straight to the 8-bit code), not that value first rounded to
+    the I/O dtype; the calibration passes take the largest magnitude of the
+    same fp32 value.
+
+    16-bit inputs decode exactly, so the value each epilogue must quantize is
+    the oracle's fp32 path -- pinned to float64 torch by the pins above --
+    run on the decoded inputs (for the residual forms, on the decoded rounded
+    sum, which pin_residual_add ties to eager add).  Required: codes ==
+    E4M3FN(value * inv_scale) bit for bit at three scales (one saturating),
+    amax == max |value| exactly, and, independently of the oracle's encoder,
+    codes within one step of torch's float8_e4m3fn cast of a float64 value.
+    A dtype-rounded source moves about one code in sixteen (bf16) and fails."""
+    g = np.random.default_rng(44)
+    eps = 1e-6
+    for dtype in (BF16, F16):
+        # residual-add RMSNorm, both weight conventions and no weight
+        H = 2048
+        x = W.to_bits(g.standard_normal((8, H)), dtype)
+        r = W.to_bits(g.standard_normal((8, H)), dtype)
+        for delta, w in ((0, W.to_bits(g.standard_normal(H) * 0.05 + 1, dtype)),
+                         (1, W.to_bits(g.standard_normal(H) * 0.05, dtype)), (0, None)):
+            _, s_bits = orc.fused_add_rmsnorm(x, r, w, eps, delta, dtype)
+            sv = f32(s_bits, dtype)
+            wv = None if w is None else f32(w, dtype)
+            v32 = orc.rmsnorm_rows(sv, wv, eps, delta, F32)
+            v64 = F.rms_norm(torch.from_numpy(sv.astype(np.float64)), (H,), weight=None,
+                             eps=float(np.float32(eps))).numpy()
+            if w is not None:
+                v64 = v64 * (wv.astype(np.float64) + delta)
+            amax = orc.fused_add_rmsnorm_amax(x, r, w, eps, delta, dtype)
+            invs = [np.float32(448.0 / amax), np.float32(200.0 / amax),
+                    np.float32(1000.0 / amax)]
+            y, r8 = orc.fused_add_rmsnorm_fp8(x, r, w, invs[0], eps, delta, dtype)
+            assert same_bits(r8, s_bits, dtype), "FP8 norm: residual stream"
+            _check_fp8_once(orc, y, amax, v32, v64, invs,
+                            lambda inv: orc.fused_add_rmsnorm_fp8(x, r, w, inv, eps, delta,
+                                                                  dtype)[0],
+                            f"norm fp8 ({dtype}, delta {delta}, weight {w is not None})")
+        # gated activations
+        d = 1024
+        gu = W.to_bits(g.standard_normal((6, 2 * d)) * 1.5, dtype)
+        guv = f32(gu, dtype)
+        gt = torch.from_numpy(guv[:, :d].astype(np.float64))
+        ut = guv[:, d:].astype(np.float64)
+        for act, lib in ((W.SILU, F.silu(gt).numpy()),
+                         (W.GELU_TANH, F.gelu(gt, approximate="tanh").numpy())):
+            v32 = orc.gated_act(guv, act, F32)
+            amax = orc.gated_act_amax(gu, act, dtype)
+            invs = [np.float32(448.0 / amax), np.float32(100.0 / amax),
+                    np.float32(2000.0 / amax)]
+            y = orc.gated_act_fp8(gu, invs[0], act, dtype)
+            _check_fp8_once(orc, y, amax, v32, lib * ut, invs,
+                            lambda inv: orc.gated_act_fp8(gu, inv, act, dtype),
+                            f"act fp8 ({dtype}, act {act})")
+        # adaptive RMSNorm: gated residual, plain residual, no residual
+        H = 512
+        x = W.to_bits(g.standard_normal((6, H)), dtype)
+        r = W.to_bits(g.standard_normal((6, H)) * 2, dtype)
+        gt_ = W.to_bits(g.standard_normal(H) * 0.3 + 1, dtype)
+        sc = W.to_bits(g.standard_normal(H) * 0.1, dtype)
+        sh = W.to_bits(g.standard_normal(H) * 0.1, dtype)
+        scv, shv = f32(sc, dtype), f32(sh, dtype)
+        for res, gate in ((r, gt_), (r, None), (None, None)):
+            if res is None:
+                s_bits = x
+            else:
+                s_bits = orc.adarms(x, res, gate, sc, sh, eps, dtype)[1]
+            sv = f32(s_bits, dtype)
+            v32 = orc.adarms(sv, None, None, scv, shv, eps, F32)[0]
+            n64 = F.rms_norm(torch.from_numpy(sv.astype(np.float64)), (H,), weight=None,
+                             eps=float(np.float32(eps))).numpy()
+            v64 = n64 * (1.0 + scv.astype(np.float64)) + shv.astype(np.float64)
+            amax = orc.adarms_amax(x, res, gate, sc, sh, eps, dtype)
+            invs = [np.float32(448.0 / amax), np.float32(150.0 / amax),
+                    np.float32(900.0 / amax)]
+            y, r8 = orc.adarms_fp8(x, res, gate, sc, sh, invs[0], eps, dtype)
+            if res is not None:
+                assert same_bits(r8, s_bits, dtype), "FP8 adaptive norm: residual stream"
+            _check_fp8_once(orc, y, amax, v32, v64, invs,
+                            lambda inv: orc.adarms_fp8(x, res, gate, sc, sh, inv, eps,
+                                                       dtype)[0],
+                            f"adarms fp8 ({dtype}, residual {res is not None}, "
+                            f"gate {gate is not None})")
+
+
 ALL_PINS = [
     pin_bf16_converter, pin_f16_converter, pin_e4m3fn_converter,
     pin_rmsnorm_vs_torch, pin_rmsnorm_closed_forms, pin_rmsnorm_bruteforce,
@@ -731,4 +851,5 @@ ALL_PINS = [
     pin_prologue_composition, pin_prologue_constant_head, pin_prologue_round_once,
     pin_residual_add, pin_norm_fp8, pin_quantize_vs_torch,
     pin_act_vs_torch, pin_act_exhaustive_bf16, pin_act_identities, pin_act_fp8,
+    pin_fp8_epilogues_16bit,
 ]

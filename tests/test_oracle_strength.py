@@ -31,6 +31,12 @@ MUTATIONS = {
     14: "single-rounding prologue rounds the norm result before rotating",
     15: "adaptive norm scales by scale instead of 1 + scale",
     16: "adaptive norm ignores the residual gate",
+    17: "norm FP8 epilogue quantizes the dtype-rounded value",
+    18: "norm calibration amax of the dtype-rounded value",
+    19: "adaptive norm FP8 epilogue quantizes the dtype-rounded value",
+    20: "adaptive norm calibration amax of the dtype-rounded value",
+    21: "activation FP8 epilogue quantizes the dtype-rounded value",
+    22: "activation calibration amax of the dtype-rounded value",
 }
 
 # fast pins first: most mutations are caught within a second
