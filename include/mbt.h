@@ -181,8 +181,12 @@ MBT_API mbt_status mbt_qknorm_rope_ex(const void* q_in, const void* k_in, void* 
  *   k_cache[slot[t]]    <- the prologue's key heads of qkv[t][Q : Q + K]
  *   v_cache[slot[t]]    <- qkv[t][Q + K : Q + 2K], copied unchanged
  * A slot outside [0, n_slots) (e.g. -1 for padding) writes no cache row; the
- * token's q_out row is still written.  Two valid tokens must not share a slot
- * (their writes would race).
+ * token's q_out row is still written.  Valid tokens should map to distinct
+ * slots.  Tokens that share one race for its row: the call still succeeds,
+ * every element of that row ends up holding the element of one of those
+ * tokens, and which token's element lands is unspecified (it may differ
+ * from element to element).  The library does not check for shared slots,
+ * since that would need the slot table on the host.
  *
  *  qkv      [T][Q + 2K][head_dim]  dtype  read
  *  q_out    [T][Q][head_dim]       dtype  written (may be NULL when Q == 0)

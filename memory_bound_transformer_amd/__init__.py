@@ -293,7 +293,9 @@ def qkv_norm_rope_cache(qkv, w_q, w_k, cos_sin, pos, slot, k_cache, v_cache, Q, 
                         round_once=False, max_pos=None, stream=None):
     """qkv [T, Q + 2K, D] -> q_out [T, Q, D]; the prologue's key heads and
     the unchanged value heads of token t go to row slot[t] of
-    k_cache / v_cache [n_slots, K, D] (slots outside [0, n_slots): no write)."""
+    k_cache / v_cache [n_slots, K, D] (slots outside [0, n_slots): no write).
+    Tokens sharing a slot race for its row: each element holds one of
+    theirs, which one is unspecified."""
     _dev(qkv, w_q, w_k, cos_sin, pos, slot, k_cache, v_cache, q_out)
     _same_dtype(qkv, w_q, w_k, k_cache, v_cache, q_out)
     if slot.dtype != torch.int64:

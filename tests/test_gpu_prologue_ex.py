@@ -6,12 +6,15 @@
   and all dtypes; and its batch / alignment invariance;
 * mbt_qknorm_rope_ex on strided views (thox-edge-ops v2, section 6: strided
   views; q and k as slices of one fused QKV buffer): out of place, in place
-  inside the buffer and into padded outputs, bit for bit equal to the dense
-  op, with the rest of the buffer untouched;
+  inside the buffer and into padded outputs, against the oracle within the
+  contract's tolerance and bit for bit equal to the dense op, with the rest
+  of the buffer untouched;
 * mbt_qkv_norm_rope_cache (FlashRT's qkv_split_rope_kvcache with the
-  per-head norm; thox-edge-ops v2, section 10, item 4): q_out equals the
-  dense prologue, key rows land at their slots as the dense prologue's
-  key output, value rows land unchanged, invalid slots write nothing.
+  per-head norm; thox-edge-ops v2, section 10, item 4): q_out and the key
+  rows at their slots against the oracle (and bit for bit against the dense
+  prologue), value rows equal to a scatter of the value input by slot,
+  invalid slots write nothing; tokens sharing a slot leave each element of
+  that row equal to one of theirs.
 """
 import numpy as np
 import pytest
@@ -76,6 +79,29 @@ def once(mbt, cell, i, offset=0):
                                 torch.from_numpy(i["pos"]).to(DEV), cell.rot, cell.eps,
                                 cell.weight_offset, cell.layout, round_once=True)
     return host(qo, dt), host(ko, dt)
+
+
+def oracle_check(orc, cell, i, gq, gk, round_once, label, k_rows=None):
+    """The prologue's results against the oracle, by the contract's rules:
+    gq [T, Q, D] bits (or None), gk [T, K, D] bits (or None), or with
+    `k_rows` the key results of those tokens only, in that order."""
+    dt = cell.dtype
+    qo, ko = orc.qknorm_rope(i["q"], i["k"], i["w_q"], i["w_k"], i["cos_sin"], i["pos"],
+                             cell.rot, cell.eps, cell.weight_offset, cell.layout, dt,
+                             max_pos=cell.max_pos, round_once=round_once)
+    qn = orc.rmsnorm_rows(i["q"], i["w_q"], cell.eps, cell.weight_offset, dt)
+    kn = orc.rmsnorm_rows(i["k"], i["w_k"], cell.eps, cell.weight_offset, dt)
+    cs, pos = i["cos_sin"], i["pos"]
+    stats = []
+    if gq is not None and cell.Q:
+        stats.append(C.check_prologue(gq, qo, qn, cs, pos, cell.rot, cell.layout, dt,
+                                      cell.max_pos, label=f"{label} q vs oracle"))
+    if gk is not None and cell.K:
+        if k_rows is not None:
+            ko, kn, pos = ko[k_rows], kn[k_rows], pos[k_rows]
+        stats.append(C.check_prologue(gk, ko, kn, cs, pos, cell.rot, cell.layout, dt,
+                                      cell.max_pos, label=f"{label} k vs oracle"))
+    return stats
 
 
 ONCE_CELLS = [
@@ -180,11 +206,14 @@ STRIDE_CELLS = [
 @pytest.mark.parametrize("pad", [0, 1], ids=["aligned", "odd_stride"])
 @pytest.mark.parametrize("round_once", [False, True], ids=["contract", "once"])
 @pytest.mark.parametrize("cell", STRIDE_CELLS, ids=lambda c: c.name)
-def test_strided_views(mbt, cell, round_once, pad):
-    """pad 0: 16-byte strides (vector kernel); pad 1: odd strides (scalar)."""
+def test_strided_views(mbt, orc, cell, round_once, pad):
+    """pad 0: 16-byte strides (vector kernel); pad 1: odd strides (scalar).
+    Every result is checked against the oracle; the dense op's result, also
+    checked against it, must then match bit for bit."""
     i = cell.inputs()
     dt = cell.dtype
     ref = once(mbt, cell, i) if round_once else dense(mbt, cell, i)
+    oracle_check(orc, cell, i, ref[0], ref[1], round_once, f"{cell.name} dense")
     rows, _ = fused_buffer(i, cell, pad, 1)
     wq, wk = dev(i["w_q"], dt), dev(i["w_k"], dt)
     cs = torch.from_numpy(i["cos_sin"]).to(DEV)
@@ -195,6 +224,9 @@ def test_strided_views(mbt, cell, round_once, pad):
     buf = dev(rows, dt)
     q, k = views(buf, cell)
     qo, ko = mbt.qknorm_rope_ex(q, k, *args, round_once=round_once)
+    st = oracle_check(orc, cell, i, host(qo, dt), host(ko, dt), round_once,
+                      f"{cell.name} strided in")
+    print(f"{cell.name} strided: {st}", flush=True)
     C.check_bitwise(host(qo, dt), ref[0], label=f"{cell.name} strided in q")
     C.check_bitwise(host(ko, dt), ref[1], label=f"{cell.name} strided in k")
     C.check_bitwise(host(buf, dt), rows, label=f"{cell.name} input buffer untouched")
@@ -205,7 +237,11 @@ def test_strided_views(mbt, cell, round_once, pad):
     Q, K, D, T = cell.Q, cell.K, cell.D, cell.T
     want[:, :Q * D] = ref[0].reshape(T, Q * D)
     want[:, Q * D:(Q + K) * D] = ref[1].reshape(T, K * D)
-    C.check_bitwise(host(buf, dt), want, label=f"{cell.name} in place in qkv")
+    got = host(buf, dt)
+    oracle_check(orc, cell, i, got[:, :Q * D].reshape(T, Q, D),
+                 got[:, Q * D:(Q + K) * D].reshape(T, K, D), round_once,
+                 f"{cell.name} in place")
+    C.check_bitwise(got, want, label=f"{cell.name} in place in qkv")
 
     # into padded outputs (token stride (heads + 1) * D + pad)
     qpad = torch.full((T, (Q + 1) * D + pad), 7.0, dtype=buf.dtype, device=DEV)
@@ -214,6 +250,8 @@ def test_strided_views(mbt, cell, round_once, pad):
     mbt.qknorm_rope_ex(q, k, *args, q_out=qpad[:, :Q * D].unflatten(1, (Q, D)),
                        k_out=kpad[:, :K * D].unflatten(1, (K, D)), round_once=round_once)
     gq, gk = host(qpad, dt), host(kpad, dt)
+    oracle_check(orc, cell, i, gq[:, :Q * D].reshape(T, Q, D), gk[:, :K * D].reshape(T, K, D),
+                 round_once, f"{cell.name} padded out")
     C.check_bitwise(gq[:, :Q * D].reshape(T, Q, D), ref[0], label=f"{cell.name} padded q")
     C.check_bitwise(gk[:, :K * D].reshape(T, K, D), ref[1], label=f"{cell.name} padded k")
     seven = W.to_bits(np.full(1, 7.0), dt)[0]
@@ -245,7 +283,10 @@ CACHE_CELLS = [
 
 @pytest.mark.parametrize("round_once", [False, True], ids=["contract", "once"])
 @pytest.mark.parametrize("cell", CACHE_CELLS, ids=lambda c: c.name)
-def test_qkv_cache(mbt, cell, round_once):
+def test_qkv_cache(mbt, orc, cell, round_once):
+    """q_out and each written key row against the oracle (and bit for bit
+    against the dense prologue); value rows against a numpy scatter of the
+    value input by slot; rows no token maps to keep their sentinel."""
     i = cell.inputs()
     dt, T, Q, K, D = cell.dtype, cell.T, cell.Q, cell.K, cell.D
     ref_q, ref_k = once(mbt, cell, i) if round_once else dense(mbt, cell, i)
@@ -265,13 +306,65 @@ def test_qkv_cache(mbt, cell, round_once):
                                     torch.from_numpy(slot).to(DEV), kc, vc, Q, cell.rot,
                                     cell.eps, cell.weight_offset, cell.layout,
                                     round_once=round_once)
-    if Q:
-        C.check_bitwise(host(q_out, dt), ref_q, label=f"{cell.name} q_out")
+    gq = host(q_out, dt)
     gk, gv = host(kc, dt), host(vc, dt)
     valid = (slot >= 0) & (slot < n_slots)
+    # q_out, and the key row at each written slot, token by token
+    st = oracle_check(orc, cell, i, gq, gk[slot[valid]], round_once, f"{cell.name} cache",
+                      k_rows=np.nonzero(valid)[0])
+    print(f"{cell.name} cache: {st}", flush=True)
+    if Q:
+        C.check_bitwise(gq, ref_q, label=f"{cell.name} q_out")
     C.check_bitwise(gk[slot[valid]], ref_k[valid], label=f"{cell.name} key cache rows")
-    C.check_bitwise(gv[slot[valid]], v[valid], label=f"{cell.name} value cache rows")
+    want_v = np.full_like(gv, sentinel)
+    want_v[slot[valid]] = v[valid]                      # numpy scatter of the value input
+    C.check_bitwise(gv, want_v, label=f"{cell.name} value cache")
     untouched = np.setdiff1d(np.arange(n_slots), slot[valid])
     assert np.all(gk[untouched] == sentinel) and np.all(gv[untouched] == sentinel), \
         "a cache row without a token was written"
     C.check_bitwise(host(qkv, dt).reshape(T, -1), rows, label=f"{cell.name} qkv untouched")
+
+
+@pytest.mark.parametrize("cell", [c for c in CACHE_CELLS
+                                  if c.name in ("cache_bf16_16x2_decode",
+                                                "cache_bf16_prefill_24x4", "cache_f32_d128")],
+                         ids=lambda c: c.name)
+def test_qkv_cache_shared_slots(mbt, orc, cell):
+    """Tokens mapped to one slot race for its row; which token's value lands
+    there is unspecified.  Each element of such a row must still be that
+    element of one of the contending tokens' rows (the dense prologue's key
+    row, itself checked against the oracle here, or the value input), q_out
+    is unaffected, and rows no token maps to keep their sentinel."""
+    i = cell.inputs()
+    dt, T, Q, K, D = cell.dtype, cell.T, cell.Q, cell.K, cell.D
+    ref_q, ref_k = dense(mbt, cell, i)
+    oracle_check(orc, cell, i, ref_q, ref_k, False, f"{cell.name} dense")
+    rows, v = fused_buffer(i, cell, 0, 3)
+    qkv = dev(rows, dt).view(T, Q + 2 * K, D)
+    n_slots = max(4, T // 3)
+    slot = np.random.default_rng([95, cell.cell, 4]).integers(0, n_slots, T).astype(np.int64)
+    assert len(np.unique(slot)) < T, "the case needs shared slots"
+    sentinel = W.to_bits(np.full(1, -3.0), dt)[0]
+    kc = torch.full((n_slots + 2, K, D), -3.0, dtype=qkv.dtype, device=DEV)
+    vc = torch.full((n_slots + 2, K, D), -3.0, dtype=qkv.dtype, device=DEV)
+    q_out = mbt.qkv_norm_rope_cache(qkv, dev(i["w_q"], dt), dev(i["w_k"], dt),
+                                    torch.from_numpy(i["cos_sin"]).to(DEV),
+                                    torch.from_numpy(i["pos"]).to(DEV),
+                                    torch.from_numpy(slot).to(DEV), kc, vc, Q, cell.rot,
+                                    cell.eps, cell.weight_offset, cell.layout)
+    C.check_bitwise(host(q_out, dt), ref_q, label=f"{cell.name} q_out")
+    gk, gv = host(kc, dt), host(vc, dt)
+    shared = 0
+    for s in np.unique(slot):
+        toks = np.nonzero(slot == s)[0]
+        shared += len(toks) > 1
+        ok_k = np.zeros((K, D), bool)
+        ok_v = np.zeros((K, D), bool)
+        for t in toks:
+            ok_k |= gk[s] == ref_k[t]
+            ok_v |= gv[s] == v[t]
+        assert ok_k.all(), f"slot {s}: a key element from none of tokens {toks.tolist()}"
+        assert ok_v.all(), f"slot {s}: a value element from none of tokens {toks.tolist()}"
+    untouched = np.setdiff1d(np.arange(n_slots + 2), slot)
+    assert np.all(gk[untouched] == sentinel) and np.all(gv[untouched] == sentinel)
+    print(f"{cell.name}: {shared} shared slots of {len(np.unique(slot))}", flush=True)

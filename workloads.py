@@ -305,13 +305,16 @@ def config3_cells():
                     dtype=dtype, weight_offset=1, w_mean=0.0, w_std=0.05, x_std=2.0,
                     positions="arange"))
                 i += 1
-    for (Q, K) in ((24, 4), (16, 2)):
-        for T in (256, 2048):
-            cells.append(PrologueCell(
-                name=f"interleaved{Q}x{K}_T{T}", config=3, cell=i, T=T, Q=Q, K=K, D=256,
-                rot=256, theta=1e7, layout=INTERLEAVED, dtype=BF16, weight_offset=1,
-                w_mean=0.0, w_std=0.05, x_std=2.0, positions="arange"))
-            i += 1
+    # widths 256 and 2048 first, then 512 and 1024, so each cell keeps the
+    # seed it had before the middle widths were added
+    for widths in ((256, 2048), (512, 1024)):
+        for (Q, K) in ((24, 4), (16, 2)):
+            for T in widths:
+                cells.append(PrologueCell(
+                    name=f"interleaved{Q}x{K}_T{T}", config=3, cell=i, T=T, Q=Q, K=K, D=256,
+                    rot=256, theta=1e7, layout=INTERLEAVED, dtype=BF16, weight_offset=1,
+                    w_mean=0.0, w_std=0.05, x_std=2.0, positions="arange"))
+                i += 1
     return cells
 
 
