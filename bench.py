@@ -1,37 +1,43 @@
-"""Throughput of the fused memory-bound decoder path on one MI355X.
+"""Throughput of the fused QK-RMSNorm + RoPE prologue on one MI355X, with the
+sibling memory-bound ops measured beside it.
 
-One step = one pass of the whole path over a batch of T synthetic tokens,
-the memory-bound half of a decoder layer with FP8 GEMM inputs:
+Headline step: one launch of the prologue over the widest prefill batch of
+the 256-wide text-head geometry -- (Q, K) = (24, 4) heads, head_dim 256,
+rot_dim 64 (rotate-half), 1 + w weights, theta 1e7, T = 2048 tokens at
+positions 0 .. 2047, bf16 storage with fp32 arithmetic.  Inputs are resident
+in HBM before timing starts.  Each step reads and writes its own slot of a
+buffer ring larger than 1 GiB (five times the 256 MB Infinity Cache), so the
+traffic comes from HBM; graphs captured over the ring are replayed.  W
+untimed steps, then exactly K timed steps between HIP events, with a device
+synchronisation on both sides.  `value` = tokens/s of the K steps; `roofline`
+= the algorithmic bytes of one launch over the average launch time of the
+same K steps, against 8 TB/s.
 
-    residual-add RMSNorm -> e4m3fn      (H = 2048, static scale)
-    fused QK-RMSNorm + RoPE prologue    ((Q, K) = (16, 2), head_dim 256,
-                                         rot_dim 64, 1 + w weight, theta 1e7)
-    residual-add RMSNorm -> e4m3fn      (H = 2048)
-    gated SiLU -> e4m3fn                (gate_up [T, 2 x 10240])
+Also reported: microseconds per call at T = 1 (warm, a graph of 32 calls,
+median of 200 samples: the method of the ninfer PR the text-head shapes come
+from); the fraction of peak of every prefill cell (T >= 256), event-timed and
+from the committed rocprofv3 kernel trace; the decode-width sweep; the
+decode-layer step (norm -> FP8, prologue, norm -> FP8, SiLU -> FP8 at
+T = 128); the residual-norm and activation sweeps; the fused-vs-split route
+comparison; the extended prologue forms; the oracle timed on the host CPU.
 
-in bf16 storage with fp32 arithmetic.  T defaults to 128, the widest decode
-batch of the 256-wide text-head configuration.  Inputs are resident in HBM
-before timing starts.  Each step reads and writes its own slot of a buffer
-ring larger than 1 GiB (four times the 256 MB Infinity Cache), so the timed
-traffic really comes from HBM; the graph of one pass over the ring is
-captured once and replayed.  The FP8 scales come from one calibration pass
-on the GPU (amax entry points) over inputs drawn with another seed.
+    python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-cpu]
 
-Reported on one JSON line: tokens/s of the step, the roofline of the
-dominant kernel (algorithmic bytes / its own average duration, timed with
-HIP events over graphs of back-to-back launches), the oracle timed on the
-host CPU, plus the prologue's own figures: microseconds per call at T = 1
-(warm, graph of 32 calls, the method of the PR the text-head shapes come
-from), decode-width sweep and prefill widths T = 256 .. 2048 (cold).
+Profiling aids (each runs committed code only):
 
-    python bench.py [--steps K] [--warmup W] [--tokens T]
+    python bench.py --only {prologue_prefill|prefill_cells|norm_fp8|prologue|act_fp8}
+    python bench.py --copy-probe BYTES
+    python bench.py --trace-stats TRACE.csv OUT.csv       (no GPU)
+    python bench.py --write-profiles DIR                  (no GPU)
 """
 import argparse
+import csv
 import hashlib
 import json
 import os
 import platform
 import re
+import statistics
 import sys
 import time
 
@@ -40,21 +46,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "QK-norm+RoPE tokens/s & achieved HBM GB/s (% of peak); µs/call at T=1"
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
+INFINITY_CACHE_BYTES = 256 * 2 ** 20
 RING_BYTES = int(1.25 * 2 ** 30)
-# Ring slots per graph: enough buffer sets to cover RING_BYTES (five times the
-# 256 MB Infinity Cache), but at most MAX_SLOTS, so a small call (a decode
-# row) does not become a graph of tens of thousands of launches.  At the
-# cap a ring still spans MAX_SLOTS distinct buffer sets.
+# A graph is captured over one pass of a ring, so its slot count is the
+# graph's node count.  Graphs are kept at or below MAX_SLOTS nodes (see
+# ring_slots).
 MAX_SLOTS = 4096
+# Spin kernel queued ahead of each timed region, so the host has queued the
+# graph's launches before the first timed one starts (cycles of the
+# shader clock: some tens of microseconds).
+GATE_CYCLES = 100_000
 
-
-def ring_slots(nbytes):
-    return max(8, min(MAX_SLOTS, -(-RING_BYTES // max(1, nbytes))))
-
-
-def phase(name):
-    """Progress marker on stderr (the JSON line alone goes to stdout)."""
-    print(f"bench: {name}", file=sys.stderr, flush=True)
 KERNEL_SOURCES = {
     "qknorm_rope": "qknorm_rope.hip",
     "rmsnorm": "rmsnorm.hip",
@@ -62,28 +64,58 @@ KERNEL_SOURCES = {
 }
 
 
+def ring_slots(nbytes, cache_resident_ok=False):
+    """Buffer sets in a ring for a call that moves `nbytes`: enough to cover
+    RING_BYTES, so consecutive calls never find their data in the Infinity
+    Cache.  A call small enough to need more than MAX_SLOTS sets raises,
+    unless the caller accepts a ring of MAX_SLOTS sets and labels its figure
+    with ring_mode() (such a ring can stay resident in the cache)."""
+    need = max(8, -(-RING_BYTES // max(1, nbytes)))
+    if need <= MAX_SLOTS:
+        return need
+    if not cache_resident_ok:
+        raise ValueError(f"a cold ring for {nbytes} B calls needs {need} buffer sets, more "
+                         f"than the {MAX_SLOTS} one captured graph may hold")
+    return MAX_SLOTS
+
+
+def ring_mode(nbytes, R):
+    """How a ring of R buffer sets of nbytes each meets the Infinity Cache."""
+    total = R * nbytes
+    if total >= RING_BYTES:
+        return "cold"
+    return "cache-resident" if total <= INFINITY_CACHE_BYTES else "partly cache-resident"
+
+
+def phase(name):
+    """Progress marker on stderr (the JSON line alone goes to stdout)."""
+    print(f"bench: {name}", file=sys.stderr, flush=True)
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--tokens", type=int, default=128)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="CPU work for the oracle baseline (0 disables it)")
-    ap.add_argument("--no-sweep", action="store_true", help="skip the prologue sweeps")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="headline, T = 1 and the prefill fractions only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", default=None,
-                    help="profiling aid: run one kernel of the step repeatedly "
-                         "(norm_fp8 | prologue | act_fp8), or the prefill prologue "
-                         "(prologue_prefill), and exit")
+                    help="profiling aid: launch one thing repeatedly and exit: "
+                         "prologue_prefill (the headline launch), prefill_cells (every "
+                         "prefill cell in turn), or a kernel of the decode-layer step "
+                         "(norm_fp8 | prologue | act_fp8)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="profiling aid: copy this many bytes with torch 20 times and exit")
+    ap.add_argument("--trace-stats", nargs=2, metavar=("TRACE_CSV", "OUT_CSV"),
+                    help="reduce a rocprofv3 kernel trace to per-launch-size statistics")
+    ap.add_argument("--write-profiles", metavar="DIR",
+                    help="write the profiles/ summaries from a profiling run's outputs")
     return ap.parse_args()
 
 
 def median(xs):
-    xs = sorted(xs)
-    n = len(xs)
-    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return statistics.median(xs)
 
 
 def pct(xs, p):
@@ -91,8 +123,119 @@ def pct(xs, p):
     return xs[min(len(xs) - 1, int(p / 100.0 * len(xs)))]
 
 
-class Step:
-    """Device buffers of the decode-layer step, one slot per ring entry."""
+# ---------------------------------------------------------------------------
+# graphs and timing
+# ---------------------------------------------------------------------------
+
+def capture(torch, fn, n):
+    """A graph of fn(0) .. fn(n - 1), captured on a side stream."""
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def timed_replays(torch, graphs, gate=False):
+    """Elapsed ms of replaying `graphs` (a list) back to back, bracketed by
+    synchronisations and HIP events on the current stream.  gate: a spin
+    kernel goes ahead of the first event, so the launches are queued before
+    the timed region starts and host submission stays outside it."""
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    if gate:
+        torch.cuda._sleep(GATE_CYCLES)
+    a.record()
+    for g in graphs:
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def kernel_time_us(torch, fn, R, launches):
+    """Average duration of one launch: graphs of R back-to-back launches over
+    the ring slots, replayed until `launches` launches are timed."""
+    g = capture(torch, fn, R)
+    timed_replays(torch, [g])                    # warm the graph itself
+    reps = max(1, launches // R)
+    ms = timed_replays(torch, [g] * reps, gate=True)
+    return 1000.0 * ms / (reps * R)
+
+
+class Steps:
+    """Steps fn(slot) over a ring of R slots, each run continuing where the
+    last one stopped, so a slot is reused only after the other R - 1 (a
+    warm-up never leaves the first timed slots in the Infinity Cache).
+    Graphs (one full pass from a start slot, or a shorter run) are captured
+    on first use, before the timed region."""
+
+    def __init__(self, torch, fn, R):
+        self.torch, self.fn, self.R = torch, fn, R
+        self.pos = 0
+        self.graphs = {}
+
+    def _graph(self, start, n):
+        if (start, n) not in self.graphs:
+            self.graphs[(start, n)] = capture(self.torch, lambda j: self.fn(start + j), n)
+        return self.graphs[(start, n)]
+
+    def run(self, n, gate):
+        start = self.pos % self.R
+        graphs = [self._graph(start, self.R)] * (n // self.R)
+        if n % self.R:
+            graphs.append(self._graph(start, n % self.R))
+        self.pos += n
+        return timed_replays(self.torch, graphs, gate=gate)
+
+
+# ---------------------------------------------------------------------------
+# the headline step and the decode-layer step
+# ---------------------------------------------------------------------------
+
+def prefill_cell(W):
+    """The widest prefill cell: (Q, K) = (24, 4), T = 2048, bf16, rotate-half."""
+    return max((c for c in W.config3_cells()
+                if c.dtype == W.BF16 and c.layout == W.ROTATE_HALF),
+               key=lambda c: c.bytes_algorithmic())
+
+
+class Headline:
+    """Device buffers of the headline step: the prologue over the widest
+    prefill cell, out of place, one ring slot per step."""
+
+    def __init__(self, torch, mbt, W):
+        self.mbt = mbt
+        self.cell = c = prefill_cell(W)
+        i = c.inputs()
+        t = lambda bits: W.to_torch(bits, c.dtype, "cuda:0")
+        self.wq, self.wk = t(i["w_q"]), t(i["w_k"])
+        self.cs = torch.from_numpy(i["cos_sin"]).to("cuda:0")
+        self.pos = torch.from_numpy(i["pos"]).to("cuda:0")
+        self.bytes = c.bytes_algorithmic()
+        self.R = ring_slots(self.bytes)
+        q0, k0 = t(i["q"]), t(i["k"])
+        self.ring = [(q0.clone(), k0.clone(), torch.empty_like(q0), torch.empty_like(k0))
+                     for _ in range(self.R)]
+        torch.cuda.synchronize()
+
+    def step(self, j):
+        c = self.cell
+        q, k, qo, ko = self.ring[j % self.R]
+        self.mbt.qknorm_rope(q, k, self.wq, self.wk, self.cs, self.pos, c.rot, c.eps,
+                             c.weight_offset, c.layout, q_out=qo, k_out=ko)
+
+
+class DecodeStep:
+    """Device buffers of the decode-layer step (the memory-bound half of a
+    decoder layer with FP8 GEMM inputs) at T tokens: residual RMSNorm -> FP8
+    (H = 2048), the prologue at (16, 2), residual RMSNorm -> FP8, SiLU-gate
+    -> FP8 (d = 10240); one ring slot per step.  The FP8 scales come from one
+    calibration pass on the GPU over inputs drawn with another seed."""
 
     def __init__(self, torch, mbt, W, T):
         self.torch, self.mbt, self.W, self.T = torch, mbt, W, T
@@ -108,12 +251,10 @@ class Step:
                              act=W.SILU, dtype=dt, fp8=True)
         pi, ni, ai = self.pro.inputs(), self.norm.inputs(), self.act.inputs()
         t = lambda bits: W.to_torch(bits, dt, dev)
-        # shared: weights, rotary cache, positions
         self.w_q, self.w_k = t(pi["w_q"]), t(pi["w_k"])
         self.cos_sin = torch.from_numpy(pi["cos_sin"]).to(dev)
         self.pos = torch.from_numpy(pi["pos"]).to(dev)
         self.w1, self.w2 = t(ni["w"]), t(ni["w"])
-        # calibration pass on the GPU over inputs drawn with another seed
         nc, ac = self.norm.calibration_inputs(), self.act.calibration_inputs()
         amax_n = mbt.fused_add_rmsnorm_amax(t(nc["x"]), t(nc["residual"]), self.w1, 1e-6, 0)
         amax_a = mbt.gated_act_amax(t(ac["gate_up"]), W.SILU)
@@ -135,7 +276,6 @@ class Step:
             self.slots.append(s)
         torch.cuda.synchronize()
 
-    # the four launches of one step
     def norm1(self, s):
         self.mbt.fused_add_rmsnorm_fp8(s["x1"], s["r1"], self.w1, self.inv_n, 1e-6, 0, y=s["y1"])
 
@@ -150,56 +290,49 @@ class Step:
     def act_fp8(self, s):
         self.mbt.gated_act_fp8(s["gu"], self.inv_a, self.W.SILU, out=s["ao"])
 
-    def step(self, s):
+    def step(self, j):
+        s = self.slots[j % self.R]
         self.norm1(s)
         self.prologue(s)
         self.norm2(s)
         self.act_fp8(s)
 
-
-def capture(torch, fn, n):
-    """A graph of fn(0) .. fn(n - 1), captured on a side stream."""
-    g = torch.cuda.CUDAGraph()
-    stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(n):
-            fn(i)
-    torch.cuda.synchronize()
-    return g
+    def kernels(self):
+        return {"norm_fp8": (self.norm1, self.norm.bytes_algorithmic(), "rmsnorm"),
+                "prologue": (self.prologue, self.pro.bytes_algorithmic(), "qknorm_rope"),
+                "act_fp8": (self.act_fp8, self.act.bytes_algorithmic(), "gated_act")}
 
 
-def timed_replays(torch, graphs):
-    """Elapsed ms of replaying `graphs` (a list) back to back, bracketed by
-    synchronisations and HIP events on the current stream."""
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for g in graphs:
-        g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b)
+def decode_layer_step(torch, mbt, W, T=128, steps=2000):
+    """The decode-layer step at T tokens: tokens/s over `steps` cold steps and
+    each kernel's own average launch time."""
+    st = DecodeStep(torch, mbt, W, T)
+    run = Steps(torch, st.step, st.R)
+    run.run(200, gate=False)
+    ms = run.run(steps, gate=True)
+    per = {}
+    for name, (fn, nbytes, _) in st.kernels().items():
+        us = kernel_time_us(torch, lambda j, fn=fn: fn(st.slots[j]), st.R, 2000)
+        per[name] = dict(us=round(us, 3), bytes=nbytes, GBps=round(nbytes / us / 1e3, 1),
+                         frac_peak=round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
+                         traffic=traffic_for(f"{name}_T{T}", st.kernels()[name][2]))
+    out = {"workload": "residual RMSNorm->fp8 (H 2048), QK-RMSNorm+RoPE (16,2) D256 rot64, "
+                       "residual RMSNorm->fp8, SiLU-gate->fp8 (d 10240), bf16",
+           "tokens": T, "steps": steps, "ms_per_step": round(ms / steps, 6),
+           "tokens_per_s": round(T * steps / (ms / 1e3), 1), "ring_slots": st.R,
+           "ring": ring_mode(st.slot_bytes, st.R), "kernels": per}
+    del st
+    torch.cuda.empty_cache()
+    return out
 
 
-def run_steps(torch, st, gfull, grem, n):
-    graphs = [gfull] * (n // st.R) + ([grem[n % st.R]] if n % st.R else [])
-    return timed_replays(torch, graphs)
-
-
-def kernel_time_us(torch, fn, R, launches):
-    """Average duration of one launch: graphs of R back-to-back launches over
-    the ring slots, replayed until `launches` launches are timed."""
-    g = capture(torch, fn, R)
-    timed_replays(torch, [g])                    # warm the graph itself
-    reps = max(1, launches // R)
-    ms = timed_replays(torch, [g] * reps)
-    return 1000.0 * ms / (reps * R)
-
+# ---------------------------------------------------------------------------
+# per-cell measurements
+# ---------------------------------------------------------------------------
 
 def prologue_warm_us(torch, mbt, W, cell, samples=200, inner=32):
-    """P2-style: a graph of 32 calls on one buffer set, timed per replay."""
+    """The ninfer PR's method: a graph of 32 calls on one buffer set, 20
+    warm-up replays, then `samples` replays each timed on its own."""
     dev = "cuda:0"
     i = cell.inputs()
     t = lambda b: W.to_torch(b, cell.dtype, dev)
@@ -293,7 +426,7 @@ def route_us(torch, mbt, W, cell, cold, passes=7, samples=50, inner=32, launches
 
     def one(name):
         if cold:
-            return 1000.0 * timed_replays(torch, [g[name]] * reps) / (reps * n)
+            return 1000.0 * timed_replays(torch, [g[name]] * reps, gate=True) / (reps * n)
         return median([1000.0 * timed_replays(torch, [g[name]]) / n for _ in range(samples)])
 
     kept, dropped = [], 0
@@ -364,12 +497,12 @@ def extended_cold_us(torch, mbt, W, cell, form, launches=2000):
 
 
 def norm_fp8_cold_us(torch, mbt, W, cell, inv_scale, launches=2000):
-    """Residual RMSNorm -> FP8, cold: each launch uses its own ring slot."""
+    """Residual RMSNorm -> FP8 over a ring of buffer sets.  Returns (us, ring mode)."""
     dev = "cuda:0"
     i = cell.inputs()
     t = lambda b: W.to_torch(b, cell.dtype, dev)
     w = None if i["w"] is None else t(i["w"])
-    R = ring_slots(cell.bytes_algorithmic())
+    R = ring_slots(cell.bytes_algorithmic(), cache_resident_ok=True)
     x0, r0 = t(i["x"]), t(i["residual"])
     ring = [(x0.clone(), r0.clone(), torch.empty(x0.shape, dtype=torch.uint8, device=dev))
             for _ in range(R)]
@@ -381,12 +514,13 @@ def norm_fp8_cold_us(torch, mbt, W, cell, inv_scale, launches=2000):
     us = kernel_time_us(torch, call, R, launches)
     del ring
     torch.cuda.empty_cache()
-    return us
+    return us, ring_mode(cell.bytes_algorithmic(), R)
 
 
 def adarms_fp8_cold_us(torch, mbt, W, cell, launches=2000):
-    """Adaptive RMSNorm -> FP8 (gated residual), cold; the scale comes from
-    the GPU's own calibration pass over seed data."""
+    """Adaptive RMSNorm -> FP8 (gated residual) over a ring of buffer sets;
+    the scale comes from the GPU's own calibration pass over seed data.
+    Returns (us, ring mode)."""
     dev = "cuda:0"
     i = cell.inputs()
     t = lambda b: None if b is None else W.to_torch(b, cell.dtype, dev)
@@ -394,7 +528,7 @@ def adarms_fp8_cold_us(torch, mbt, W, cell, launches=2000):
     cal = cell.calibration_inputs()
     amax = mbt.adarms_amax(t(cal["x"]), t(cal["residual"]), g, sc, sh, cell.eps)
     inv_scale = W.fp8_inv_scale(float(amax.item()))
-    R = ring_slots(cell.bytes_algorithmic())
+    R = ring_slots(cell.bytes_algorithmic(), cache_resident_ok=True)
     x0, r0 = t(i["x"]), t(i["residual"])
     ring = [(x0.clone(), r0.clone(), torch.empty(x0.shape, dtype=torch.uint8, device=dev))
             for _ in range(R)]
@@ -406,17 +540,17 @@ def adarms_fp8_cold_us(torch, mbt, W, cell, launches=2000):
     us = kernel_time_us(torch, call, R, launches)
     del ring
     torch.cuda.empty_cache()
-    return us
+    return us, ring_mode(cell.bytes_algorithmic(), R)
 
 
 def norm_cold_us(torch, mbt, W, cell, launches=1500):
-    """Residual RMSNorm in place (dtype output), cold: each launch uses its
-    own ring slot."""
+    """Residual RMSNorm in place (dtype output) over a ring of buffer sets.
+    Returns (us, ring mode)."""
     dev = "cuda:0"
     i = cell.inputs()
     t = lambda b: W.to_torch(b, cell.dtype, dev)
     w = t(i["w"])
-    R = ring_slots(cell.bytes_algorithmic())
+    R = ring_slots(cell.bytes_algorithmic(), cache_resident_ok=True)
     x0, r0 = t(i["x"]), t(i["residual"])
     ring = [(x0.clone(), r0.clone()) for _ in range(R)]
 
@@ -427,14 +561,15 @@ def norm_cold_us(torch, mbt, W, cell, launches=1500):
     us = kernel_time_us(torch, call, R, launches)
     del ring
     torch.cuda.empty_cache()
-    return us
+    return us, ring_mode(cell.bytes_algorithmic(), R)
 
 
 def act_cold_us(torch, mbt, W, cell, inv_scale=1.0, launches=1500):
-    """Gated activation, dtype or FP8 output, cold."""
+    """Gated activation, dtype or FP8 output, over a ring of buffer sets.
+    Returns (us, ring mode)."""
     dev = "cuda:0"
     gu0 = W.to_torch(cell.inputs()["gate_up"], cell.dtype, dev)
-    R = ring_slots(cell.bytes_algorithmic())
+    R = ring_slots(cell.bytes_algorithmic(), cache_resident_ok=True)
     odt = torch.uint8 if cell.fp8 else gu0.dtype
     ring = [(gu0.clone(), torch.empty((cell.T, cell.d), dtype=odt, device=dev))
             for _ in range(R)]
@@ -449,7 +584,7 @@ def act_cold_us(torch, mbt, W, cell, inv_scale=1.0, launches=1500):
     us = kernel_time_us(torch, call, R, launches)
     del ring
     torch.cuda.empty_cache()
-    return us
+    return us, ring_mode(cell.bytes_algorithmic(), R)
 
 
 def copy_ceiling_gbps(torch, nbytes, launches=1000):
@@ -464,12 +599,9 @@ def copy_ceiling_gbps(torch, nbytes, launches=1000):
     return 2 * half / us / 1e3
 
 
-def prefill_cell(W):
-    """The widest prefill cell: (Q, K) = (24, 4), T = 2048, bf16."""
-    return max((c for c in W.config3_cells()
-                if c.dtype == W.BF16 and c.layout == W.ROTATE_HALF),
-               key=lambda c: c.bytes_algorithmic())
-
+# ---------------------------------------------------------------------------
+# committed profile summaries (profiles/), tied to the kernel sources
+# ---------------------------------------------------------------------------
 
 def source_digest(kernel):
     h = hashlib.sha256()
@@ -477,7 +609,8 @@ def source_digest(kernel):
     # the compiler flags (build.py) shape the kernel as much as its source;
     # comments and layout do not, so they are left out of the digest
     for path in (os.path.join(pkg, "csrc", KERNEL_SOURCES[kernel]),
-                 os.path.join(pkg, "csrc", "mbt_device.hpp"), os.path.join(pkg, "build.py")):
+                 os.path.join(pkg, "csrc", "mbt_device.hpp"),
+                 os.path.join(pkg, "csrc", "mbt_launch.hpp"), os.path.join(pkg, "build.py")):
         with open(path) as f:
             h.update(_code_only(f.read(), path.endswith(".py")).encode())
     return h.hexdigest()
@@ -493,105 +626,343 @@ def _code_only(text, python):
     return "\n".join(l.strip() for l in text.splitlines() if l.strip())
 
 
-def traffic_for(key, kernel):
-    """HBM bytes per launch of launch `key` from the committed counter
-    summary (profiles/traffic.json), or None once the kernel's source has
-    changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _profile_record(name, key, kernel):
+    """Entry `key` of profiles/<name>, or None once the kernel's source has
+    changed since it was taken."""
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
             rec = json.load(f).get(key)
     except (OSError, ValueError):
         return None
     if not rec or rec.get("source_sha256") != source_digest(kernel):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
 
 
-def cpu_baseline(W, st, seconds):
-    """The oracle, as it stands, on the host: the same step on the same
-    inputs, single-threaded, repeated until `seconds` of CPU work."""
-    import oracle
-    orc = oracle.default()
-    pi, ni, ai = st.pro.inputs(), st.norm.inputs(), st.act.inputs()
-    p = st.pro
-    # the oracle's own calibration pass (nothing here comes from the GPU)
-    nc, ac = st.norm.calibration_inputs(), st.act.calibration_inputs()
-    inv_n = W.fp8_inv_scale(orc.fused_add_rmsnorm_amax(nc["x"], nc["residual"], ni["w"], 1e-6,
-                                                       0, W.BF16))
-    inv_a = W.fp8_inv_scale(orc.gated_act_amax(ac["gate_up"], W.SILU, W.BF16))
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        orc.fused_add_rmsnorm_fp8(ni["x"], ni["residual"], ni["w"], inv_n, 1e-6, 0, W.BF16)
-        orc.qknorm_rope(pi["q"], pi["k"], pi["w_q"], pi["w_k"], pi["cos_sin"], pi["pos"], p.rot,
-                        p.eps, p.weight_offset, p.layout, W.BF16)
-        orc.fused_add_rmsnorm_fp8(ni["x"], ni["residual"], ni["w"], inv_n, 1e-6, 0, W.BF16)
-        orc.gated_act_fp8(ai["gate_up"], inv_a, W.SILU, W.BF16)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds and n >= 2:
-            break
+def traffic_for(key, kernel):
+    """HBM bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a
+    plain copy's reading) from profiles/traffic.json."""
+    rec = _profile_record("traffic.json", key, kernel)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
+
+
+def rocprof_us_for(cell_name):
+    """rocprofv3 kernel-trace average and median duration of a prefill
+    cell's launch, from profiles/prologue_prefill_cells.json."""
+    rec = _profile_record("prologue_prefill_cells.json", cell_name, "qknorm_rope")
+    return (None, None) if rec is None else (rec["average_us"], rec["median_us"])
+
+
+def _short(name):
+    return name.replace("void mbt::(anonymous namespace)::", "").split("(")[0]
+
+
+def trace_stats(src, dst):
+    """Reduce a rocprofv3 kernel-trace CSV (tens of MB) to one row per
+    kernel and launch size, plus the time-ordered runs of prologue launches
+    (needed to tell the prefill cells apart)."""
+    groups, runs = {}, []
+    with open(src) as f:
+        r = csv.DictReader(f)
+        gcol = [c for c in r.fieldnames if c.startswith("Grid_Size")]
+        rows = sorted(r, key=lambda row: int(row["Start_Timestamp"]))
+    for row in rows:
+        name = _short(row["Kernel_Name"])
+        grid = "x".join(row[c] for c in gcol)
+        d = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+        groups.setdefault((name, grid), []).append(d)
+        if name.startswith("qknorm_rope"):
+            if runs and runs[-1][0] == (name, grid):
+                runs[-1][1].append(d)
+            else:
+                runs.append(((name, grid), [d]))
+    with open(dst, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kind", "Name", "Grid", "Calls", "AverageNs", "MedianNs", "MinNs", "MaxNs"])
+        for (n, g), d in sorted(groups.items(), key=lambda kv: -len(kv[1])):
+            w.writerow(["group", n, g, len(d), sum(d) / len(d), statistics.median(d), min(d),
+                        max(d)])
+        for (n, g), d in runs:
+            w.writerow(["run", n, g, len(d), sum(d) / len(d), statistics.median(d), min(d),
+                        max(d)])
+
+
+def _read_stats(path):
+    with open(path) as f:
+        rows = list(csv.DictReader(f))
+    us = lambda r, k: float(r[k]) / 1000.0
+    groups = {(r["Name"], r["Grid"]): r for r in rows if r["Kind"] == "group"}
+    runs = [r for r in rows if r["Kind"] == "run"]
+    return groups, runs, us
+
+
+def write_profiles(d):
+    """Write profiles/ from one profiling run's outputs in directory d:
+      bench.json            python bench.py (unprofiled)
+      default_stats.csv     --trace-stats of rocprofv3 --kernel-trace over
+                            python bench.py --no-cpu (the same command)
+      cells_stats.csv       --trace-stats of rocprofv3 --kernel-trace over
+                            python bench.py --only prefill_cells
+      cells.json            that run's stdout (the cells in launch order)
+      pmc_<launch>_<counter>/pmc_counter_collection.csv
+                            rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs"""
+    import workloads as W
+    P = os.path.join(ROOT, "profiles")
+    repo = "$REPO"
+    bj = json.loads(open(os.path.join(d, "bench.json")).read().strip().splitlines()[-1])
+    cells_run = json.loads(open(os.path.join(d, "cells.json")).read().strip().splitlines()[-1])
+    groups_c, runs_c, us = _read_stats(os.path.join(d, "cells_stats.csv"))
+    names = cells_run["cells"]
+    kept = [r for r in runs_c if int(r["Calls"]) >= 100]
+    assert len(kept) == len(names), (len(kept), len(names))
+    cells = {c.name: c for c in W.config3_cells()}
+    digest = source_digest("qknorm_rope")
+    cmd_cells = ("rocprofv3 --kernel-trace --output-format csv -d <out> -o cells -- "
+                 f"python -u {repo}/bench.py --only prefill_cells")
+    per_cell = {"_command": cmd_cells}
+    lines = []
+    event = {x["cell"]: x for x in bj["prefill"]}
+    for name, r in zip(names, kept):
+        c = cells[name]
+        avg, med = us(r, "AverageNs"), us(r, "MedianNs")
+        per_cell[name] = {"source_sha256": digest, "kernel": r["Name"],
+                          "grid_work_items": r["Grid"], "launches": int(r["Calls"]),
+                          "average_us": round(avg, 3), "median_us": round(med, 3),
+                          "algorithmic_bytes": c.bytes_algorithmic()}
+        ev = event.get(name, {}).get("event_us")
+        gb = c.bytes_algorithmic() / avg / 1e3
+        lines.append(f"| {name} | `{r['Name']}` | {r['Grid'].split('x')[0]} | {r['Calls']} | "
+                     f"{avg:.3f} | {med:.3f} | {ev if ev is not None else '-'} | "
+                     f"{gb:.0f} | {gb / PEAK_HBM_GBPS:.3f} |")
+    with open(os.path.join(P, "prologue_prefill_cells.json"), "w") as f:
+        json.dump(per_cell, f, indent=1)
+    md = ["# Prologue launch durations per prefill cell: rocprofv3 --kernel-trace (MI355X, gfx950)",
+          "", "Command (from /tmp with TMPDIR=/tmp; `$REPO` is the repository root):", "",
+          "```", cmd_cells, f"python {repo}/bench.py --trace-stats <out>/cells_kernel_trace.csv "
+          "cells_stats.csv", "```", "",
+          "`--only prefill_cells` launches every configuration-3 cell in turn (T = 256 .. 2048,",
+          "(24, 4) and (16, 2), bf16 / fp16 rotate-half with rot_dim 64, bf16 interleaved with full",
+          "rotary), each over its own cold buffer ring (> 1 GiB).  Each cell's launches form one run",
+          "of identical (kernel, grid) dispatches in the trace, matched to the cells in launch order.",
+          "GB/s = algorithmic bytes / rocprofv3 average; fraction of 8 TB/s.  The event column is",
+          "the unprofiled bench.py run's HIP-event average per launch (graphs over the same ring).", "",
+          "| cell | kernel | grid (work-items) | launches | average us | median us | "
+          "bench.py events us | GB/s | of peak |",
+          "|---|---|---|---|---|---|---|---|---|", *lines, "",
+          "Kernel instantiation: `qknorm_rope_vec<dtype, lanes/row, chunks/lane, layout, general, "
+          "load order>` (dtype 2 = bf16, 1 = fp16; layout 0 = rotate-half, 1 = interleaved).",
+          "`profiles/prologue_prefill_cells.json` holds the same figures with a SHA-256 of the",
+          "kernel source; bench.py reports them only while that digest matches."]
+    with open(os.path.join(P, "prologue_prefill_cells_kernel_trace.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+    # the same command as the headline: the whole default run under the profiler
+    groups_d, _, _ = _read_stats(os.path.join(d, "default_stats.csv"))
+    head = per_cell[bj["config"]["cell"]]
+    hk = groups_d[(head["kernel"], head["grid_work_items"])]
+    cmd_d = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o bench -- "
+             f"python -u {repo}/bench.py --no-cpu")
+    top = sorted(groups_d.values(), key=lambda r: -int(r["Calls"]) * float(r["AverageNs"]))[:30]
+    tl = [f"| `{r['Name']}` | {r['Grid'].split('x')[0]} | {r['Calls']} | "
+          f"{us(r, 'AverageNs'):.3f} | {us(r, 'MedianNs'):.3f} |" for r in top]
+    ev_us = bj["roofline"]["avg_launch_us"]
+    av = us(hk, "AverageNs")
+    md = ["# Kernel durations of the default bench run: rocprofv3 --kernel-trace --stats "
+          "(MI355X, gfx950)", "",
+          "Command (from /tmp with TMPDIR=/tmp; `$REPO` is the repository root):", "",
+          "```", cmd_d, f"python {repo}/bench.py --trace-stats <out>/bench_kernel_trace.csv "
+          "default_stats.csv", "```", "",
+          "`--no-cpu` drops only the host-CPU oracle leg, which launches nothing on the GPU.", "",
+          "## The headline launch", "",
+          f"Cell `{bj['config']['cell']}`: `{head['kernel']}`, grid {head['grid_work_items']} "
+          "work-items.", "",
+          "| figure | us per launch |", "|---|---|",
+          f"| rocprofv3 average over every launch of it in the run ({hk['Calls']} launches) | "
+          f"{av:.3f} |",
+          f"| rocprofv3 median | {us(hk, 'MedianNs'):.3f} |",
+          f"| bench.py HIP events over the timed steps (unprofiled run, "
+          f"{bj['steps']} steps) | {ev_us} |",
+          f"| difference (rocprofv3 average / events - 1) | {100 * (av / ev_us - 1):+.1f} % |", "",
+          f"Algorithmic bytes per launch {bj['roofline']['algorithmic_bytes_per_launch']}: "
+          f"{bj['roofline']['algorithmic_bytes_per_launch'] / av / 1e3:.0f} GB/s by the rocprofv3 "
+          f"average, {bj['roofline']['achieved']} GB/s by the events.", "",
+          "## Launches with the most total time in the run", "",
+          "| kernel | grid (work-items) | launches | average us | median us |",
+          "|---|---|---|---|---|", *tl]
+    with open(os.path.join(P, "bench_default_kernel_trace.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+    # HBM traffic from the counter runs, scaled by a plain copy's reading
+    def pmc(tag, ctr):
+        path = os.path.join(d, f"pmc_{tag}_{ctr}", "pmc_counter_collection.csv")
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        v = [float(r["Counter_Value"]) for r in rows
+             if ("mbt::" in r["Kernel_Name"]) or (tag == "copy" and "copyBuffer" in r["Kernel_Name"])]
+        return statistics.median(v), len(v)
+    copy_f, _ = pmc("copy", "FETCH_SIZE")
+    copy_w, _ = pmc("copy", "WRITE_SIZE")
+    half_kib = 67108864 // 2 / 1024
+    ff, wf = half_kib / copy_f, half_kib / copy_w
+    cmd_p = ("rocprofv3 --pmc {ctr} --output-format csv -d <out> -o pmc -- "
+             f"python -u {repo}/bench.py --only {{only}}")
+    traffic = {"_calibration": {"copy_bytes_read": 33554432, "copy_bytes_written": 33554432,
+                                "FETCH_SIZE_KiB": copy_f, "WRITE_SIZE_KiB": copy_w,
+                                "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
+                                "command": cmd_p.replace("--only {only}", "--copy-probe 67108864")
+                                .format(ctr="{FETCH_SIZE|WRITE_SIZE}")}}
+    step = bj.get("decode_layer_step", {}).get("kernels", {})
+    launches = {"prologue_prefill": ("prologue_prefill", "qknorm_rope",
+                                     bj["roofline"]["algorithmic_bytes_per_launch"])}
+    for k, src in (("norm_fp8", "rmsnorm"), ("prologue", "qknorm_rope"), ("act_fp8", "gated_act")):
+        if k in step and os.path.exists(os.path.join(d, f"pmc_{k}_FETCH_SIZE")):
+            launches[f"{k}_T128"] = (k, src, step[k]["bytes"])
+    tl = []
+    for key, (only, src, algo) in launches.items():
+        f_, n = pmc(only, "FETCH_SIZE")
+        w_, _ = pmc(only, "WRITE_SIZE")
+        hbm = f_ * 1024 * ff + w_ * 1024 * wf
+        traffic[key] = {"source_sha256": source_digest(src), "FETCH_SIZE_KiB": f_,
+                        "WRITE_SIZE_KiB": w_, "hbm_bytes_per_launch": round(hbm),
+                        "algorithmic_bytes_per_launch": algo,
+                        "traffic_over_algorithmic": round(hbm / algo, 4), "dispatches": n,
+                        "command": cmd_p.format(ctr="{FETCH_SIZE|WRITE_SIZE}", only=only)}
+        tl.append(f"| {key} | {f_:.3f} | {w_:.3f} | {hbm / 1e6:.3f} | {algo / 1e6:.3f} | "
+                  f"{hbm / algo:.3f} |")
+    with open(os.path.join(P, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    md = ["# HBM traffic per launch from rocprofv3 counters (MI355X, gfx950)", "",
+          "Counters are taken one per run (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`), each over",
+          "launches that stream through a buffer ring larger than 1 GiB (so every launch misses the",
+          "256 MB Infinity Cache); the median per-dispatch value is used.", "",
+          "Calibration: a plain device copy of 32 MiB -> 32 MiB (torch `copy_`, HIP's",
+          f"`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = {copy_f:.1f} KiB and WRITE_SIZE = "
+          f"{copy_w:.1f} KiB per dispatch against 32768 KiB each, so FETCH_SIZE is scaled by "
+          f"{ff:.4f} and WRITE_SIZE by {wf:.4f}.", "",
+          "| launch | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB (scaled) | algorithmic MB | ratio |",
+          "|---|---|---|---|---|---|", *tl, "",
+          "`prologue_prefill` is the headline launch: the prologue at (Q, K) = (24, 4), head_dim 256,",
+          "rot_dim 64, T = 2048, bf16.  `*_T128` are the kernels of the decode-layer step at T = 128.",
+          "", "Commands (from /tmp with TMPDIR=/tmp; `$REPO` is the repository root):", "", "```",
+          *[cmd_p.format(ctr=c, only=o) for o in [v[0] for v in launches.values()]
+            for c in ("FETCH_SIZE", "WRITE_SIZE")],
+          *[cmd_p.replace("--only {only}", "--copy-probe 67108864").format(ctr=c)
+            for c in ("FETCH_SIZE", "WRITE_SIZE")], "```", "",
+          "`profiles/traffic.json` holds the same figures with a SHA-256 of each kernel's source;",
+          "bench.py reports `traffic` only while that digest still matches."]
+    with open(os.path.join(P, "hbm_traffic_counters.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
+# ---------------------------------------------------------------------------
+# the oracle on the host CPU (a reported baseline, not the target)
+# ---------------------------------------------------------------------------
+
+def _cpu_model():
     model = platform.processor() or "unknown"
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": round(n * st.T / el, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} full steps of T={st.T} tokens ({el:.1f} s), single thread, "
-                      f"host CPU: {model}, {len(os.sched_getaffinity(0))} cores visible"}
+    return model
 
 
-def cpu_baseline_threads(W, st, seconds):
-    """The same oracle calls, as they stand, from several host threads at
-    once, each thread on its own contiguous slice of the step's tokens (the
-    token-parallel CPU structure of "thox-edge-ops v2", section 5.3; ctypes
-    releases the interpreter lock inside the C oracle)."""
+def cpu_baseline(W, cell, threads=1, tokens_per_call=32):
+    """The oracle, as it stands, on the headline cell's inputs, following the
+    measurement protocol of "thox-edge-ops v2" (section 7.1): 20 warm-up
+    calls, then 30 trials of up to 50 calls each, as many as make a trial
+    last about 0.2 s; median and quartiles of tokens/s over the trials.
+
+    threads = 1: one call is the prologue on `tokens_per_call` tokens, on
+    one thread pinned to one core (restored afterwards).  threads = n: one
+    call runs n host threads at once, each on its own `tokens_per_call`
+    tokens (the token-parallel CPU structure of its section 5.3; ctypes
+    releases the interpreter lock inside the oracle)."""
     import concurrent.futures as cf
     import oracle
     orc = oracle.default()
-    pi, ni, ai = st.pro.inputs(), st.norm.inputs(), st.act.inputs()
-    p = st.pro
-    nc, ac = st.norm.calibration_inputs(), st.act.calibration_inputs()
-    inv_n = W.fp8_inv_scale(orc.fused_add_rmsnorm_amax(nc["x"], nc["residual"], ni["w"], 1e-6,
-                                                       0, W.BF16))
-    inv_a = W.fp8_inv_scale(orc.gated_act_amax(ac["gate_up"], W.SILU, W.BF16))
-    n_thr = max(1, min(len(os.sched_getaffinity(0)), st.T, 16))
-    bounds = [(i * st.T // n_thr, (i + 1) * st.T // n_thr) for i in range(n_thr)]
+    i = cell.inputs()
+    n = tokens_per_call
+    slices = [(a * n, (a + 1) * n) for a in range(threads)]
 
     def work(b):
         a, e = b
-        orc.fused_add_rmsnorm_fp8(ni["x"][a:e], ni["residual"][a:e], ni["w"], inv_n, 1e-6, 0,
-                                  W.BF16)
-        orc.qknorm_rope(pi["q"][a:e], pi["k"][a:e], pi["w_q"], pi["w_k"], pi["cos_sin"],
-                        pi["pos"][a:e], p.rot, p.eps, p.weight_offset, p.layout, W.BF16)
-        orc.fused_add_rmsnorm_fp8(ni["x"][a:e], ni["residual"][a:e], ni["w"], inv_n, 1e-6, 0,
-                                  W.BF16)
-        orc.gated_act_fp8(ai["gate_up"][a:e], inv_a, W.SILU, W.BF16)
+        orc.qknorm_rope(i["q"][a:e], i["k"][a:e], i["w_q"], i["w_k"], i["cos_sin"],
+                        i["pos"][a:e], cell.rot, cell.eps, cell.weight_offset, cell.layout,
+                        cell.dtype)
 
-    n = 0
-    with cf.ThreadPoolExecutor(n_thr) as ex:
+    old = os.sched_getaffinity(0)
+    ex = None
+    try:
+        if threads == 1:
+            os.sched_setaffinity(0, {min(old)})
+            call = lambda: work(slices[0])
+        else:
+            ex = cf.ThreadPoolExecutor(threads)
+            call = lambda: list(ex.map(work, slices))
+        for _ in range(20):
+            call()
         t0 = time.perf_counter()
-        while True:
-            list(ex.map(work, bounds))
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= seconds and n >= 2:
-                break
-    lo, hi = st.T // n_thr, -(-st.T // n_thr)
-    per = f"{lo}" if lo == hi else f"{lo}-{hi}"
-    return {"value": round(n * st.T / el, 1), "unit": "tokens/s", "cores": n_thr,
-            "kind": "oracle",
-            "sample": f"{n} full steps of T={st.T} tokens ({el:.1f} s wall), {n_thr} threads, "
-                      f"each on {per} tokens of every step"}
+        call()
+        per_call = time.perf_counter() - t0
+        m = max(1, min(50, int(round(0.2 / max(per_call, 1e-9)))))
+        rates = []
+        for _ in range(30):
+            t0 = time.perf_counter()
+            for _ in range(m):
+                call()
+            rates.append(m * n * threads / (time.perf_counter() - t0))
+    finally:
+        if ex is not None:
+            ex.shutdown()
+        os.sched_setaffinity(0, old)
+    where = ("one thread pinned to one core" if threads == 1
+             else f"{threads} threads, each on its own {n} tokens")
+    return {"value": round(median(rates), 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "p25": round(pct(rates, 25), 1), "p75": round(pct(rates, 75), 1),
+            "sample": f"the prologue on {n * threads} of the headline cell's {cell.T} tokens per "
+                      f"call ({cell.Q}x{cell.K} heads, head_dim {cell.D}), {where}; 20 warm-up "
+                      f"calls, 30 trials of {m} calls, median",
+            "cpu_model": _cpu_model(), "cores_visible": len(old)}
+
+
+# ---------------------------------------------------------------------------
+
+def only_mode(torch, mbt, W, what, steps):
+    """Profiling aids: launch one thing repeatedly, print a JSON line, exit."""
+    if what == "prologue_prefill":
+        h = Headline(torch, mbt, W)
+        n = max(steps, h.R)
+        for j in range(n):
+            h.step(j)
+        torch.cuda.synchronize()
+        return {"only": what, "cell": h.cell.name, "launches": n}
+    if what == "prefill_cells":
+        names = []
+        for c in W.config3_cells():
+            prologue_cold_us(torch, mbt, W, c, launches=500)
+            names.append(c.name)
+        return {"only": what, "cells": names}
+    st = DecodeStep(torch, mbt, W, 128)
+    fn = st.kernels()[what][0]
+    n = max(steps, st.R)
+    for j in range(n):
+        fn(st.slots[j % st.R])
+    torch.cuda.synchronize()
+    return {"only": what, "tokens": 128, "launches": n}
 
 
 def main():
     args = parse_args()
+    if args.trace_stats:
+        trace_stats(*args.trace_stats)
+        return
+    if args.write_profiles:
+        write_profiles(args.write_profiles)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: every op of this path is independent per "
               "token row, so the multi-GPU layout is token sharding with no exchange; "
@@ -614,203 +985,173 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_moved": 2 * (args.copy_probe // 2)}))
         return
-
-    phase("step buffers")
-    st = Step(torch, mbt, W, args.tokens)
-    kernels = {"norm_fp8": (st.norm1, st.norm.bytes_algorithmic(), "rmsnorm"),
-               "prologue": (st.prologue, st.pro.bytes_algorithmic(), "qknorm_rope"),
-               "act_fp8": (st.act_fp8, st.act.bytes_algorithmic(), "gated_act")}
-
-    if args.only == "prologue_prefill":
-        prologue_cold_us(torch, mbt, W, prefill_cell(W), launches=args.steps)
-        print(json.dumps({"only": args.only, "launches": args.steps}))
-        return
     if args.only:
-        fn = kernels[args.only][0]
-        for j in range(max(args.steps, st.R)):
-            fn(st.slots[j % st.R])
-        torch.cuda.synchronize()
-        print(json.dumps({"only": args.only, "launches": max(args.steps, st.R)}))
+        print(json.dumps(only_mode(torch, mbt, W, args.only, args.steps)), flush=True)
         return
 
-    R = st.R
-    gfull = capture(torch, lambda j: st.step(st.slots[j]), R)
-    grem = {}
-    for n in {args.steps % R, args.warmup % R} - {0}:
-        grem[n] = capture(torch, lambda j: st.step(st.slots[j]), n)
-    run_steps(torch, st, gfull, grem, args.warmup)                    # warmup
-    ms = run_steps(torch, st, gfull, grem, args.steps)                # timed
+    # ---- the headline: K steps of the prologue at the widest prefill cell
+    phase("headline buffers")
+    h = Headline(torch, mbt, W)
+    c = h.cell
+    run = Steps(torch, h.step, h.R)
+    phase("headline warm-up and timed steps")
+    run.run(args.warmup, gate=False)                       # untimed
+    ms = run.run(args.steps, gate=True)                     # timed: exactly K steps
     ms_per_step = ms / args.steps
-    tokens_per_s = args.tokens * args.steps / (ms / 1e3)
-
-    # per-kernel average launch durations (same cold ring, graphs of R launches)
-    per = {}
-    for name, (fn, nbytes, _) in kernels.items():
-        us = kernel_time_us(torch, lambda j, fn=fn: fn(st.slots[j]), R, 2000)
-        per[name] = dict(us=round(us, 3), bytes=nbytes, GBps=round(nbytes / us / 1e3, 1),
-                         frac_peak=round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4))
-    # norm_fp8 runs twice per step
-    share = {k: v["us"] * (2 if k == "norm_fp8" else 1) for k, v in per.items()}
-    dom = max(share, key=share.get)
-    dom_fn, dom_bytes, dom_src = kernels[dom]
-    achieved = dom_bytes / per[dom]["us"] / 1e3
-    phase("roofline")
+    us_launch = 1000.0 * ms_per_step
+    achieved = h.bytes / us_launch / 1e3
+    ungated = run.run(args.steps, gate=False) / args.steps
+    rp_avg, rp_med = rocprof_us_for(c.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                "traffic": traffic_for(f"{dom}_T{args.tokens}", dom_src), "kernel": dom,
-                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": per[dom]["us"],
-                "copy_ceiling_GBps": round(copy_ceiling_gbps(torch, dom_bytes), 1)}
+                "traffic": traffic_for("prologue_prefill", "qknorm_rope"),
+                "kernel": f"qknorm_rope {c.Q}x{c.K} D{c.D} rot{c.rot} T={c.T} bf16",
+                "algorithmic_bytes_per_launch": h.bytes, "avg_launch_us": round(us_launch, 3),
+                "rocprof_avg_us": rp_avg, "rocprof_median_us": rp_med,
+                "copy_ceiling_GBps": round(copy_ceiling_gbps(torch, h.bytes), 1)}
+    del run, h
+    torch.cuda.empty_cache()
 
-    # the prologue's own figures (the headline metric's parts)
-    out_extra = {}
-    prologue = {"step_T": args.tokens,
-                "tokens_per_s": round(args.tokens / per["prologue"]["us"] * 1e6, 1),
-                "GBps": per["prologue"]["GBps"], "frac_peak": per["prologue"]["frac_peak"]}
+    phase("T = 1")
+    t1 = [x for x in W.config2_cells() if x.T == 1][0]
+    w1 = prologue_warm_us(torch, mbt, W, t1)
+    us_t1 = {k: round(v, 3) for k, v in w1.items()}
+    us_t1["method"] = ("(16,2) D256 rot64 bf16, graph of 32 calls on one buffer set, 20 warm-up "
+                       "replays, median / quartiles of 200 replays; stream = direct launches")
+
+    phase("prefill cells")
+    prefill = []
+    for x in W.config3_cells():
+        us = prologue_cold_us(torch, mbt, W, x)
+        gbps = x.bytes_algorithmic() / us / 1e3
+        ra, rm = rocprof_us_for(x.name)
+        prefill.append({
+            "cell": x.name, "QK": f"{x.Q}x{x.K}", "T": x.T, "dtype": W.DTYPE_NAMES[x.dtype],
+            "layout": "interleaved" if x.layout == W.INTERLEAVED else "rotate_half",
+            "rot_dim": x.rot, "bytes": x.bytes_algorithmic(), "event_us": round(us, 3),
+            "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
+            "tokens_per_s": round(x.T / us * 1e6, 1), "rocprof_avg_us": ra,
+            "rocprof_frac_peak": None if ra is None else
+            round(x.bytes_algorithmic() / ra / 1e3 / PEAK_HBM_GBPS, 4)})
+
+    out = {
+        "metric": METRIC, "value": round(c.T / ms_per_step * 1e3, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"fused QK-RMSNorm+RoPE prologue, (Q,K)=({c.Q},{c.K}) heads, "
+                               f"head_dim {c.D}, rot_dim {c.rot} rotate-half, 1+w weights, "
+                               f"theta 1e7, T={c.T} tokens at positions 0..{c.T - 1}, bf16 "
+                               f"storage, fp32 arithmetic, out of place, cold HBM ring",
+                   "cell": c.name, "tokens": c.T, "heads_q": c.Q, "heads_kv": c.K,
+                   "head_dim": c.D, "rot_dim": c.rot, "io_dtype": "bf16", "arithmetic": "fp32",
+                   "ring_slots": ring_slots(c.bytes_algorithmic()),
+                   "ring_bytes": ring_slots(c.bytes_algorithmic()) * c.bytes_algorithmic(),
+                   "mode": "cold, hipGraph replays, spin kernel queued ahead of the timed "
+                           "region", "parallelism": "none (1 GPU)"},
+        "achieved_GBps": roofline["achieved"], "frac_peak": roofline["frac"],
+        "us_per_call_T1": us_t1,
+        "roofline": roofline,
+        "ungated_ms_per_step": round(ungated, 6),
+        "prefill": prefill,
+        "prefill_frac_min": min(x["frac_peak"] for x in prefill),
+    }
+
     if not args.no_sweep:
-        t1 = [c for c in W.config2_cells() if c.T == 1][0]
-        w1 = prologue_warm_us(torch, mbt, W, t1)
-        prologue["us_per_call_T1"] = {k: round(v, 3) for k, v in w1.items()}
         phase("decode sweep")
         sweep = []
-        for c in W.config2_cells():
-            w = prologue_warm_us(torch, mbt, W, c, samples=50)
-            sweep.append({"T": c.T, "warm_us": round(w["median"], 3),
-                          "tokens_per_s": round(c.T / w["median"] * 1e6, 1),
-                          "logical_GBps_warm": round(c.bytes_logical() / w["median"] / 1e3, 1)})
-        prologue["decode_sweep_16x2"] = sweep
-        pre = []
-        for c in W.config3_cells():
-            if c.dtype != W.BF16 or c.layout != W.ROTATE_HALF:
-                continue
-            us = prologue_cold_us(torch, mbt, W, c)
-            gbps = c.bytes_algorithmic() / us / 1e3
-            pre.append({"QK": f"{c.Q}x{c.K}", "T": c.T, "cold_us": round(us, 3),
-                        "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                        "tokens_per_s": round(c.T / us * 1e6, 1)})
-        prologue["prefill_cold"] = pre
-        phase("prefill, other cells")
-        # the rest of configuration 3: fp16, and interleaved pairs with full
-        # rotary on head_dim 256
-        other = []
-        for c in W.config3_cells():
-            if c.dtype == W.BF16 and c.layout == W.ROTATE_HALF:
-                continue
-            if c.T not in (256, 2048):
-                continue
-            us = prologue_cold_us(torch, mbt, W, c)
-            gbps = c.bytes_algorithmic() / us / 1e3
-            other.append({"cell": c.name, "QK": f"{c.Q}x{c.K}", "T": c.T,
-                          "layout": "interleaved" if c.layout == W.INTERLEAVED else "rotate_half",
-                          "rot_dim": c.rot, "dtype": W.DTYPE_NAMES[c.dtype],
-                          "cold_us": round(us, 3), "GBps": round(gbps, 1),
-                          "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)})
-        prologue["prefill_cold_other"] = other
-        # the residual norm (configuration 4, bf16 and fp32, both weight
-        # conventions folded: delta 0) and the gated activation
-        # (configuration 5), as rows/s and GB/s
+        for x in W.config2_cells():
+            w = prologue_warm_us(torch, mbt, W, x, samples=50)
+            sweep.append({"T": x.T, "warm_us": round(w["median"], 3),
+                          "tokens_per_s": round(x.T / w["median"] * 1e6, 1),
+                          "logical_GBps_warm": round(x.bytes_logical() / w["median"] / 1e3, 1)})
+        out["decode_sweep_16x2"] = sweep
+        phase("decode-layer step")
+        out["decode_layer_step"] = decode_layer_step(torch, mbt, W)
+        # the residual norm (configuration 4, bf16 and fp32, direct weights)
+        # and the gated activation (configuration 5), as rows/s and GB/s
         phase("norm sweep (configuration 4)")
         nsweep = []
-        for c in W.config4_cells():
-            if c.weight_offset != 0 or c.dtype == W.F16:
+        for x in W.config4_cells():
+            if x.weight_offset != 0 or x.dtype == W.F16:
                 continue
-            us = norm_cold_us(torch, mbt, W, c)
-            gbps = c.bytes_algorithmic() / us / 1e3
-            nsweep.append({"dtype": W.DTYPE_NAMES[c.dtype], "H": c.H, "T": c.T,
-                           "cold_us": round(us, 3), "rows_per_s": round(c.T / us * 1e6, 1),
+            us, mode = norm_cold_us(torch, mbt, W, x)
+            gbps = x.bytes_algorithmic() / us / 1e3
+            nsweep.append({"dtype": W.DTYPE_NAMES[x.dtype], "H": x.H, "T": x.T, "us": round(us, 3),
+                           "ring": mode, "rows_per_s": round(x.T / us * 1e6, 1),
                            "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)})
+        out["norm_sweep_config4"] = nsweep
         phase("activation sweep (configuration 5)")
         asweep = []
-        for c in W.config5_cells():
-            if not isinstance(c, W.ActCell):
+        for x in W.config5_cells():
+            if not isinstance(x, W.ActCell):
                 continue
-            us = act_cold_us(torch, mbt, W, c)
-            gbps = c.bytes_algorithmic() / us / 1e3
-            asweep.append({"act": "silu" if c.act == W.SILU else "gelu_tanh", "T": c.T,
-                           "out": "fp8" if c.fp8 else "bf16", "d": c.d, "cold_us": round(us, 3),
-                           "rows_per_s": round(c.T / us * 1e6, 1), "GBps": round(gbps, 1),
-                           "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)})
-        out_extra = {"norm_sweep_config4": nsweep, "act_sweep_config5": asweep}
-        # fused vs split route (norm q rows, norm k rows, rope), in place
+            us, mode = act_cold_us(torch, mbt, W, x)
+            gbps = x.bytes_algorithmic() / us / 1e3
+            asweep.append({"act": "silu" if x.act == W.SILU else "gelu_tanh", "T": x.T,
+                           "out": "fp8" if x.fp8 else "bf16", "d": x.d, "us": round(us, 3),
+                           "ring": mode, "rows_per_s": round(x.T / us * 1e6, 1),
+                           "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)})
+        out["act_sweep_config5"] = asweep
         phase("routes")
-        routes = {"warm": [route_us(torch, mbt, W, c, cold=False)
-                           for c in W.config2_cells() if c.T in (1, 8, 32, 128)],
-                  "cold": [route_us(torch, mbt, W, c, cold=True)
-                           for c in W.config3_cells()
-                           if c.dtype == W.BF16 and c.layout == W.ROTATE_HALF]}
-        prologue["routes"] = routes
-        # the prefill launch the >= 70 % HBM target is set for
-        big = prefill_cell(W)
-        us = [x for x in pre if x["QK"] == f"{big.Q}x{big.K}" and x["T"] == big.T][0]["cold_us"]
-        gbps = big.bytes_algorithmic() / us / 1e3
-        prologue["roofline_prefill"] = {
-            "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(gbps / PEAK_HBM_GBPS, 4),
-            "traffic": traffic_for("prologue_prefill", "qknorm_rope"),
-            "kernel": f"prologue {big.Q}x{big.K} T={big.T} bf16", "avg_launch_us": us,
-            "algorithmic_bytes_per_launch": big.bytes_algorithmic(),
-            "copy_ceiling_GBps": round(copy_ceiling_gbps(torch, big.bytes_algorithmic()), 1)}
-        # the extended forms: single rounding, and the fused QKV -> KV-cache op
+        out["routes"] = {"warm": [route_us(torch, mbt, W, x, cold=False)
+                                  for x in W.config2_cells() if x.T in (1, 8, 32, 128)],
+                         "cold": [route_us(torch, mbt, W, x, cold=True)
+                                  for x in W.config3_cells()
+                                  if x.dtype == W.BF16 and x.layout == W.ROTATE_HALF]}
+        phase("extended prologue forms")
         ext = []
-        for c in (st.pro, big):
-            base = [x for x in pre if x["QK"] == f"{c.Q}x{c.K}" and x["T"] == c.T]
-            row = {"QK": f"{c.Q}x{c.K}", "T": c.T,
-                   "contract_us": base[0]["cold_us"] if base else per["prologue"]["us"]}
+        step_pro = W.PrologueCell(name="step_prologue", config=2, cell=4, T=128, Q=16, K=2,
+                                  D=256, rot=64, theta=1e7, layout=W.ROTATE_HALF, dtype=W.BF16,
+                                  weight_offset=1, w_mean=0.0, w_std=0.05, x_std=2.0)
+        for x in (step_pro, c):
+            row = {"QK": f"{x.Q}x{x.K}", "T": x.T,
+                   "contract_us": round(prologue_cold_us(torch, mbt, W, x), 3)}
             for form in ("once", "qkv_cache"):
-                us, nb = extended_cold_us(torch, mbt, W, c, form)
+                us, nb = extended_cold_us(torch, mbt, W, x, form)
                 row[form + "_us"] = round(us, 3)
                 row[form + "_GBps"] = round(nb / us / 1e3, 1)
             ext.append(row)
-        prologue["extended_forms_cold"] = ext
-
-    # RMSNorm -> FP8 with the weight against the no-weight form (the scale
-    # folded into the next GEMM), H = 2048, bf16, cold
-    phase("no-weight norm")
-    noweight = []
-    if not args.no_sweep:
-        for T in (args.tokens, 512):
-            row = {"T": T, "H": st.H}
+        out["extended_forms"] = ext
+        # RMSNorm -> FP8 with the weight against the no-weight form (the scale
+        # folded into the next GEMM), H = 2048, bf16
+        phase("no-weight norm")
+        noweight = []
+        for T in (128, 512):
+            row = {"T": T, "H": 2048}
             for wt in (True, False):
-                c = W.NormCell(name="nw", config=5, cell=60 + T, T=T, H=st.H, dtype=W.BF16,
+                x = W.NormCell(name="nw", config=5, cell=60 + T, T=T, H=2048, dtype=W.BF16,
                                weight_offset=0 if not wt else 1, w_mean=0.0, w_std=0.05,
                                fp8=True, weight=wt)
-                us = norm_fp8_cold_us(torch, mbt, W, c, st.inv_n)
+                xi, cal = x.inputs(), x.calibration_inputs()
+                t = lambda b: None if b is None else W.to_torch(b, W.BF16, "cuda:0")
+                amax = mbt.fused_add_rmsnorm_amax(t(cal["x"]), t(cal["residual"]), t(xi["w"]),
+                                                  x.eps, x.weight_offset)
+                inv = W.fp8_inv_scale(float(amax.item()))
+                us, mode = norm_fp8_cold_us(torch, mbt, W, x, inv)
                 key = "weighted" if wt else "no_weight"
                 row[key + "_us"] = round(us, 3)
-                row[key + "_GBps"] = round(c.bytes_algorithmic() / us / 1e3, 1)
+                row[key + "_GBps"] = round(x.bytes_algorithmic() / us / 1e3, 1)
+                row["ring"] = mode
             noweight.append(row)
-    # adaptive RMSNorm -> FP8 with a gated residual (style vector per call):
-    # the Pi0.5 decoder's 10-token rows and a 512-token batch, H = 2048
-    phase("adaptive norm")
-    adarms = []
-    if not args.no_sweep:
+        out["norm_fp8_weight_vs_none"] = noweight
+        # adaptive RMSNorm -> FP8 with a gated residual (style vector per
+        # call): the Pi0.5 decoder's 10-token rows and a 512-token batch
+        phase("adaptive norm")
+        ada = []
         for T in (10, 512):
-            c = W.AdaCell(name="ada", config=5, cell=70 + T, T=T, H=st.H, dtype=W.BF16, fp8=True)
-            us = adarms_fp8_cold_us(torch, mbt, W, c)
-            adarms.append({"T": T, "H": st.H, "us": round(us, 3),
-                           "GBps": round(c.bytes_algorithmic() / us / 1e3, 1),
-                           "frac_peak": round(c.bytes_algorithmic() / us / 1e3 / PEAK_HBM_GBPS, 4)})
+            x = W.AdaCell(name="ada", config=5, cell=70 + T, T=T, H=2048, dtype=W.BF16, fp8=True)
+            us, mode = adarms_fp8_cold_us(torch, mbt, W, x)
+            ada.append({"T": T, "H": 2048, "us": round(us, 3), "ring": mode,
+                        "GBps": round(x.bytes_algorithmic() / us / 1e3, 1),
+                        "frac_peak": round(x.bytes_algorithmic() / us / 1e3 / PEAK_HBM_GBPS, 4)})
+        out["adarms_fp8_gated"] = ada
 
-    out = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": "decode-layer memory-bound path: residual RMSNorm->fp8, "
-                               "QK-RMSNorm+RoPE, residual RMSNorm->fp8, SiLU-gate->fp8",
-                   "tokens": args.tokens, "io_dtype": "bf16", "heads_q": 16, "heads_kv": 2,
-                   "head_dim": 256, "rot_dim": 64, "hidden": st.H, "intermediate": st.d,
-                   "ring_slots": R, "ring_bytes": R * st.slot_bytes, "mode": "cold, hipGraph",
-                   "parallelism": "none (1 GPU)"},
-        "roofline": roofline,
-        "kernels": per,
-        "prologue": prologue,
-        "norm_fp8_weight_vs_none": noweight,
-        "adarms_fp8_gated": adarms,
-        **out_extra,
-    }
-    if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(W, st, args.cpu_seconds)
-        out["cpu_baseline_threads"] = cpu_baseline_threads(W, st, min(args.cpu_seconds, 5.0))
+    if not args.no_cpu:
+        phase("oracle on the host CPU")
+        out["cpu_baseline"] = cpu_baseline(W, c, threads=1)
+        n_thr = max(1, min(len(os.sched_getaffinity(0)), 16))
+        out["cpu_baseline_threads"] = cpu_baseline(W, c, threads=n_thr)
     print(json.dumps(out), flush=True)
 
 
