@@ -39,13 +39,8 @@
  *    execute in order; calls on different streams that write the same
  *    memory race, as with any kernel.
  *  - Launch shapes (lanes and chunks per row, load order) are picked per
- *    call from the sizes.  A few environment variables, read once per
- *    process, override the thresholds for sweeps (MBT_QK_C_WAVES,
- *    MBT_QK_C_MAX, MBT_QK_MID_WAVES_LO, MBT_QK_THR_WAVES_LO,
- *    MBT_QK_THR_WAVES_HI, MBT_NORM_WPR, MBT_NORM_WIDE_CHUNKS,
- *    MBT_NORM_HALF_WAVES, MBT_ACT_U, MBT_ACT_U2_CHUNKS,
- *    MBT_ACT_HALF_WAVES); every shape gives
- *    the same bits, so they change timing only.
+ *    call from the sizes, by thresholds fixed at compile time; the
+ *    environment plays no part.  Every shape gives the same bits.
  */
 #ifndef MBT_H
 #define MBT_H

@@ -209,25 +209,11 @@ __global__ __launch_bounds__(256) void gated_scalar(ActParams p) {
     }
 }
 
-// Launch-shape tunables, read once from the environment (sweeps only; the
-// defaults are the measured best on MI355X).
-int env_int(const char* name, int dflt) {
-    const char* e = getenv(name);
-    return e ? atoi(e) : dflt;
-}
-int tun_act_u() {
-    static const int v = env_int("MBT_ACT_U", 0);
-    return v;
-}
-// Half-chunk lanes while the launch has at most this many waves.
-int tun_act_half_waves() {
-    static const int v = env_int("MBT_ACT_HALF_WAVES", 1024);
-    return v;
-}
-int64_t tun_act_u2_chunks() {
-    static const int v = env_int("MBT_ACT_U2_CHUNKS", 400000);
-    return v;
-}
+// Launch-shape thresholds (compile-time constants, the measured best on
+// MI355X): half-chunk lanes while the launch has at most kActHalfWaves
+// waves; two chunks per lane from kActU2Chunks chunks.
+constexpr int64_t kActHalfWaves = 1024;
+constexpr int64_t kActU2Chunks = 400000;
 
 template <int DT, int ACT, int MODE>
 hipError_t launch_mode(const ActArgs& a, hipStream_t s) {
@@ -249,7 +235,7 @@ hipError_t launch_mode(const ActArgs& a, hipStream_t s) {
     // full chunk.
     if constexpr (DT != kF32 && MODE != kActFp8) {
         const int64_t bpr = (2 * (int64_t)(a.d / V) + 255) / 256;     // 8-byte units
-        if (vec && a.T * bpr * 4 <= tun_act_half_waves() && a.T * bpr <= 0x7FFFFFFFll) {
+        if (vec && a.T * bpr * 4 <= kActHalfWaves && a.T * bpr <= 0x7FFFFFFFll) {
             p.chunks = a.d / V;
             p.blocks_per_row = (int32_t)bpr;
             hipLaunchKernelGGL((gated_half<DT, ACT, MODE>), dim3((uint32_t)(a.T * bpr)),
@@ -261,8 +247,7 @@ hipError_t launch_mode(const ActArgs& a, hipStream_t s) {
         p.chunks = a.d / V;
         // Two chunks per lane only at prefill widths: at decode widths the
         // per-wave latency matters more than the per-wave overhead.
-        int U = (a.T * (int64_t)p.chunks >= tun_act_u2_chunks()) ? 2 : 1;
-        if (tun_act_u() == 1 || tun_act_u() == 2) U = tun_act_u();
+        const int U = (a.T * (int64_t)p.chunks >= kActU2Chunks) ? 2 : 1;
         p.blocks_per_row = (p.chunks + 256 * U - 1) / (256 * U);
         const int64_t blocks = a.T * (int64_t)p.blocks_per_row;
         if (blocks <= 0x7FFFFFFFll) {

@@ -591,22 +591,12 @@ __global__ __launch_bounds__(256) void qknorm_rope_scalar(QkParams p, QkGen<true
     }
 }
 
-// Launch-shape tunable, read once from the environment (sweeps only; the
-// default is the measured best on MI355X).
-int env_int(const char* name, int dflt) {
-    const char* e = getenv(name);
-    return e ? atoi(e) : dflt;
-}
-// Chunks per lane: the fewest that bring the launch to at most this many
-// waves (about ten per CU: one resident round, short per-wave work).
-int tun_c_waves() {
-    static const int v = env_int("MBT_QK_C_WAVES", 2560);
-    return v;
-}
-int tun_c_max() {
-    static const int v = env_int("MBT_QK_C_MAX", 4);
-    return v;
-}
+// Chunks per lane: the fewest that bring the launch to at most kCWaves
+// waves (about ten per CU: one resident round, short per-wave work), and at
+// most kCMax.  Launch-shape thresholds are compile-time constants, the
+// measured best on MI355X; every shape gives the same bits.
+constexpr int64_t kCWaves = 2560;
+constexpr int kCMax = 4;
 
 // Waves of a launch with G lanes per row.
 int64_t vec_waves(const QkParams& p, int G) {
@@ -614,21 +604,12 @@ int64_t vec_waves(const QkParams& p, int G) {
     return (p.T * p.Q + rpw - 1) / rpw + (p.T * p.K + rpw - 1) / rpw;
 }
 
-// Load orders by wave count (C >= 2): order 2 above MID_LO waves, order 1
-// above THR_LO, both up to THR_HI (one full resident round of 256 CUs x
-// 4 SIMDs x 8 waves); order 0 elsewhere.
-int tun_mid_lo() {
-    static const int v = env_int("MBT_QK_MID_WAVES_LO", 2560);
-    return v;
-}
-int tun_thr_lo() {
-    static const int v = env_int("MBT_QK_THR_WAVES_LO", 5000);
-    return v;
-}
-int tun_thr_hi() {
-    static const int v = env_int("MBT_QK_THR_WAVES_HI", 8192);
-    return v;
-}
+// Load orders by wave count (C >= 2): order 2 above kMidWavesLo waves,
+// order 1 above kThrWavesLo, both up to kThrWavesHi (one full resident
+// round of 256 CUs x 4 SIMDs x 8 waves); order 0 elsewhere.
+constexpr int64_t kMidWavesLo = 2560;
+constexpr int64_t kThrWavesLo = 5000;
+constexpr int64_t kThrWavesHi = 8192;
 
 template <int DT, int G, int C, int LAYOUT, bool GEN, int ORD>
 hipError_t launch_vec(const QkParams& p0, const QkGen<true>& g0, hipStream_t s) {
@@ -653,7 +634,7 @@ hipError_t launch_gc(const QkParams& p, const QkGen<true>& g, int L, int C, hipS
     int ord = 0;
     if (C >= 2) {
         const int64_t w = vec_waves(p, L / C);
-        if (w <= tun_thr_hi()) ord = w > tun_thr_lo() ? 1 : (w > tun_mid_lo() ? 2 : 0);
+        if (w <= kThrWavesHi) ord = w > kThrWavesLo ? 1 : (w > kMidWavesLo ? 2 : 0);
     }
 #define MBT_QK_CASE1(LL)                                                 \
     if (L == LL && C == 1) return launch_vec<DT, LL, 1, LAYOUT, GEN, 0>(p, g, s);
@@ -714,7 +695,7 @@ hipError_t launch_dt(const QkArgs& a, hipStream_t s) {
     vec = vec && a.T * (int64_t)(a.Q > a.K ? a.Q : a.K) < (int64_t(1) << 24);
     if (vec) {
         // Chunks per lane: the fewest (1, 2, 4) whose launch has at most
-        // tun_c_waves() waves, else the most allowed.  Rotate-half rotates
+        // kCWaves waves, else the most allowed.  Rotate-half rotates
         // chunk group 0 only (its partner permute spans G lanes), so G must
         // cover the rotated chunks; interleaved pairs are lane-local, so any
         // chunk may rotate.  Measured: (24, 4) D = 256 T = 256 takes 2
@@ -723,12 +704,12 @@ hipError_t launch_dt(const QkArgs& a, hipStream_t s) {
         const int rc = (a.rot_dim == 0) ? 0
                        : (a.layout == 0 ? 2 * (half / V) : (a.rot_dim + V - 1) / V);
         int C = 1;
-        if (vec_waves(p, L) > tun_c_waves()) {
+        if (vec_waves(p, L) > kCWaves) {
             for (int cand : {2, 4}) {
                 const int G = L / cand;
-                if (cand > tun_c_max() || G < 4 || (a.layout == 0 && G < rc)) continue;
+                if (cand > kCMax || G < 4 || (a.layout == 0 && G < rc)) continue;
                 C = cand;
-                if (vec_waves(p, G) <= tun_c_waves()) break;
+                if (vec_waves(p, G) <= kCWaves) break;
             }
         }
         p.inv_Q = a.Q > 0 ? 1.0f / (float)a.Q : 0.0f;

@@ -511,10 +511,6 @@ __global__ __launch_bounds__(256) void rmsnorm_scalar(NormParams p) {
 // shortest per-wave latency) unless there are rows enough to fill the chip,
 // then as few waves as kMaxNch chunks per lane allow (more would spill under
 // the 1024-thread launch bound, which caps a wave at 128 VGPRs).
-int env_int(const char* name, int dflt) {
-    const char* e = getenv(name);
-    return e ? atoi(e) : dflt;
-}
 
 // Half-chunk lanes (rows of at most four 64-chunk groups) while the launch
 // has at most this many waves (four per SIMD of 256 CUs).  Measured on
@@ -522,19 +518,15 @@ int env_int(const char* name, int dflt) {
 // width tried (norm -> FP8 H = 2048 T = 256 / 512 2.74 / 3.15 -> 2.61 / 3.07
 // us; H = 1024 T = 1024 3.16 -> 2.96 us), above it slower (H = 2048 T = 1024
 // 4.03 -> 4.13 us).
-int tun_half_waves() {
-    static const int v = env_int("MBT_NORM_HALF_WAVES", 4096);
-    return v;
-}
+constexpr int64_t kHalfWaves = 4096;
 
 int pick_wpr(int64_t T, int chunks) {
-    static const int forced = env_int("MBT_NORM_WPR", 0);
-    static const int wide_rows = env_int("MBT_NORM_WIDE_CHUNKS", 8192);
+    // fewer waves per row once rows x 64-chunk groups reach this
+    constexpr int64_t wide_rows = 8192;
     const int per64 = (chunks + kWave - 1) / kWave;    // chunk groups
     const int min_wpr = (per64 + kMaxNch - 1) / kMaxNch;
     int wpr;
-    if (forced > 0) wpr = forced;
-    else if (T * per64 >= wide_rows) wpr = min_wpr;
+    if (T * per64 >= wide_rows) wpr = min_wpr;
     else wpr = per64;
     if (wpr < min_wpr) wpr = min_wpr;
     if (wpr > 16) wpr = 16;
@@ -587,7 +579,7 @@ hipError_t launch_mode(const NormArgs& a, hipStream_t s) {
     }
     if (vec && DT != kF32 && !ADA) {
         const int per64 = (chunks + kWave - 1) / kWave;
-        if (per64 <= 4 && a.T * 2 * per64 <= tun_half_waves()) {
+        if (per64 <= 4 && a.T * 2 * per64 <= kHalfWaves) {
             p.wpr = 2 * per64;
             hipLaunchKernelGGL((rmsnorm_half<DT == kF32 ? kBF16 : DT, MODE>), dim3((uint32_t)a.T),
                                dim3(kWave * p.wpr), 0, s, p);
