@@ -52,10 +52,6 @@ RING_BYTES = int(1.25 * 2 ** 30)
 # graph's node count.  Graphs are kept at or below MAX_SLOTS nodes (see
 # ring_slots).
 MAX_SLOTS = 4096
-# Spin kernel queued ahead of each timed region, so the host has queued the
-# graph's launches before the first timed one starts (cycles of the
-# shader clock: some tens of microseconds).
-GATE_CYCLES = 100_000
 
 KERNEL_SOURCES = {
     "qknorm_rope": "qknorm_rope.hip",
@@ -139,16 +135,12 @@ def capture(torch, fn, n):
     return g
 
 
-def timed_replays(torch, graphs, gate=False):
+def timed_replays(torch, graphs):
     """Elapsed ms of replaying `graphs` (a list) back to back, bracketed by
-    synchronisations and HIP events on the current stream.  gate: a spin
-    kernel goes ahead of the first event, so the launches are queued before
-    the timed region starts and host submission stays outside it."""
+    synchronisations and HIP events on the current stream."""
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
-    if gate:
-        torch.cuda._sleep(GATE_CYCLES)
     a.record()
     for g in graphs:
         g.replay()
@@ -163,7 +155,7 @@ def kernel_time_us(torch, fn, R, launches):
     g = capture(torch, fn, R)
     timed_replays(torch, [g])                    # warm the graph itself
     reps = max(1, launches // R)
-    ms = timed_replays(torch, [g] * reps, gate=True)
+    ms = timed_replays(torch, [g] * reps)
     return 1000.0 * ms / (reps * R)
 
 
@@ -184,13 +176,13 @@ class Steps:
             self.graphs[(start, n)] = capture(self.torch, lambda j: self.fn(start + j), n)
         return self.graphs[(start, n)]
 
-    def run(self, n, gate):
+    def run(self, n):
         start = self.pos % self.R
         graphs = [self._graph(start, self.R)] * (n // self.R)
         if n % self.R:
             graphs.append(self._graph(start, n % self.R))
         self.pos += n
-        return timed_replays(self.torch, graphs, gate=gate)
+        return timed_replays(self.torch, graphs)
 
 
 # ---------------------------------------------------------------------------
@@ -308,8 +300,8 @@ def decode_layer_step(torch, mbt, W, T=128, steps=2000):
     each kernel's own average launch time."""
     st = DecodeStep(torch, mbt, W, T)
     run = Steps(torch, st.step, st.R)
-    run.run(200, gate=False)
-    ms = run.run(steps, gate=True)
+    run.run(200)
+    ms = run.run(steps)
     per = {}
     for name, (fn, nbytes, _) in st.kernels().items():
         us = kernel_time_us(torch, lambda j, fn=fn: fn(st.slots[j]), st.R, 2000)
@@ -426,7 +418,7 @@ def route_us(torch, mbt, W, cell, cold, passes=7, samples=50, inner=32, launches
 
     def one(name):
         if cold:
-            return 1000.0 * timed_replays(torch, [g[name]] * reps, gate=True) / (reps * n)
+            return 1000.0 * timed_replays(torch, [g[name]] * reps) / (reps * n)
         return median([1000.0 * timed_replays(torch, [g[name]]) / n for _ in range(samples)])
 
     kept, dropped = [], 0
@@ -995,12 +987,11 @@ def main():
     c = h.cell
     run = Steps(torch, h.step, h.R)
     phase("headline warm-up and timed steps")
-    run.run(args.warmup, gate=False)                       # untimed
-    ms = run.run(args.steps, gate=True)                     # timed: exactly K steps
+    run.run(args.warmup)                                    # untimed
+    ms = run.run(args.steps)                                # timed: exactly K steps
     ms_per_step = ms / args.steps
     us_launch = 1000.0 * ms_per_step
     achieved = h.bytes / us_launch / 1e3
-    ungated = run.run(args.steps, gate=False) / args.steps
     rp_avg, rp_med = rocprof_us_for(c.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
@@ -1047,12 +1038,10 @@ def main():
                    "head_dim": c.D, "rot_dim": c.rot, "io_dtype": "bf16", "arithmetic": "fp32",
                    "ring_slots": ring_slots(c.bytes_algorithmic()),
                    "ring_bytes": ring_slots(c.bytes_algorithmic()) * c.bytes_algorithmic(),
-                   "mode": "cold, hipGraph replays, spin kernel queued ahead of the timed "
-                           "region", "parallelism": "none (1 GPU)"},
+                   "mode": "cold, hipGraph replays", "parallelism": "none (1 GPU)"},
         "achieved_GBps": roofline["achieved"], "frac_peak": roofline["frac"],
         "us_per_call_T1": us_t1,
         "roofline": roofline,
-        "ungated_ms_per_step": round(ungated, 6),
         "prefill": prefill,
         "prefill_frac_min": min(x["frac_peak"] for x in prefill),
     }
