@@ -596,6 +596,9 @@ __global__ __launch_bounds__(256) void qknorm_rope_scalar(QkParams p, QkGen<true
 // most kCMax.  Launch-shape thresholds are compile-time constants, the
 // measured best on MI355X; every shape gives the same bits.
 constexpr int64_t kCWaves = 2560;
+// Interleaved pairs rotate in every chunk, so a lane's chain grows with its
+// chunks: those launches keep fewer chunks per lane, up to this many waves.
+constexpr int64_t kCWavesInterleaved = 8000;
 constexpr int kCMax = 4;
 
 // Waves of a launch with G lanes per row.
@@ -695,21 +698,29 @@ hipError_t launch_dt(const QkArgs& a, hipStream_t s) {
     vec = vec && a.T * (int64_t)(a.Q > a.K ? a.Q : a.K) < (int64_t(1) << 24);
     if (vec) {
         // Chunks per lane: the fewest (1, 2, 4) whose launch has at most
-        // kCWaves waves, else the most allowed.  Rotate-half rotates
-        // chunk group 0 only (its partner permute spans G lanes), so G must
-        // cover the rotated chunks; interleaved pairs are lane-local, so any
-        // chunk may rotate.  Measured: (24, 4) D = 256 T = 256 takes 2
-        // (3.29 us; 1 chunk 3.43, 4 chunks 3.37), T = 512 takes 4.
+        // kCWaves waves (kCWavesInterleaved for interleaved pairs), else the
+        // most allowed.  Rotate-half rotates chunk group 0 only (its partner
+        // permute spans G lanes), so G must cover the rotated chunks;
+        // interleaved pairs are lane-local, so any chunk may rotate.
+        // Measured on MI355X, cold, D = 256: rotate-half rot_dim 64 (24, 4)
+        // T = 256 takes 2 (3.29 us; 1 chunk 3.43, 4 chunks 3.37), T = 512
+        // takes 4, and bounds of 1500, 4000 or 8000 waves were slower or
+        // equal at every configuration-3 width; interleaved full rotary
+        // with the 8000 bound against 2560: (24, 4) T = 256 / 512 / 1024 /
+        // 2048 3.35 / 4.48 / 6.57 / 11.32 -> 3.26 / 4.37 / 6.43 / 11.14 us,
+        // (16, 2) T = 512 / 1024 / 2048 3.66 / 5.28 / 7.94 -> 3.60 / 4.94 /
+        // 7.83 us.
         const int half = a.rot_dim / 2;
         const int rc = (a.rot_dim == 0) ? 0
                        : (a.layout == 0 ? 2 * (half / V) : (a.rot_dim + V - 1) / V);
         int C = 1;
-        if (vec_waves(p, L) > kCWaves) {
+        const int64_t cwaves = a.layout == 0 ? kCWaves : kCWavesInterleaved;
+        if (vec_waves(p, L) > cwaves) {
             for (int cand : {2, 4}) {
                 const int G = L / cand;
                 if (cand > kCMax || G < 4 || (a.layout == 0 && G < rc)) continue;
                 C = cand;
-                if (vec_waves(p, G) <= kCWaves) break;
+                if (vec_waves(p, G) <= cwaves) break;
             }
         }
         p.inv_Q = a.Q > 0 ? 1.0f / (float)a.Q : 0.0f;
