@@ -65,6 +65,18 @@ def normal_bits(key, shape, mean, std, dtype):
     return to_bits(g.normal(mean, std, size=shape), dtype)
 
 
+def device_normal(key, shape, std, dtype, device):
+    """Seeded N(0, std) tensor drawn on the device, in the storage dtype, for
+    inputs too large to draw on the host (gigabytes at the row-count limits).
+    The same key gives the same bits; tests copy sampled rows back to the
+    host, so the oracle and the kernels consume identical inputs."""
+    seed = int(np.random.SeedSequence([int(k) for k in key]).generate_state(1)[0])
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return (x * std).to(TORCH_DTYPES[dtype])
+
+
 def rope_cache(max_pos, rot_dim, theta):
     """Caller-side rotary cache, fp32 [max_pos][rot_dim]: cos in the first
     rot_dim/2 columns, sin in the last rot_dim/2.  Angle of pair i at position
