@@ -97,6 +97,8 @@ def parse_args():
                     help="headline, T = 1 and the prefill fractions only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", default=None,
+                    choices=["prologue_prefill", "prefill_cells", "norm_fp8", "prologue",
+                             "act_fp8"],
                     help="profiling aid: launch one thing repeatedly and exit: "
                          "prologue_prefill (the headline launch), prefill_cells (every "
                          "prefill cell in turn), or a kernel of the decode-layer step "
