@@ -1012,6 +1012,14 @@ def main():
     us_t1["method"] = ("(16,2) D256 rot64 bf16, graph of 32 calls on one buffer set, 20 warm-up "
                        "replays, median / quartiles of 200 replays; stream = direct launches")
 
+    # configuration 1: the Qwen3-style cell (head_dim 128, full rotary,
+    # (16, 8) heads, T = 4, one token outside the cache), same method
+    config1 = []
+    for x in W.config1_cells():
+        w = prologue_warm_us(torch, mbt, W, x, samples=100)
+        config1.append({"cell": x.name, "T": x.T, "warm_us": round(w["median"], 3),
+                        "p25": round(w["p25"], 3), "p75": round(w["p75"], 3)})
+
     phase("prefill cells")
     prefill = []
     for x in W.config3_cells():
@@ -1043,6 +1051,7 @@ def main():
                    "mode": "cold, hipGraph replays", "parallelism": "none (1 GPU)"},
         "achieved_GBps": roofline["achieved"], "frac_peak": roofline["frac"],
         "us_per_call_T1": us_t1,
+        "config1_us_per_call": config1,
         "roofline": roofline,
         "prefill": prefill,
         "prefill_frac_min": min(x["frac_peak"] for x in prefill),
