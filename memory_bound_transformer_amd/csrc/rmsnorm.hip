@@ -521,12 +521,17 @@ __global__ __launch_bounds__(256) void rmsnorm_scalar(NormParams p) {
 constexpr int64_t kHalfWaves = 4096;
 
 int pick_wpr(int64_t T, int chunks) {
-    // fewer waves per row once rows x 64-chunk groups reach this
+    // fewer waves per row once rows x 64-chunk groups reach this bound; the
+    // bound is lower when a row's groups (one wave each) do not split evenly
+    // over a CU's four SIMDs (H = 2560, 3584 in bf16; 1536, 2560 in fp32),
+    // whose uneven blocks measured 4-20 % slower from about 5000 on
     constexpr int64_t wide_rows = 8192;
+    constexpr int64_t wide_rows_uneven = 5000;
     const int per64 = (chunks + kWave - 1) / kWave;    // chunk groups
     const int min_wpr = (per64 + kMaxNch - 1) / kMaxNch;
+    const int64_t bound = (per64 % 4) ? wide_rows_uneven : wide_rows;
     int wpr;
-    if (T * per64 >= wide_rows) wpr = min_wpr;
+    if (T * per64 >= bound) wpr = min_wpr;
     else wpr = per64;
     if (wpr < min_wpr) wpr = min_wpr;
     if (wpr > 16) wpr = 16;

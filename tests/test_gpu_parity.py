@@ -375,6 +375,14 @@ EDGE_NORM = [
     _ncell(name="half_f16_no_residual_H2048_T64", dtype=W.F16, residual=False, H=2048, T=64,
            cell=36),
     _ncell(name="half_noweight_fp8_H2048_T128", weight=False, fp8=True, H=2048, T=128, cell=37),
+    # widths whose 64-chunk groups do not split evenly over four SIMDs take
+    # fewer waves per row from 5000 rows x groups: either side of that bound
+    # at H = 2560 (5 groups), fp32 at 10 groups and at 6, and 7 groups
+    _ncell(name="uneven_H2560_T999", H=2560, T=999, cell=38),
+    _ncell(name="uneven_H2560_T1000", H=2560, T=1000, cell=39),
+    _ncell(name="uneven_fp8_f32_H2560_T768", dtype=W.F32, H=2560, T=768, fp8=True, cell=40),
+    _ncell(name="uneven_H3584_T1023", H=3584, T=1023, cell=41),
+    _ncell(name="uneven_fp8_f32_H1536_T1023", dtype=W.F32, H=1536, T=1023, fp8=True, cell=42),
 ]
 
 
