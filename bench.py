@@ -581,6 +581,22 @@ def act_cold_us(torch, mbt, W, cell, inv_scale=1.0, launches=1500):
     return us, ring_mode(cell.bytes_algorithmic(), R)
 
 
+def stream_copy_us(torch, mbt, nbytes, launches=1000, chunks=(1, 2, 4, 8)):
+    """Cold µs per launch of the library's streaming copy moving nbytes
+    (nbytes/2 read, nbytes/2 written) at each chunks-per-lane value."""
+    half = max(16, nbytes // 2 // 16 * 16)
+    R = ring_slots(2 * half)
+    src = [torch.empty(half, dtype=torch.uint8, device="cuda:0") for _ in range(R)]
+    dst = [torch.empty(half, dtype=torch.uint8, device="cuda:0") for _ in range(R)]
+    out = {}
+    for c in chunks:
+        out[c] = kernel_time_us(torch, lambda j, c=c: mbt.stream_copy(src[j], dst[j], c), R,
+                                launches)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_ceiling_gbps(torch, nbytes, launches=1000):
     """torch's device copy of nbytes/2 -> nbytes/2 (nbytes of traffic), cold."""
     half = max(16, nbytes // 2)
@@ -783,6 +799,17 @@ def write_profiles(d):
           "## Launches with the most total time in the run", "",
           "| kernel | grid (work-items) | launches | average us | median us |",
           "|---|---|---|---|---|", *tl]
+    # the copy ceilings: every launch shape of the streaming copy in the run
+    cp = sorted((r for r in groups_d.values() if "stream_copy" in r["Name"]),
+                key=lambda r: (int(r["Grid"].split("x")[0]), r["Name"]))
+    if cp:
+        md += ["", "## The streaming copy (copy ceilings of the prefill cells)", "",
+               "`stream_copy<C>`: C 16-byte chunks per lane, one launch copying half a cell's "
+               "bytes into the other half.", "",
+               "| kernel | grid (work-items) | launches | average us | median us |",
+               "|---|---|---|---|---|",
+               *[f"| `{r['Name']}` | {r['Grid'].split('x')[0]} | {r['Calls']} | "
+                 f"{us(r, 'AverageNs'):.3f} | {us(r, 'MedianNs'):.3f} |" for r in cp]]
     with open(os.path.join(P, "bench_default_kernel_trace.md"), "w") as f:
         f.write("\n".join(md) + "\n")
 
@@ -1000,8 +1027,22 @@ def main():
                 "traffic": traffic_for("prologue_prefill", "qknorm_rope"),
                 "kernel": f"qknorm_rope {c.Q}x{c.K} D{c.D} rot{c.rot} T={c.T} bf16",
                 "algorithmic_bytes_per_launch": h.bytes, "avg_launch_us": round(us_launch, 3),
-                "rocprof_avg_us": rp_avg, "rocprof_median_us": rp_med,
-                "copy_ceiling_GBps": round(copy_ceiling_gbps(torch, h.bytes), 1)}
+                "rocprof_avg_us": rp_avg, "rocprof_median_us": rp_med}
+    phase("copy ceilings")
+    copies = {}                  # bytes -> {chunks per lane: µs}, the streaming copy
+
+    def best_copy(nbytes):
+        if nbytes not in copies:
+            copies[nbytes] = stream_copy_us(torch, mbt, nbytes)
+        k = min(copies[nbytes], key=copies[nbytes].get)
+        return copies[nbytes][k], k
+
+    cu, ck = best_copy(h.bytes)
+    roofline["copy_ceiling_GBps"] = round(h.bytes / cu / 1e3, 1)
+    roofline["copy_ceiling_us"] = round(cu, 3)
+    roofline["copy_ceiling_kernel"] = f"mbt_stream_copy, {ck} chunk(s) of 16 B per lane, cold"
+    roofline["of_copy"] = round(cu / us_launch, 4)
+    roofline["torch_copy_GBps"] = round(copy_ceiling_gbps(torch, h.bytes), 1)
     del run, h
     torch.cuda.empty_cache()
 
@@ -1026,6 +1067,7 @@ def main():
         us = prologue_cold_us(torch, mbt, W, x)
         gbps = x.bytes_algorithmic() / us / 1e3
         ra, rm = rocprof_us_for(x.name)
+        cu, ck = best_copy(x.bytes_algorithmic())
         prefill.append({
             "cell": x.name, "QK": f"{x.Q}x{x.K}", "T": x.T, "dtype": W.DTYPE_NAMES[x.dtype],
             "layout": "interleaved" if x.layout == W.INTERLEAVED else "rotate_half",
@@ -1033,7 +1075,9 @@ def main():
             "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
             "tokens_per_s": round(x.T / us * 1e6, 1), "rocprof_avg_us": ra,
             "rocprof_frac_peak": None if ra is None else
-            round(x.bytes_algorithmic() / ra / 1e3 / PEAK_HBM_GBPS, 4)})
+            round(x.bytes_algorithmic() / ra / 1e3 / PEAK_HBM_GBPS, 4),
+            "copy_us": round(cu, 3), "copy_chunks_per_lane": ck,
+            "of_copy": round(cu / us, 4)})
 
     out = {
         "metric": METRIC, "value": round(c.T / ms_per_step * 1e3, 1), "unit": "tokens/s",
@@ -1055,6 +1099,9 @@ def main():
         "roofline": roofline,
         "prefill": prefill,
         "prefill_frac_min": min(x["frac_peak"] for x in prefill),
+        "prefill_of_copy_min": min(x["of_copy"] for x in prefill),
+        "copy_ceilings_us": {str(b): {str(k): round(v, 3) for k, v in d.items()}
+                             for b, d in sorted(copies.items())},
     }
 
     if not args.no_sweep:

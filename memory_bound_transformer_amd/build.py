@@ -21,7 +21,8 @@ LIB = os.path.join(HERE, "libmbt.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["mbt_api.cpp", "qknorm_rope.hip", "rope.hip", "rmsnorm.hip", "gated_act.hip"]
+SOURCES = ["mbt_api.cpp", "qknorm_rope.hip", "rope.hip", "rmsnorm.hip", "gated_act.hip",
+           "stream_copy.hip"]
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-Wall", "-Wno-unused-function",

@@ -650,4 +650,23 @@ mbt_status mbt_quantize_fp8(const float* x, uint8_t* y, int64_t n, float inv_sca
                       "quantize_fp8 launch");
 }
 
+mbt_status mbt_stream_copy(const void* src, void* dst, int64_t nbytes, int32_t chunks_per_lane,
+                           void* stream) {
+    if (nbytes < 0 || nbytes % 16 != 0 || nbytes > (INT64_C(1) << 44))
+        return fail(MBT_ERR_BAD_SHAPE, "nbytes=%lld must be a multiple of 16 in [0, 2^44]",
+                    (long long)nbytes);
+    if (chunks_per_lane != 1 && chunks_per_lane != 2 && chunks_per_lane != 4 &&
+        chunks_per_lane != 8)
+        return fail(MBT_ERR_BAD_ENUM, "chunks_per_lane %d not 1, 2, 4 or 8", chunks_per_lane);
+    if (nbytes == 0) return ok();
+    if (!src || !dst) return fail(MBT_ERR_NULL_POINTER, "src and dst are required");
+    if (!aligned(src, 16) || !aligned(dst, 16))
+        return fail(MBT_ERR_ALIGN, "src and dst must be 16-byte aligned");
+    if (overlap(Range{(const char*)src, nbytes, "src"}, Range{(const char*)dst, nbytes, "dst"}))
+        return fail(MBT_ERR_ALIAS, "dst overlaps src");
+    return hip_status(mbt::launch_stream_copy(src, dst, nbytes, chunks_per_lane,
+                                              (hipStream_t)stream),
+                      "stream_copy launch");
+}
+
 }  // extern "C"

@@ -50,6 +50,7 @@ def lib():
         "mbt_gated_act_fp8": [vp, vp, f32, i64, i32, i32, i32, vp],
         "mbt_gated_act_amax": [vp, vp, i64, i32, i32, i32, vp],
         "mbt_quantize_fp8": [vp, vp, i64, f32, vp],
+        "mbt_stream_copy": [vp, vp, i64, i32, vp],
     }
     for name, args in sigs.items():
         getattr(lib, name).argtypes = args
@@ -63,7 +64,7 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), f"{n} declared in mbt.h but not exported"
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
@@ -193,6 +194,23 @@ def test_act_rejects(lib):
     assert q(A + 2, B, 16, 1.0, None) == ALIGN
     assert q(A, A + 8, 16, 1.0, None) == ALIAS
     assert q(None, None, 0, 1.0, None) == OK
+
+
+def test_stream_copy_rejects(lib):
+    c = lib.mbt_stream_copy
+    assert c(A, B, -16, 1, None) == SHAPE
+    assert c(A, B, 24, 1, None) == SHAPE            # not a multiple of 16
+    assert c(A, B, 2**44 + 16, 1, None) == SHAPE
+    assert c(A, B, 4096, 3, None) == ENUM
+    assert c(A, B, 4096, 16, None) == ENUM
+    assert c(None, B, 4096, 1, None) == NULLP
+    assert c(A, None, 4096, 1, None) == NULLP
+    assert c(A + 8, B, 4096, 1, None) == ALIGN
+    assert c(A, B + 4, 4096, 1, None) == ALIGN
+    assert c(A, A, 4096, 1, None) == ALIAS          # no in-place form
+    assert c(A, A + 2048, 4096, 2, None) == ALIAS
+    assert c(A + 2048, A, 4096, 4, None) == ALIAS
+    assert c(None, None, 0, 8, None) == OK
 
 
 def test_rope_rejects(lib):
