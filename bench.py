@@ -16,7 +16,9 @@ same K steps, against 8 TB/s.
 Also reported: microseconds per call at T = 1 (warm, a graph of 32 calls,
 median of 200 samples: the method of the ninfer PR the text-head shapes come
 from); the fraction of peak of every prefill cell (T >= 256), event-timed and
-from the committed rocprofv3 kernel trace; the decode-width sweep; the
+from the committed rocprofv3 kernel trace, each beside the library's
+streaming copy of the same bytes (mbt_stream_copy, cold: the attainable
+floor for a kernel that moves those bytes); the decode-width sweep; the
 decode-layer step (norm -> FP8, prologue, norm -> FP8, SiLU -> FP8 at
 T = 128); the residual-norm and activation sweeps; the fused-vs-split route
 comparison; the extended prologue forms; the oracle timed on the host CPU.
@@ -83,9 +85,13 @@ def ring_mode(nbytes, R):
     return "cache-resident" if total <= INFINITY_CACHE_BYTES else "partly cache-resident"
 
 
+_T0 = time.monotonic()
+
+
 def phase(name):
-    """Progress marker on stderr (the JSON line alone goes to stdout)."""
-    print(f"bench: {name}", file=sys.stderr, flush=True)
+    """Progress marker on stderr (the JSON line alone goes to stdout), with
+    the seconds since start."""
+    print(f"bench: {name} (+{time.monotonic() - _T0:.1f} s)", file=sys.stderr, flush=True)
 
 
 def parse_args():
@@ -1100,8 +1106,6 @@ def main():
         "prefill": prefill,
         "prefill_frac_min": min(x["frac_peak"] for x in prefill),
         "prefill_of_copy_min": min(x["of_copy"] for x in prefill),
-        "copy_ceilings_us": {str(b): {str(k): round(v, 3) for k, v in d.items()}
-                             for b, d in sorted(copies.items())},
     }
 
     if not args.no_sweep:
@@ -1124,9 +1128,15 @@ def main():
                 continue
             us, mode = norm_cold_us(torch, mbt, W, x)
             gbps = x.bytes_algorithmic() / us / 1e3
-            nsweep.append({"dtype": W.DTYPE_NAMES[x.dtype], "H": x.H, "T": x.T, "us": round(us, 3),
-                           "ring": mode, "rows_per_s": round(x.T / us * 1e6, 1),
-                           "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)})
+            row = {"dtype": W.DTYPE_NAMES[x.dtype], "H": x.H, "T": x.T, "us": round(us, 3),
+                   "ring": mode, "rows_per_s": round(x.T / us * 1e6, 1),
+                   "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+            if mode == "cold":
+                # the in-place norm reads and writes equal bytes, like a copy
+                cu, ck = best_copy(x.bytes_algorithmic())
+                row.update({"copy_us": round(cu, 3), "copy_chunks_per_lane": ck,
+                            "of_copy": round(cu / us, 4)})
+            nsweep.append(row)
         out["norm_sweep_config4"] = nsweep
         phase("activation sweep (configuration 5)")
         asweep = []
@@ -1199,6 +1209,9 @@ def main():
         out["cpu_baseline"] = cpu_baseline(W, c, threads=1)
         n_thr = max(1, min(len(os.sched_getaffinity(0)), 16))
         out["cpu_baseline_threads"] = cpu_baseline(W, c, threads=n_thr)
+    # every streaming-copy ceiling taken above: bytes -> {chunks per lane: µs}
+    out["copy_ceilings_us"] = {str(b): {str(k): round(v, 3) for k, v in d.items()}
+                               for b, d in sorted(copies.items())}
     print(json.dumps(out), flush=True)
 
 
