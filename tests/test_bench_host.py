@@ -82,3 +82,18 @@ def test_multi_gpu_request_exits(monkeypatch, capsys):
         B.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+@pytest.mark.parametrize("threads", [1, 2])
+def test_cpu_baseline_fields_and_affinity(threads):
+    # the oracle leg on a tiny sample (two tokens per thread and call): the
+    # fields the JSON line carries, quartiles around the median, and the
+    # process's CPU affinity restored after the pinned single-thread leg
+    import workloads as W
+    before = os.sched_getaffinity(0)
+    r = B.cpu_baseline(W, B.prefill_cell(W), threads=threads, tokens_per_call=2)
+    assert os.sched_getaffinity(0) == before
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["cores"] == threads
+    assert 0 < r["p25"] <= r["value"] <= r["p75"]
+    assert r["cores_visible"] == len(before)
+    assert f"on {2 * threads} of the headline cell's 2048 tokens" in r["sample"]
