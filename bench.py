@@ -761,7 +761,11 @@ def write_profiles(d):
           "rotary), each over its own cold buffer ring (> 1 GiB).  Each cell's launches form one run",
           "of identical (kernel, grid) dispatches in the trace, matched to the cells in launch order.",
           "GB/s = algorithmic bytes / rocprofv3 average; fraction of 8 TB/s.  The event column is",
-          "the unprofiled bench.py run's HIP-event average per launch (graphs over the same ring).", "",
+          "the unprofiled bench.py run's HIP-event average per launch (graphs over the same ring).",
+          "Launches of a few microseconds read up to about 1.5 us longer under the tracer than in "
+          "the unprofiled run, and vary more between runs; the streaming copy, which does no "
+          "arithmetic, does the same (bench_default_kernel_trace.md, last section), so the event "
+          "column is the figure for those cells.", "",
           "| cell | kernel | grid (work-items) | launches | average us | median us | "
           "bench.py events us | GB/s | of peak |",
           "|---|---|---|---|---|---|---|---|---|", *lines, "",
@@ -809,13 +813,32 @@ def write_profiles(d):
     cp = sorted((r for r in groups_d.values() if "stream_copy" in r["Name"]),
                 key=lambda r: (int(r["Grid"].split("x")[0]), r["Name"]))
     if cp:
+        # the unprofiled run's event time of each copy launch shape: a copy of
+        # b bytes (b/2 read, b/2 written) at C chunks per lane has a grid of
+        # ceil(b/2 / 16 / (256 C)) blocks of 256 work-items
+        ev = {}
+        for b, forms in bj.get("copy_ceilings_us", {}).items():
+            half = int(b) // 2 // 16 * 16
+            for k, v in forms.items():
+                g = -(-half // 16 // (256 * int(k))) * 256
+                ev[(f"stream_copy<{k}>", str(g))] = (int(b), v)
+        rows_cp = []
+        for r in cp:
+            b, e = ev.get((r["Name"], r["Grid"].split("x")[0]), (None, None))
+            rows_cp.append(f"| `{r['Name']}` | {r['Grid'].split('x')[0]} | "
+                           f"{'' if b is None else b} | {r['Calls']} | "
+                           f"{us(r, 'AverageNs'):.3f} | {us(r, 'MedianNs'):.3f} | "
+                           f"{'' if e is None else e} |")
         md += ["", "## The streaming copy (copy ceilings of the prefill cells)", "",
                "`stream_copy<C>`: C 16-byte chunks per lane, one launch copying half a cell's "
-               "bytes into the other half.", "",
-               "| kernel | grid (work-items) | launches | average us | median us |",
-               "|---|---|---|---|---|",
-               *[f"| `{r['Name']}` | {r['Grid'].split('x')[0]} | {r['Calls']} | "
-                 f"{us(r, 'AverageNs'):.3f} | {us(r, 'MedianNs'):.3f} |" for r in cp]]
+               "bytes into the other half.  The last column is the unprofiled run's HIP-event "
+               "average for the same launch shape.  The copy does no arithmetic, so where the "
+               "traced average exceeds the event time (launches of a few microseconds), the "
+               "difference is the tracer's, and the prologue's short launches read long under "
+               "it by about as much.", "",
+               "| kernel | grid (work-items) | bytes moved | launches | average us | median us "
+               "| bench.py events us |",
+               "|---|---|---|---|---|---|---|", *rows_cp]
     with open(os.path.join(P, "bench_default_kernel_trace.md"), "w") as f:
         f.write("\n".join(md) + "\n")
 
