@@ -91,7 +91,11 @@ uint16_t mbt_ref_f32_to_f16(float f) {
     if (e >= -14) {                                   /* normal binary16 */
         uint32_t half = ((uint32_t)(e + 15) << 10) | (m >> 13);
         uint32_t rest = m & 0x1fffu;
+#if MBT_ORACLE_MUTATION == 24
+        (void)rest;                                   /* planted: truncation */
+#else
         if (rest > 0x1000u || (rest == 0x1000u && (half & 1u))) half += 1u;
+#endif
         return (uint16_t)(sign | half);               /* a carry may reach inf */
     }
     if (e < -25) return sign;                         /* below half the least subnormal */
@@ -125,7 +129,11 @@ uint8_t mbt_ref_f32_to_e4m3fn(float f) {
     uint8_t sign = (f2u(f) >> 24) & 0x80u;
     if (isnan(f)) return (uint8_t)(sign | 0x7fu);
     float a = fabsf(f);
+#if MBT_ORACLE_MUTATION == 29
+    if (a > 448.0f) return (uint8_t)(sign | 0x7fu);  /* planted: overflow to NaN */
+#else
     if (a > 448.0f) return (uint8_t)(sign | 0x7eu);
+#endif
     if (a < 0.015625f) {                              /* below 2^-6: subnormal grid 2^-9 */
 #if MBT_ORACLE_MUTATION == 8
         float q = truncf(ldexpf(a, 9));               /* planted: truncation */
@@ -209,6 +217,12 @@ static float inv_rms(const float* x, int32_t D, int32_t rot_dim, float eps) {
 #if MBT_ORACLE_MUTATION == 3
     if (rot_dim > 0) return 1.0f / sqrtf(ss / (float)rot_dim + eps); /* planted */
 #endif
+#if MBT_ORACLE_MUTATION == 28
+    if (D > 1) return 1.0f / sqrtf(ss / (float)(D - 1) + eps); /* planted: D - 1 */
+#endif
+#if MBT_ORACLE_MUTATION == 33
+    return 1.0f / (sqrtf(ss / (float)D) + eps);       /* planted: eps outside the root */
+#endif
     return 1.0f / sqrtf(ss / (float)D + eps);
 }
 
@@ -224,6 +238,9 @@ static float weight_term(const void* w, int64_t i, int32_t dtype, int32_t delta)
  * scale folded into the next GEMM's weights: FlashRT optimization details,
  * the weight-folding paragraph) the product is used as it is. */
 static float apply_weight(float xn, const void* w, int64_t i, int32_t dtype, int32_t delta) {
+#if MBT_ORACLE_MUTATION == 36
+    xn = rounded(xn, dtype);                 /* planted: x * inv rounded before the weight */
+#endif
     if (w) return xn * weight_term(w, i, dtype, delta);
 #if MBT_ORACLE_MUTATION == 13
     return xn * 2.0f;                    /* planted: a missing weight read as 1 + 1 */
@@ -243,6 +260,15 @@ static float fp8_source(float v, int32_t dtype, int site) {
 #endif
     (void)dtype; (void)site;
     return v;
+}
+
+/* |v|: a calibration pass takes the largest magnitude. */
+static float magnitude(float v) {
+#if MBT_ORACLE_MUTATION == 30
+    return v;                                         /* planted: signed maximum */
+#else
+    return fabsf(v);
+#endif
 }
 
 int mbt_ref_rmsnorm_rows(const void* x, void* y, const void* w, int64_t rows,
@@ -288,6 +314,12 @@ static const float* cache_row(const float* cos_sin, int64_t p, int64_t max_pos,
 #if MBT_ORACLE_MUTATION == 12
     if (p >= max_pos && max_pos > 0) p = max_pos - 1; /* planted: clamp */
 #endif
+#if MBT_ORACLE_MUTATION == 26
+    if (p >= max_pos - 1) return NULL;                /* planted: last row outside */
+#endif
+#if MBT_ORACLE_MUTATION == 32
+    if (p < 0 && p >= -max_pos) p += max_pos;         /* planted: negative wraps */
+#endif
     if (p < 0 || p >= max_pos) return NULL;
     return cos_sin + p * (int64_t)rot;
 }
@@ -301,11 +333,21 @@ static void rotate_head(const float* n, float* o, int32_t D, int32_t rot,
         int32_t a, b;
         pair_index(i, rot, layout, &a, &b);
         float c = cs[i], s = cs[rot / 2 + i];
+#if MBT_ORACLE_MUTATION == 25
+        if (layout == MBT_REF_INTERLEAVED) {          /* planted: channel index */
+            c = cs[(2 * i) % (rot / 2)];
+            s = cs[rot / 2 + (2 * i) % (rot / 2)];
+        }
+#endif
 #if MBT_ORACLE_MUTATION == 4
         s = -s;                                        /* planted: wrong sign */
 #endif
         float oa = n[a] * c - n[b] * s;
+#if MBT_ORACLE_MUTATION == 31
+        float ob = n[b] * c - n[a] * s;                /* planted: o_b sign */
+#else
         float ob = n[b] * c + n[a] * s;
+#endif
 #if MBT_ORACLE_MUTATION == 1
         oa *= 1.000001f; ob *= 1.000001f;              /* planted: strength control */
 #endif
@@ -444,7 +486,11 @@ static void residual_sum(const void* x, void* residual, int64_t t, int32_t H,
 #else
             s[i] = rounded(sum, dtype);
 #endif
+#if MBT_ORACLE_MUTATION == 34
+            (void)write_res;                          /* planted: residual not updated */
+#else
             if (write_res) st(residual, k, dtype, sum);
+#endif
         } else {
             s[i] = xv;
         }
@@ -503,8 +549,8 @@ float mbt_ref_fused_add_rmsnorm_amax(const void* x, const void* residual,
         residual_sum(x, (void*)residual, t, H, dtype, 0, s);
         float inv = inv_rms(s, H, 0, eps);
         for (int32_t i = 0; i < H; i++) {
-            float v = fabsf(fp8_source(apply_weight(s[i] * inv, w, i, dtype, weight_offset),
-                                       dtype, 18));
+            float v = magnitude(fp8_source(apply_weight(s[i] * inv, w, i, dtype,
+                                                        weight_offset), dtype, 18));
             if (v > amax) amax = v;
         }
     }
@@ -571,8 +617,8 @@ static float adarms(void* x, void* residual, const void* gate, const void* scale
             if (mode == 0) st(x, t * H + i, dtype, m);
             else if (mode == 1)
                 y[t * H + i] = mbt_ref_f32_to_e4m3fn(fp8_source(m, dtype, 19) * inv_scale);
-            else if (fabsf(fp8_source(m, dtype, 20)) > amax)
-                amax = fabsf(fp8_source(m, dtype, 20));
+            else if (magnitude(fp8_source(m, dtype, 20)) > amax)
+                amax = magnitude(fp8_source(m, dtype, 20));
         }
     }
     free(s);
@@ -618,6 +664,9 @@ static float sigmoid(float x) {
 }
 
 static float act_value(float g, int32_t act) {
+#if MBT_ORACLE_MUTATION == 27
+    if (act == MBT_REF_SILU) return g * sigmoid(-g);  /* planted: sigmoid of -g */
+#endif
     if (act == MBT_REF_SILU) return g * sigmoid(g);
 #if MBT_ORACLE_MUTATION == 7
     float z = 0.7978845608f * (g + 0.0447f * g * g * g);   /* planted */
@@ -625,6 +674,25 @@ static float act_value(float g, int32_t act) {
     float z = 0.7978845608f * (g + 0.044715f * g * g * g);
 #endif
     return g * sigmoid(2.0f * z);
+}
+
+/* Offsets of g and u in a row of gate_up: the gate projection first. */
+#if MBT_ORACLE_MUTATION == 23
+#define GATE_OFF(d) ((int64_t)(d))                    /* planted: halves swapped */
+#define UP_OFF(d) ((int64_t)0)
+#else
+#define GATE_OFF(d) ((int64_t)0)
+#define UP_OFF(d) ((int64_t)(d))
+#endif
+
+/* The activation's value as the product consumes it: fp32, not rounded. */
+static float act_operand(float a, int32_t dtype) {
+#if MBT_ORACLE_MUTATION == 35
+    return rounded(a, dtype);                         /* planted: act(g) rounded first */
+#else
+    (void)dtype;
+    return a;
+#endif
 }
 
 static int act_args_ok(int64_t T, int32_t d, int32_t act, int32_t dtype) {
@@ -637,9 +705,9 @@ int mbt_ref_gated_act(const void* gate_up, void* out, int64_t T, int32_t d,
     if (!act_args_ok(T, d, act, dtype)) return -1;
     for (int64_t t = 0; t < T; t++)
         for (int32_t j = 0; j < d; j++) {
-            float g = ld(gate_up, t * 2 * (int64_t)d + j, dtype);
-            float u = ld(gate_up, t * 2 * (int64_t)d + d + j, dtype);
-            st(out, t * (int64_t)d + j, dtype, act_value(g, act) * u);
+            float g = ld(gate_up, t * 2 * (int64_t)d + GATE_OFF(d) + j, dtype);
+            float u = ld(gate_up, t * 2 * (int64_t)d + UP_OFF(d) + j, dtype);
+            st(out, t * (int64_t)d + j, dtype, act_operand(act_value(g, act), dtype) * u);
         }
     return 0;
 }
@@ -649,9 +717,9 @@ int mbt_ref_gated_act_fp8(const void* gate_up, uint8_t* out, float inv_scale,
     if (!act_args_ok(T, d, act, dtype)) return -1;
     for (int64_t t = 0; t < T; t++)
         for (int32_t j = 0; j < d; j++) {
-            float g = ld(gate_up, t * 2 * (int64_t)d + j, dtype);
-            float u = ld(gate_up, t * 2 * (int64_t)d + d + j, dtype);
-            float v = fp8_source(act_value(g, act) * u, dtype, 21);
+            float g = ld(gate_up, t * 2 * (int64_t)d + GATE_OFF(d) + j, dtype);
+            float u = ld(gate_up, t * 2 * (int64_t)d + UP_OFF(d) + j, dtype);
+            float v = fp8_source(act_operand(act_value(g, act), dtype) * u, dtype, 21);
             out[t * (int64_t)d + j] = mbt_ref_f32_to_e4m3fn(v * inv_scale);
         }
     return 0;
@@ -663,9 +731,9 @@ float mbt_ref_gated_act_amax(const void* gate_up, int64_t T, int32_t d,
     float amax = 0.0f;
     for (int64_t t = 0; t < T; t++)
         for (int32_t j = 0; j < d; j++) {
-            float g = ld(gate_up, t * 2 * (int64_t)d + j, dtype);
-            float u = ld(gate_up, t * 2 * (int64_t)d + d + j, dtype);
-            float v = fabsf(fp8_source(act_value(g, act) * u, dtype, 22));
+            float g = ld(gate_up, t * 2 * (int64_t)d + GATE_OFF(d) + j, dtype);
+            float u = ld(gate_up, t * 2 * (int64_t)d + UP_OFF(d) + j, dtype);
+            float v = magnitude(fp8_source(act_operand(act_value(g, act), dtype) * u, dtype, 22));
             if (v > amax) amax = v;
         }
     return amax;

@@ -688,6 +688,38 @@ def pin_act_exhaustive_bf16(orc):
         assert amb <= 64, f"act {act}: {amb} midpoint cases"
 
 
+def pin_act_single_rounding_16bit(orc):
+    """bf16 and fp16 I/O with u away from 1: out = R(act(g) u), the product
+    rounded once.  Reference: act(g) u in float64 (g times the logistic of g,
+    or of 2z for GELU-tanh), rounded with round_exact; every output that is
+    not within fp32 error of a rounding midpoint must equal it.  Rounding
+    act(g) to the dtype before the product (the unfused two-op form) moves
+    about a quarter of the outputs by one step, which the exhaustive pin
+    (u = 1) and the fp32 pins cannot see."""
+    g = np.random.default_rng(57)
+    d = 4096
+    c = math.sqrt(2.0 / math.pi)
+    for dtype in (BF16, F16):
+        gb = W.to_bits(g.uniform(-6.0, 6.0, (2, d)), dtype)
+        ub = W.to_bits(g.standard_normal((2, d)) * 1.5, dtype)
+        gv, uv = f32(gb, dtype).astype(np.float64), f32(ub, dtype).astype(np.float64)
+        gu = np.concatenate([gb, ub], axis=1)
+        for act in (W.SILU, W.GELU_TANH):
+            z = gv if act == W.SILU else 2.0 * c * (gv + 0.044715 * gv ** 3)
+            exact = (gv / (1.0 + np.exp(-z))) * uv
+            out = f32(orc.gated_act(gu, act, dtype), dtype).astype(np.float64)
+            bad = amb = 0
+            for o, v in zip(out.ravel(), exact.ravel()):
+                r, a = round_exact(v, dtype)
+                if o != r:
+                    if a:
+                        amb += 1
+                    else:
+                        bad += 1
+            assert bad == 0, f"act {act} dtype {dtype}: {bad} outputs not rounded once"
+            assert amb <= exact.size // 100, f"act {act} dtype {dtype}: {amb} midpoint cases"
+
+
 def pin_act_identities(orc):
     """act(g) - act(-g) = g for SiLU and GELU-tanh; act(0) = 0; for large g
     the gate is exactly g, so out = R(g u)."""
@@ -850,6 +882,7 @@ ALL_PINS = [
     pin_rope_complex, pin_rope_closed_forms, pin_rope_invariants,
     pin_prologue_composition, pin_prologue_constant_head, pin_prologue_round_once,
     pin_residual_add, pin_norm_fp8, pin_quantize_vs_torch,
-    pin_act_vs_torch, pin_act_exhaustive_bf16, pin_act_identities, pin_act_fp8,
+    pin_act_vs_torch, pin_act_exhaustive_bf16, pin_act_single_rounding_16bit,
+    pin_act_identities, pin_act_fp8,
     pin_fp8_epilogues_16bit,
 ]

@@ -37,6 +37,20 @@ MUTATIONS = {
     20: "adaptive norm calibration amax of the dtype-rounded value",
     21: "activation FP8 epilogue quantizes the dtype-rounded value",
     22: "activation calibration amax of the dtype-rounded value",
+    23: "gate and up halves of gate_up swapped",
+    24: "fp16 rounding truncates (normal range)",
+    25: "interleaved pairs take cos/sin at the channel index 2i",
+    26: "the cache's last row (max_pos - 1) treated as outside",
+    27: "SiLU takes the sigmoid of -g",
+    28: "mean square divided by D - 1",
+    29: "e4m3fn overflow gives NaN instead of saturating",
+    30: "calibration amax takes the signed maximum",
+    31: "rotate-half o_b subtracts the partner term",
+    32: "negative positions wrap around the cache",
+    33: "eps added outside the square root",
+    34: "residual stream not written back",
+    35: "activation rounded to the dtype before the product with u",
+    36: "norm rounds x * inv to the dtype before the weight",
 }
 
 # fast pins first: most mutations are caught within a second
