@@ -339,3 +339,31 @@ def test_adarms_rejects(lib):
     assert h(A, B, GT, SC, SH, None, 4, 2048, 1e-6, BF16, None) == NULLP
     assert h(A, B, GT, SC, SH, C + 2, 4, 2048, 1e-6, BF16, None) == ALIGN
     assert h(A, B, GT, SC, SH, GT + 4, 4, 2048, 1e-6, BF16, None) == ALIAS       # amax on gate
+
+
+def test_last_error_is_per_thread(lib):
+    # Eight threads reject calls with their own T at once (ctypes releases
+    # the interpreter lock inside each call, so the calls interleave); each
+    # reads back its own detail, and its own successful no-op clears it.
+    import threading
+    errors = []
+
+    def worker(tid):
+        try:
+            for it in range(3000):
+                T = -(1 + tid * 100_000 + it)
+                assert lib.mbt_gated_act(A, B, T, 16, 0, BF16, None) == SHAPE
+                got = lib.mbt_last_error().decode()
+                assert got == f"T={T} d=16", (tid, it, got)
+                if it % 7 == 0:
+                    assert lib.mbt_gated_act(None, None, 0, 16, 0, BF16, None) == OK
+                    assert lib.mbt_last_error().decode() == "", (tid, it)
+        except AssertionError as e:
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
