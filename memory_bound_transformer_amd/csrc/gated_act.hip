@@ -61,6 +61,24 @@ __device__ __forceinline__ float sigmoid(float x) {
     return x >= 0.0f ? r : e * r;
 }
 
+// sigmoid(2z).  For 16-bit I/O the doubling goes into exp_neg's constant:
+// |2z| (-log2(e) / 2) and |z| (-log2(e)) are the same real product (scaling
+// by 2 is exact, in the constant too), rounded once either way, and 2z has
+// z's sign, so the result is sigmoid<DT>(2z)'s bits with one instruction
+// fewer per element.
+template <int DT>
+__device__ __forceinline__ float sigmoid2(float z) {
+    if constexpr (DT == kF32) {
+        return sigmoid<DT>(2.0f * z);
+    } else {
+        constexpr float k = 2.0f * -0.72134752044448170f;
+        const float h = __builtin_amdgcn_exp2f(fabsf(z) * k);
+        const float e = h * h;
+        const float r = __builtin_amdgcn_rcpf(1.0f + e);
+        return z >= 0.0f ? r : e * r;
+    }
+}
+
 template <int DT, int ACT>
 __device__ __forceinline__ float act_mul(float g, float u) {
     float a;
@@ -68,7 +86,7 @@ __device__ __forceinline__ float act_mul(float g, float u) {
         a = g * sigmoid<DT>(g);
     } else {
         const float z = 0.7978845608f * (g + 0.044715f * g * g * g);
-        a = g * sigmoid<DT>(2.0f * z);
+        a = g * sigmoid2<DT>(z);
     }
     return a * u;
 }
@@ -211,8 +229,10 @@ __global__ __launch_bounds__(256) void gated_scalar(ActParams p) {
 
 // Launch-shape thresholds (compile-time constants, the measured best on
 // MI355X): half-chunk lanes while the launch has at most kActHalfWaves
-// waves; two chunks per lane from kActU2Chunks chunks.
+// waves (kActHalfWavesFp8 for FP8 output); two chunks per lane from
+// kActU2Chunks chunks.
 constexpr int64_t kActHalfWaves = 1024;
+constexpr int64_t kActHalfWavesFp8 = 8192;
 constexpr int64_t kActU2Chunks = 400000;
 
 template <int DT, int ACT, int MODE>
@@ -226,16 +246,20 @@ hipError_t launch_mode(const ActArgs& a, hipStream_t s) {
     if (MODE == kActDtype) vec = vec && aligned16(a.out);
     if (MODE == kActFp8)
         vec = vec && ((reinterpret_cast<uintptr_t>(a.out8) & (V == 8 ? 7u : 3u)) == 0);
-    // Half-chunk lanes for 16-bit outputs at few rows.  Measured on MI355X,
+    // Half-chunk lanes for 16-bit inputs at few rows.  Measured on MI355X,
     // SiLU, d = 10240, bf16 out: T = 1 / 16 cold 1.90 / 2.15 -> 1.83 / 2.04
     // us, warm (a graph of 32 calls on one buffer set) 2.10 / 2.15 -> 1.97 /
-    // 2.00 us.  FP8 out gained cold (1.98 -> 1.89 us at T = 1) but not warm
-    // (2.07 both ways at T = 1, 2.05 -> 2.12 at T = 16), and past 1024 waves
-    // warm launches got slower, so FP8 output and wider launches keep the
-    // full chunk.
-    if constexpr (DT != kF32 && MODE != kActFp8) {
+    // 2.00 us; past 1024 waves warm launches got slower.  FP8 output
+    // converts and stores fewer bytes per element, so its arithmetic chain
+    // is the longer share and half-chunk lanes pay up to 8192 waves (T = 204
+    // at d = 10240): SiLU -> FP8 cold T = 1 / 64 / 128 / 200 2.00 / 2.54 /
+    // 3.05 / 3.64 -> 1.91 / 2.37 / 2.91 / 3.52 us, warm T = 128 2.99 ->
+    // 2.93 us; at 10240 waves (T = 256) 4.02 -> 4.62 us, so wider launches
+    // keep the full chunk.
+    if constexpr (DT != kF32) {
         const int64_t bpr = (2 * (int64_t)(a.d / V) + 255) / 256;     // 8-byte units
-        if (vec && a.T * bpr * 4 <= kActHalfWaves && a.T * bpr <= 0x7FFFFFFFll) {
+        const int64_t cap = MODE == kActFp8 ? kActHalfWavesFp8 : kActHalfWaves;
+        if (vec && a.T * bpr * 4 <= cap && a.T * bpr <= 0x7FFFFFFFll) {
             p.chunks = a.d / V;
             p.blocks_per_row = (int32_t)bpr;
             hipLaunchKernelGGL((gated_half<DT, ACT, MODE>), dim3((uint32_t)(a.T * bpr)),

@@ -472,6 +472,13 @@ EDGE_ACT = [
     # calibration amax of a narrow launch
     _acell(name="half_partial_d1000", d=1000, T=3, cell=9),
     _acell(name="half_f16_d2056", dtype=W.F16, d=2056, T=7, act=W.GELU_TANH, cell=10),
+    # FP8 output takes half-chunk lanes up to 8192 waves (40 per row at
+    # d = 10240): either side of that bound, a partial last block, fp16
+    _acell(name="half_fp8_d1000", d=1000, T=3, fp8=True, cell=11),
+    _acell(name="half_fp8_T204", d=10240, T=204, fp8=True, cell=12),
+    _acell(name="full_fp8_T205", d=10240, T=205, act=W.GELU_TANH, fp8=True, cell=13),
+    _acell(name="half_f16_fp8_d2056", dtype=W.F16, d=2056, T=7, act=W.GELU_TANH, fp8=True,
+           cell=14),
 ]
 
 
