@@ -172,7 +172,7 @@ class Steps:
     last one stopped, so a slot is reused only after the other R - 1 (a
     warm-up never leaves the first timed slots in the Infinity Cache).
     Graphs (one full pass from a start slot, or a shorter run) are captured
-    on first use, before the timed region."""
+    by prepare(), or on first use, always before the timed region."""
 
     def __init__(self, torch, fn, R):
         self.torch, self.fn, self.R = torch, fn, R
@@ -618,7 +618,9 @@ def stream_copy_us(torch, mbt, nbytes, launches=1000, chunks=(1, 2, 4, 8)):
     """Cold µs per launch of the library's streaming copy moving nbytes
     (nbytes/2 read, nbytes/2 written) at each chunks-per-lane value."""
     half = max(16, nbytes // 2 // 16 * 16)
-    R = ring_slots(2 * half)
+    # callers ask only for byte counts whose own ring is cold; rounding down
+    # to 16 bytes may add a slot, which must not turn into a refusal
+    R = ring_slots(2 * half, cache_resident_ok=True)
     src = [torch.empty(half, dtype=torch.uint8, device="cuda:0") for _ in range(R)]
     dst = [torch.empty(half, dtype=torch.uint8, device="cuda:0") for _ in range(R)]
     out = {}

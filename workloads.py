@@ -16,8 +16,7 @@ tensor])`` in float64, cast to float32, then rounded to the storage dtype
 (bf16 through torch's round-to-nearest-even cast, fp16 through numpy's).
 Tensor ids: 0 q / x / gate_up, 1 k / residual, 2 w_q / w, 3 w_k, 4 positions.
 """
-from dataclasses import dataclass, field
-from typing import Optional
+from dataclasses import dataclass
 
 import numpy as np
 import torch
