@@ -1163,6 +1163,24 @@ def main():
     }
 
     if not args.no_sweep:
+        # the headline geometry past configuration 3's widest batch (positions
+        # 0 .. T - 1 with a cache of T rows, so every token rotates)
+        phase("large prefill widths")
+        large = []
+        for T in (4096, 8192, 16384):
+            x = W.PrologueCell(name=f"prefill24x4_bf16_T{T}", config=3, cell=900 + T, T=T, Q=24,
+                               K=4, D=256, rot=64, theta=1e7, layout=W.ROTATE_HALF, dtype=W.BF16,
+                               weight_offset=1, w_mean=0.0, w_std=0.05, x_std=2.0,
+                               positions="arange", max_pos=T)
+            us = prologue_cold_us(torch, mbt, W, x, launches=400)
+            nb = x.bytes_algorithmic()
+            cu, ck = best_copy(nb)
+            large.append({"T": T, "bytes": nb, "event_us": round(us, 3),
+                          "GBps": round(nb / us / 1e3, 1),
+                          "frac_peak": round(nb / us / 1e3 / PEAK_HBM_GBPS, 4),
+                          "tokens_per_s": round(T / us * 1e6, 1), "copy_us": round(cu, 3),
+                          "copy_chunks_per_lane": ck, "of_copy": round(cu / us, 4)})
+        out["prefill_large_24x4"] = large
         phase("decode sweep")
         sweep = []
         for x in W.config2_cells():
