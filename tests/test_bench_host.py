@@ -74,6 +74,9 @@ def test_profile_records_follow_the_sources():
     assert B.traffic_for("prologue_prefill", "qknorm_rope") == rec["hbm_bytes_per_launch"]
     avg, med = B.rocprof_us_for(B.prefill_cell(__import__("workloads")).name)
     assert avg is not None and 5.0 < avg < 20.0
+    # the headline's figure comes from the default run under the tracer
+    avg, med = B.headline_rocprof_us()
+    assert avg is not None and 5.0 < avg < 20.0 and 5.0 < med < 20.0
 
 
 def test_multi_gpu_request_exits(monkeypatch, capsys):
