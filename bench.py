@@ -1091,11 +1091,14 @@ def main():
     c = h.cell
     run = Steps(torch, h.step, h.R)
     phase("headline graphs: captured and replayed once, then one pass over the ring")
-    run.prepare([args.warmup, args.steps])
+    run.prepare([args.warmup, args.steps, args.steps, args.steps])
     phase("headline warm-up and timed steps")
     run.run(args.warmup)                                    # untimed
     ms = run.run(args.steps)                                # timed: exactly K steps
     ms_per_step = ms / args.steps
+    # the same measurement twice more, on the slots that follow (a null arm:
+    # how far identical runs of K steps differ; `value` is the first)
+    repeats = [ms_per_step] + [run.run(args.steps) / args.steps for _ in range(2)]
     us_launch = 1000.0 * ms_per_step
     achieved = h.bytes / us_launch / 1e3
     rp_avg, rp_med = headline_rocprof_us()
@@ -1171,6 +1174,8 @@ def main():
                    "ring_bytes": ring_slots(c.bytes_algorithmic()) * c.bytes_algorithmic(),
                    "mode": "cold, hipGraph replays", "parallelism": "none (1 GPU)"},
         "achieved_GBps": roofline["achieved"], "frac_peak": roofline["frac"],
+        "repeats_us_per_step": [round(1000.0 * x, 3) for x in repeats],
+        "repeat_spread": round(max(repeats) / min(repeats) - 1.0, 4),
         "us_per_call_T1": us_t1,
         "config1_us_per_call": config1,
         "roofline": roofline,

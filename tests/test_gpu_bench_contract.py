@@ -45,6 +45,10 @@ def test_bench_json_contract():
     assert 0 < rf["frac"] < 1
     assert rf["traffic"] is None or rf["traffic"] > rf["algorithmic_bytes_per_launch"] * 0.9
     assert rf["copy_ceiling_GBps"] > 0 and rf["of_copy"] > 0
+    # the null arm: the same 20 steps twice more; `value` is the first run
+    reps = d["repeats_us_per_step"]
+    assert len(reps) == 3 and reps[0] == pytest.approx(1000 * d["ms_per_step"], abs=2e-3)
+    assert d["repeat_spread"] == pytest.approx(max(reps) / min(reps) - 1, abs=2e-3)
     assert "cpu_baseline" not in d                      # --no-cpu
     assert 0 < d["us_per_call_T1"]["median"] < 50
     assert len(d["prefill"]) == 24
