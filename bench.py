@@ -1163,7 +1163,7 @@ def main():
         "metric": METRIC, "value": round(c.T / ms_per_step * 1e3, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"fused QK-RMSNorm+RoPE prologue, (Q,K)=({c.Q},{c.K}) heads, "
                                f"head_dim {c.D}, rot_dim {c.rot} rotate-half, 1+w weights, "
                                f"theta 1e7, T={c.T} tokens at positions 0..{c.T - 1}, bf16 "

@@ -32,7 +32,9 @@ def test_bench_json_contract():
         assert k in d, k
     assert d["n_gpus"] == 1 and d["steps"] == 20 and d["warmup"] == 5
     assert d["unit"] == "tokens/s" and d["higher_is_better"] is True
-    assert d["dtype"] == "bf16" and d["data"] == "synthetic" and d["vs_baseline"] is None
+    # dtype is the arithmetic type (fp32 throughout); the storage type is io_dtype
+    assert d["dtype"] == "f32" and d["config"]["io_dtype"] == "bf16"
+    assert d["data"] == "synthetic" and d["vs_baseline"] is None
     assert "workload" in d["config"] and d["config"]["tokens"] == 2048
     # tokens per second = the cell's tokens over the time of one step
     assert d["value"] == pytest.approx(2048 / (d["ms_per_step"] * 1e-3), rel=1e-3)
