@@ -377,7 +377,7 @@ MBT_API mbt_status mbt_quantize_fp8(const float* x, uint8_t* y, int64_t n, float
  * pays only those, so the fastest chunks_per_lane at a byte count is the
  * floor a fused kernel moving that many bytes is measured against.
  *  src [nbytes] read; dst [nbytes] written; must not overlap at all.
- *  0 <= nbytes <= 2^44, a multiple of 16 (MBT_ERR_BAD_SHAPE); src and dst
+ *  0 <= nbytes <= 2^40, a multiple of 16 (MBT_ERR_BAD_SHAPE); src and dst
  *  16-byte aligned (MBT_ERR_ALIGN); chunks_per_lane 1, 2, 4 or 8
  *  (MBT_ERR_BAD_ENUM).  nbytes == 0 is a no-op.
  */

@@ -652,8 +652,9 @@ mbt_status mbt_quantize_fp8(const float* x, uint8_t* y, int64_t n, float inv_sca
 
 mbt_status mbt_stream_copy(const void* src, void* dst, int64_t nbytes, int32_t chunks_per_lane,
                            void* stream) {
-    if (nbytes < 0 || nbytes % 16 != 0 || nbytes > (INT64_C(1) << 44))
-        return fail(MBT_ERR_BAD_SHAPE, "nbytes=%lld must be a multiple of 16 in [0, 2^44]",
+    // 2^40 bytes at one 16-byte chunk per lane is 2^28 blocks: every form launches
+    if (nbytes < 0 || nbytes % 16 != 0 || nbytes > (INT64_C(1) << 40))
+        return fail(MBT_ERR_BAD_SHAPE, "nbytes=%lld must be a multiple of 16 in [0, 2^40]",
                     (long long)nbytes);
     if (chunks_per_lane != 1 && chunks_per_lane != 2 && chunks_per_lane != 4 &&
         chunks_per_lane != 8)

@@ -200,7 +200,7 @@ def test_stream_copy_rejects(lib):
     c = lib.mbt_stream_copy
     assert c(A, B, -16, 1, None) == SHAPE
     assert c(A, B, 24, 1, None) == SHAPE            # not a multiple of 16
-    assert c(A, B, 2**44 + 16, 1, None) == SHAPE
+    assert c(A, B, 2**40 + 16, 1, None) == SHAPE
     assert c(A, B, 4096, 3, None) == ENUM
     assert c(A, B, 4096, 16, None) == ENUM
     assert c(None, B, 4096, 1, None) == NULLP
