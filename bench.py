@@ -632,6 +632,21 @@ def stream_copy_us(torch, mbt, nbytes, launches=1000, chunks=(1, 2, 4, 8)):
     return out
 
 
+def copy_warm_us(torch, mbt, nbytes, samples=200, inner=32):
+    """The streaming copy of nbytes (nbytes/2 read, nbytes/2 written) by the
+    T = 1 method: a graph of 32 calls on one buffer set, 20 warm-up replays,
+    the median of `samples` replays.  The floor for a decode-width call that
+    moves those bytes."""
+    half = max(16, nbytes // 2 // 16 * 16)
+    src = torch.empty(half, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty(half, dtype=torch.uint8, device="cuda:0")
+    g = capture(torch, lambda _: mbt.stream_copy(src, dst, 1), inner)
+    for _ in range(20):
+        g.replay()
+    xs = [1000.0 * timed_replays(torch, [g]) / inner for _ in range(samples)]
+    return median(xs)
+
+
 def copy_ceiling_gbps(torch, nbytes, launches=1000):
     """torch's device copy of nbytes/2 -> nbytes/2 (nbytes of traffic), cold."""
     half = max(16, nbytes // 2)
@@ -1132,6 +1147,8 @@ def main():
     us_t1 = {k: round(v, 3) for k, v in w1.items()}
     us_t1["method"] = ("(16,2) D256 rot64 bf16, graph of 32 calls on one buffer set, 20 warm-up "
                        "replays, median / quartiles of 200 replays; stream = direct launches")
+    # the same method on the library's streaming copy of the call's bytes
+    us_t1["copy_floor_us"] = round(copy_warm_us(torch, mbt, t1.bytes_algorithmic()), 3)
 
     # configuration 1: the Qwen3-style cell (head_dim 128, full rotary,
     # (16, 8) heads, T = 4, one token outside the cache), same method
