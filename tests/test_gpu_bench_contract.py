@@ -56,3 +56,25 @@ def test_bench_json_contract():
     assert len(d["prefill"]) == 24
     for c in d["prefill"]:
         assert c["T"] >= 256 and 0 < c["frac_peak"] < 1 and c["copy_us"] > 0
+
+
+@pytest.mark.parametrize("args,key", [
+    (["--only", "prologue_prefill", "--steps", "30"], "launches"),
+    (["--only", "norm_fp8", "--steps", "30"], "launches"),
+    (["--only", "prologue", "--steps", "30"], "launches"),
+    (["--only", "act_fp8", "--steps", "30"], "launches"),
+    (["--copy-probe", "1048576"], "copy_probe_bytes_moved"),
+])
+def test_bench_profiling_aids(args, key):
+    # the commands the committed profiles name: each prints one JSON line
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print("bench.py", *args, flush=True)
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), *args],
+                       capture_output=True, text=True, timeout=110, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout[-2000:]
+    d = json.loads(lines[0])
+    assert d[key] > 0
