@@ -1314,6 +1314,20 @@ def main():
                         "GBps": round(x.bytes_algorithmic() / us / 1e3, 1),
                         "frac_peak": round(x.bytes_algorithmic() / us / 1e3 / PEAK_HBM_GBPS, 4)})
         out["adarms_fp8_gated"] = ada
+        # the headline held for about a quarter of a second: twelve runs of
+        # 2000 steps back to back (after every other GPU figure, so a machine
+        # that lowers its clocks under sustained streaming slows nothing else)
+        phase("sustained headline")
+        hs = Headline(torch, mbt, W)
+        rs = Steps(torch, hs.step, hs.R)
+        rs.prepare([2000] * 12)
+        per = [1000.0 * rs.run(2000) / 2000 for _ in range(12)]
+        out["headline_sustained"] = {
+            "us_per_step_by_run": [round(x, 3) for x in per],
+            "first_over_last": round(per[0] / per[-1], 4),
+            "method": "12 back-to-back timed runs of 2000 headline steps on the same ring"}
+        del rs, hs
+        torch.cuda.empty_cache()
 
     if not args.no_cpu:
         phase("oracle on the host CPU")
