@@ -23,7 +23,7 @@ decode-layer step (norm -> FP8, prologue, norm -> FP8, SiLU -> FP8 at
 T = 128); the residual-norm and activation sweeps; the fused-vs-split route
 comparison; the extended prologue forms; the oracle timed on the host CPU.
 
-    python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-cpu] [--sustained]
 
 Profiling aids (each runs committed code only):
 
@@ -102,6 +102,9 @@ def parse_args():
     ap.add_argument("--no-sweep", action="store_true",
                     help="headline, T = 1 and the prefill fractions only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--sustained", action="store_true",
+                    help="also time the headline over twelve back-to-back runs of 2000 steps "
+                         "(headline_sustained), after every other GPU figure")
     ap.add_argument("--only", default=None,
                     choices=["prologue_prefill", "prefill_cells", "norm_fp8", "prologue",
                              "act_fp8"],
@@ -1314,6 +1317,7 @@ def main():
                         "GBps": round(x.bytes_algorithmic() / us / 1e3, 1),
                         "frac_peak": round(x.bytes_algorithmic() / us / 1e3 / PEAK_HBM_GBPS, 4)})
         out["adarms_fp8_gated"] = ada
+    if args.sustained:
         # the headline held for about a quarter of a second: twelve runs of
         # 2000 steps back to back (after every other GPU figure, so a machine
         # that lowers its clocks under sustained streaming slows nothing else)
