@@ -617,9 +617,19 @@ def act_cold_us(torch, mbt, W, cell, inv_scale=1.0, launches=1500):
     return us, ring_mode(cell.bytes_algorithmic(), R)
 
 
-def stream_copy_us(torch, mbt, nbytes, launches=1000, chunks=(1, 2, 4, 8)):
+# the streaming copy's forms: (16-byte chunks per lane, block barrier between
+# a block's loads and its stores), labelled "C" or "C+sync"
+COPY_FORMS = [(c, s) for s in (False, True) for c in (1, 2, 4, 8)]
+
+
+def copy_form_label(form):
+    c, s = form
+    return f"{c}+sync" if s else str(c)
+
+
+def stream_copy_us(torch, mbt, nbytes, launches=1000, forms=COPY_FORMS):
     """Cold µs per launch of the library's streaming copy moving nbytes
-    (nbytes/2 read, nbytes/2 written) at each chunks-per-lane value."""
+    (nbytes/2 read, nbytes/2 written) in each of its forms."""
     half = max(16, nbytes // 2 // 16 * 16)
     # callers ask only for byte counts whose own ring is cold; rounding down
     # to 16 bytes may add a slot, which must not turn into a refusal
@@ -627,9 +637,10 @@ def stream_copy_us(torch, mbt, nbytes, launches=1000, chunks=(1, 2, 4, 8)):
     src = [torch.empty(half, dtype=torch.uint8, device="cuda:0") for _ in range(R)]
     dst = [torch.empty(half, dtype=torch.uint8, device="cuda:0") for _ in range(R)]
     out = {}
-    for c in chunks:
-        out[c] = kernel_time_us(torch, lambda j, c=c: mbt.stream_copy(src[j], dst[j], c), R,
-                                launches)
+    for c, sy in forms:
+        out[copy_form_label((c, sy))] = kernel_time_us(
+            torch, lambda j, c=c, sy=sy: mbt.stream_copy(src[j], dst[j], c, block_sync=sy), R,
+            launches)
     del src, dst
     torch.cuda.empty_cache()
     return out
@@ -875,8 +886,9 @@ def write_profiles(d):
         for b, forms in bj.get("copy_ceilings_us", {}).items():
             half = int(b) // 2 // 16 * 16
             for k, v in forms.items():
-                g = -(-half // 16 // (256 * int(k))) * 256
-                ev[(f"stream_copy<{k}>", str(g))] = (int(b), v)
+                c, sync = int(k.split("+")[0]), k.endswith("+sync")
+                g = -(-half // 16 // (256 * c)) * 256
+                ev[(f"stream_copy<{c}, {'true' if sync else 'false'}>", str(g))] = (int(b), v)
         rows_cp = []
         for r in cp:
             b, e = ev.get((r["Name"], r["Grid"].split("x")[0]), (None, None))
@@ -885,7 +897,8 @@ def write_profiles(d):
                            f"{us(r, 'AverageNs'):.3f} | {us(r, 'MedianNs'):.3f} | "
                            f"{'' if e is None else e} |")
         md += ["", "## The streaming copy (copy ceilings of the prefill cells)", "",
-               "`stream_copy<C>`: C 16-byte chunks per lane, one launch copying half a cell's "
+               "`stream_copy<C, sync>`: C 16-byte chunks per lane, with or without a block "
+               "barrier between a block's loads and its stores; one launch copies half a cell's "
                "bytes into the other half.  The last column is the unprofiled run's HIP-event "
                "average for the same launch shape.  The copy does no arithmetic, so where the "
                "traced average exceeds the event time (launches of a few microseconds), the "
@@ -1127,7 +1140,7 @@ def main():
                 "algorithmic_bytes_per_launch": h.bytes, "avg_launch_us": round(us_launch, 3),
                 "rocprof_avg_us": rp_avg, "rocprof_median_us": rp_med}
     phase("copy ceilings")
-    copies = {}                  # bytes -> {chunks per lane: µs}, the streaming copy
+    copies = {}                  # bytes -> {form: µs}, the streaming copy
 
     def best_copy(nbytes):
         if nbytes not in copies:
@@ -1138,7 +1151,7 @@ def main():
     cu, ck = best_copy(h.bytes)
     roofline["copy_ceiling_GBps"] = round(h.bytes / cu / 1e3, 1)
     roofline["copy_ceiling_us"] = round(cu, 3)
-    roofline["copy_ceiling_kernel"] = f"mbt_stream_copy, {ck} chunk(s) of 16 B per lane, cold"
+    roofline["copy_ceiling_kernel"] = f"mbt_stream_copy, form {ck} (chunks per lane, block sync), cold"
     roofline["of_copy"] = round(cu / us_launch, 4)
     roofline["torch_copy_GBps"] = round(copy_ceiling_gbps(torch, h.bytes), 1)
     del run, h
@@ -1176,7 +1189,7 @@ def main():
             "tokens_per_s": round(x.T / us * 1e6, 1), "rocprof_avg_us": ra,
             "rocprof_frac_peak": None if ra is None else
             round(x.bytes_algorithmic() / ra / 1e3 / PEAK_HBM_GBPS, 4),
-            "copy_us": round(cu, 3), "copy_chunks_per_lane": ck,
+            "copy_us": round(cu, 3), "copy_form": ck,
             "of_copy": round(cu / us, 4)})
 
     out = {
@@ -1221,7 +1234,7 @@ def main():
                           "GBps": round(nb / us / 1e3, 1),
                           "frac_peak": round(nb / us / 1e3 / PEAK_HBM_GBPS, 4),
                           "tokens_per_s": round(T / us * 1e6, 1), "copy_us": round(cu, 3),
-                          "copy_chunks_per_lane": ck, "of_copy": round(cu / us, 4)})
+                          "copy_form": ck, "of_copy": round(cu / us, 4)})
         out["prefill_large_24x4"] = large
         phase("decode sweep")
         sweep = []
@@ -1248,7 +1261,7 @@ def main():
             if mode == "cold":
                 # the in-place norm reads and writes equal bytes, like a copy
                 cu, ck = best_copy(x.bytes_algorithmic())
-                row.update({"copy_us": round(cu, 3), "copy_chunks_per_lane": ck,
+                row.update({"copy_us": round(cu, 3), "copy_form": ck,
                             "of_copy": round(cu / us, 4)})
             nsweep.append(row)
         out["norm_sweep_config4"] = nsweep
@@ -1338,8 +1351,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline(W, c, threads=1)
         n_thr = max(1, min(len(os.sched_getaffinity(0)), 16))
         out["cpu_baseline_threads"] = cpu_baseline(W, c, threads=n_thr)
-    # every streaming-copy ceiling taken above: bytes -> {chunks per lane: µs}
-    out["copy_ceilings_us"] = {str(b): {str(k): round(v, 3) for k, v in d.items()}
+    # every streaming-copy ceiling taken above: bytes -> {form: µs}
+    out["copy_ceilings_us"] = {str(b): {k: round(v, 3) for k, v in d.items()}
                                for b, d in sorted(copies.items())}
     print(json.dumps(out), flush=True)
 

@@ -372,17 +372,19 @@ MBT_API mbt_status mbt_quantize_fp8(const float* x, uint8_t* y, int64_t n, float
  * mbt_stream_copy -- calibration, not a step of the method: copies nbytes
  * from src to dst with the streaming (nontemporal) 16-byte loads and stores
  * the kernels above use, chunks_per_lane 16-byte chunks per lane, all loads
- * of a lane before its first store.  A memory-bound kernel pays a DRAM read,
+ * of a lane before its first store; with block_sync = 1 every load of a
+ * 256-lane block lands before any of its stores (a block barrier).  A memory-bound kernel pays a DRAM read,
  * a DRAM write and a launch (P3, the overview of its fused ops); this copy
  * pays only those, so the fastest chunks_per_lane at a byte count is the
  * floor a fused kernel moving that many bytes is measured against.
  *  src [nbytes] read; dst [nbytes] written; must not overlap at all.
  *  0 <= nbytes <= 2^40, a multiple of 16 (MBT_ERR_BAD_SHAPE); src and dst
- *  16-byte aligned (MBT_ERR_ALIGN); chunks_per_lane 1, 2, 4 or 8
- *  (MBT_ERR_BAD_ENUM).  nbytes == 0 is a no-op.
+ *  16-byte aligned (MBT_ERR_ALIGN); chunks_per_lane 1, 2, 4 or 8 and
+ *  block_sync 0 or 1 (MBT_ERR_BAD_ENUM).  nbytes == 0 is a no-op.
  */
 MBT_API mbt_status mbt_stream_copy(const void* src, void* dst, int64_t nbytes,
-                                   int32_t chunks_per_lane, void* stream);
+                                   int32_t chunks_per_lane, int32_t block_sync,
+                                   void* stream);
 
 /* Human-readable name of a status. */
 MBT_API const char* mbt_status_string(mbt_status s);

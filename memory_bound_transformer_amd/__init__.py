@@ -66,7 +66,7 @@ _SIGS = {
     "mbt_gated_act_fp8": [_vp, _vp, _f32, _i64, _i32, _i32, _i32, _vp],
     "mbt_gated_act_amax": [_vp, _vp, _i64, _i32, _i32, _i32, _vp],
     "mbt_quantize_fp8": [_vp, _vp, _i64, _f32, _vp],
-    "mbt_stream_copy": [_vp, _vp, _i64, _i32, _vp],
+    "mbt_stream_copy": [_vp, _vp, _i64, _i32, _i32, _vp],
 }
 for _name, _args in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -466,12 +466,14 @@ def quantize_fp8(x, inv_scale, y=None, stream=None):
     return y
 
 
-def stream_copy(src, dst, chunks_per_lane=1, stream=None):
+def stream_copy(src, dst, chunks_per_lane=1, block_sync=False, stream=None):
     """Calibration copy of src's bytes into dst (same byte count, 16-byte
-    aligned, disjoint) with the kernels' streaming loads and stores."""
+    aligned, disjoint) with the kernels' streaming loads and stores;
+    block_sync: every load of a block lands before any of its stores."""
     _dev(src, dst)
     n = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != n:
         raise ValueError(f"dst holds {dst.numel() * dst.element_size()} bytes, src {n}")
-    _check(_lib.mbt_stream_copy(_ptr(src), _ptr(dst), n, int(chunks_per_lane), _stream(stream)))
+    _check(_lib.mbt_stream_copy(_ptr(src), _ptr(dst), n, int(chunks_per_lane),
+                                int(bool(block_sync)), _stream(stream)))
     return dst

@@ -651,7 +651,7 @@ mbt_status mbt_quantize_fp8(const float* x, uint8_t* y, int64_t n, float inv_sca
 }
 
 mbt_status mbt_stream_copy(const void* src, void* dst, int64_t nbytes, int32_t chunks_per_lane,
-                           void* stream) {
+                           int32_t block_sync, void* stream) {
     // 2^40 bytes at one 16-byte chunk per lane is 2^28 blocks: every form launches
     if (nbytes < 0 || nbytes % 16 != 0 || nbytes > (INT64_C(1) << 40))
         return fail(MBT_ERR_BAD_SHAPE, "nbytes=%lld must be a multiple of 16 in [0, 2^40]",
@@ -659,6 +659,8 @@ mbt_status mbt_stream_copy(const void* src, void* dst, int64_t nbytes, int32_t c
     if (chunks_per_lane != 1 && chunks_per_lane != 2 && chunks_per_lane != 4 &&
         chunks_per_lane != 8)
         return fail(MBT_ERR_BAD_ENUM, "chunks_per_lane %d not 1, 2, 4 or 8", chunks_per_lane);
+    if (block_sync != 0 && block_sync != 1)
+        return fail(MBT_ERR_BAD_ENUM, "block_sync %d not 0 or 1", block_sync);
     if (nbytes == 0) return ok();
     if (!src || !dst) return fail(MBT_ERR_NULL_POINTER, "src and dst are required");
     if (!aligned(src, 16) || !aligned(dst, 16))
@@ -666,7 +668,7 @@ mbt_status mbt_stream_copy(const void* src, void* dst, int64_t nbytes, int32_t c
     if (overlap(Range{(const char*)src, nbytes, "src"}, Range{(const char*)dst, nbytes, "dst"}))
         return fail(MBT_ERR_ALIAS, "dst overlaps src");
     return hip_status(mbt::launch_stream_copy(src, dst, nbytes, chunks_per_lane,
-                                              (hipStream_t)stream),
+                                              block_sync != 0, (hipStream_t)stream),
                       "stream_copy launch");
 }
 

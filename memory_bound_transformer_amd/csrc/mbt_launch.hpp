@@ -93,8 +93,9 @@ hipError_t launch_gated_act(const ActArgs& a, hipStream_t s);
 hipError_t launch_quantize_fp8(const float* x, uint8_t* y, int64_t n, float inv_scale,
                                hipStream_t s);
 // nbytes a multiple of 16, src and dst 16-byte aligned and disjoint;
-// chunks (16-byte chunks per lane) 1, 2, 4 or 8
+// chunks (16-byte chunks per lane) 1, 2, 4 or 8; block_sync: a block's loads
+// all land before any of its waves stores
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t nbytes, int chunks,
-                              hipStream_t s);
+                              bool block_sync, hipStream_t s);
 
 }  // namespace mbt

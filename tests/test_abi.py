@@ -50,7 +50,7 @@ def lib():
         "mbt_gated_act_fp8": [vp, vp, f32, i64, i32, i32, i32, vp],
         "mbt_gated_act_amax": [vp, vp, i64, i32, i32, i32, vp],
         "mbt_quantize_fp8": [vp, vp, i64, f32, vp],
-        "mbt_stream_copy": [vp, vp, i64, i32, vp],
+        "mbt_stream_copy": [vp, vp, i64, i32, i32, vp],
     }
     for name, args in sigs.items():
         getattr(lib, name).argtypes = args
@@ -198,19 +198,21 @@ def test_act_rejects(lib):
 
 def test_stream_copy_rejects(lib):
     c = lib.mbt_stream_copy
-    assert c(A, B, -16, 1, None) == SHAPE
-    assert c(A, B, 24, 1, None) == SHAPE            # not a multiple of 16
-    assert c(A, B, 2**40 + 16, 1, None) == SHAPE
-    assert c(A, B, 4096, 3, None) == ENUM
-    assert c(A, B, 4096, 16, None) == ENUM
-    assert c(None, B, 4096, 1, None) == NULLP
-    assert c(A, None, 4096, 1, None) == NULLP
-    assert c(A + 8, B, 4096, 1, None) == ALIGN
-    assert c(A, B + 4, 4096, 1, None) == ALIGN
-    assert c(A, A, 4096, 1, None) == ALIAS          # no in-place form
-    assert c(A, A + 2048, 4096, 2, None) == ALIAS
-    assert c(A + 2048, A, 4096, 4, None) == ALIAS
-    assert c(None, None, 0, 8, None) == OK
+    assert c(A, B, -16, 1, 0, None) == SHAPE
+    assert c(A, B, 24, 1, 0, None) == SHAPE         # not a multiple of 16
+    assert c(A, B, 2**40 + 16, 1, 0, None) == SHAPE
+    assert c(A, B, 4096, 3, 0, None) == ENUM
+    assert c(A, B, 4096, 16, 1, None) == ENUM
+    assert c(A, B, 4096, 4, 2, None) == ENUM        # block_sync 0 or 1
+    assert c(A, B, 4096, 4, -1, None) == ENUM
+    assert c(None, B, 4096, 1, 0, None) == NULLP
+    assert c(A, None, 4096, 1, 1, None) == NULLP
+    assert c(A + 8, B, 4096, 1, 0, None) == ALIGN
+    assert c(A, B + 4, 4096, 1, 1, None) == ALIGN
+    assert c(A, A, 4096, 1, 0, None) == ALIAS       # no in-place form
+    assert c(A, A + 2048, 4096, 2, 1, None) == ALIAS
+    assert c(A + 2048, A, 4096, 4, 0, None) == ALIAS
+    assert c(None, None, 0, 8, 1, None) == OK
 
 
 def test_rope_rejects(lib):

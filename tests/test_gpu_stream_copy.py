@@ -26,32 +26,34 @@ def _bytes(n, seed):
     return torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda:0", generator=g)
 
 
-def _check(mbt, nbytes, chunks, seed, src_offset=0):
-    print(f"stream_copy nbytes={nbytes} chunks={chunks} src_offset={src_offset}", flush=True)
+def _check(mbt, nbytes, chunks, seed, src_offset=0, sync=False):
+    print(f"stream_copy nbytes={nbytes} chunks={chunks} sync={sync} src_offset={src_offset}",
+          flush=True)
     src_buf = _bytes(nbytes + src_offset, seed)
     src = src_buf[src_offset:src_offset + nbytes]
     buf = torch.full((GUARD + nbytes + GUARD,), SENTINEL, dtype=torch.uint8, device="cuda:0")
     dst = buf[GUARD:GUARD + nbytes]
-    mbt.stream_copy(src, dst, chunks)
+    mbt.stream_copy(src, dst, chunks, block_sync=sync)
     torch.cuda.synchronize()
     assert torch.equal(dst, src), f"copy differs at nbytes={nbytes} chunks={chunks}"
     assert bool((buf[:GUARD] == SENTINEL).all()), "bytes before dst written"
     assert bool((buf[GUARD + nbytes:] == SENTINEL).all()), "bytes after dst written"
 
 
+@pytest.mark.parametrize("sync", [False, True])
 @pytest.mark.parametrize("chunks", [1, 2, 4, 8])
 @pytest.mark.parametrize("blocks,tail", [(0, 1), (0, 37), (1, 0), (3, 0), (3, 1), (5, 255),
                                          (7, 64 * 3 + 5)])
-def test_stream_copy_sizes(mbt, chunks, blocks, tail):
+def test_stream_copy_sizes(mbt, chunks, blocks, tail, sync):
     # a block is 256 lanes x chunks x 16 bytes; `tail` more 16-byte chunks
     nbytes = (blocks * 256 * chunks + tail) * 16
-    _check(mbt, nbytes, chunks, seed=1000 * chunks + 10 * blocks + tail)
+    _check(mbt, nbytes, chunks, seed=1000 * chunks + 10 * blocks + tail, sync=sync)
 
 
-@pytest.mark.parametrize("chunks", [1, 4])
-def test_stream_copy_large(mbt, chunks):
+@pytest.mark.parametrize("chunks,sync", [(1, False), (4, False), (8, True)])
+def test_stream_copy_large(mbt, chunks, sync):
     # many blocks, the last one ragged: 64 MiB + 48 bytes
-    _check(mbt, (64 << 20) + 48, chunks, seed=77 + chunks)
+    _check(mbt, (64 << 20) + 48, chunks, seed=77 + chunks, sync=sync)
 
 
 def test_stream_copy_unaligned_to_blocks(mbt):
@@ -62,6 +64,7 @@ def test_stream_copy_unaligned_to_blocks(mbt):
 def test_stream_copy_empty_and_rejects(mbt):
     a = torch.zeros(64, dtype=torch.uint8, device="cuda:0")
     mbt.stream_copy(a[:0], a[:0], 4)              # nbytes 0: no-op
+    mbt.stream_copy(a[:0], a[:0], 8, block_sync=True)
     with pytest.raises(mbt.MbtError):
         mbt.stream_copy(a[:48], a[16:64], 1)       # overlap
     with pytest.raises(mbt.MbtError):
