@@ -89,3 +89,10 @@ def test_broadcast_and_overlapping_views_refused():
     # no heads: nothing is addressed, so any stride passes
     mbt._token_stride(torch.zeros(4, 0, 8), "k")
     mbt._token_stride(torch.zeros(1, 0, 8).expand(4, 0, 8), "k")
+
+
+def test_stream_copy_refuses_host_tensors():
+    # the calibration copy takes device tensors only; the check comes first
+    a = torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        mbt.stream_copy(a[:32], a[32:], 1)
