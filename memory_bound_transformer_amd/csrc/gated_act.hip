@@ -13,10 +13,12 @@
 // MI355X design: a pure stream.  Each lane moves one 16-byte chunk of g and
 // the matching chunk of u (8 bf16 / fp16 or 4 fp32) and stores 16 bytes of
 // output or 8 / 4 packed e4m3fn codes; a 256-thread block covers U chunks per
-// lane of one token's row, so the token index is a scalar division per block,
-// not per lane.  sigmoid is evaluated from e^-|x| so it can neither overflow
-// nor cancel; 16-bit I/O takes e^-|x| from the hardware exp2 (with a rescale
-// that keeps results below FLT_MIN), fp32 I/O from the full-accuracy expf.
+// lane of one token's row (or, where rows are whole 256-chunk groups, two
+// groups that may lie in consecutive rows), so the token index is a scalar
+// division per block, not per lane.  sigmoid is evaluated from e^-|x| so it
+// can neither overflow nor cancel; 16-bit I/O takes e^-|x| from the hardware
+// exp2 (with a rescale that keeps results below FLT_MIN), fp32 I/O from the
+// full-accuracy expf.
 
 #include <stdlib.h>
 
@@ -61,22 +63,21 @@ __device__ __forceinline__ float sigmoid(float x) {
     return x >= 0.0f ? r : e * r;
 }
 
-// sigmoid(2z).  For 16-bit I/O the doubling goes into exp_neg's constant:
-// |2z| (-log2(e) / 2) and |z| (-log2(e)) are the same real product (scaling
-// by 2 is exact, in the constant too), rounded once either way, and 2z has
-// z's sign, so the result is sigmoid<DT>(2z)'s bits with one instruction
-// fewer per element.
-template <int DT>
-__device__ __forceinline__ float sigmoid2(float z) {
-    if constexpr (DT == kF32) {
-        return sigmoid<DT>(2.0f * z);
-    } else {
-        constexpr float k = 2.0f * -0.72134752044448170f;
-        const float h = __builtin_amdgcn_exp2f(fabsf(z) * k);
-        const float e = h * h;
-        const float r = __builtin_amdgcn_rcpf(1.0f + e);
-        return z >= 0.0f ? r : e * r;
-    }
+// GELU-tanh for 16-bit I/O.  z = sqrt(2/pi) g (1 + 0.044715 g^2) and the
+// bracket is positive, so z has g's sign and |z| = |g| sqrt(2/pi) (1 +
+// 0.044715 g^2): with k1 = -log2(e) sqrt(2/pi) and k3 = 0.044715 k1,
+// h = 2^(|g| (k1 + k3 g^2)) = e^-|z| takes one multiply and one FMA
+// beside the exp2 (against five instructions for z and one for its scaled
+// magnitude), e^-|2z| = h^2 as in exp_neg, and the sign test reads g.  The
+// exponent rounds differently from the oracle's z, by a few fp32 ulps, far
+// inside the output's 16-bit rounding.
+__device__ __forceinline__ float gelu_tanh16(float g) {
+    constexpr float k1 = -1.44269504088896341f * 0.7978845608f;
+    constexpr float k3 = k1 * 0.044715f;
+    const float h = __builtin_amdgcn_exp2f(fabsf(g) * fmaf(k3, g * g, k1));
+    const float e = h * h;
+    const float r = __builtin_amdgcn_rcpf(1.0f + e);
+    return g * (g >= 0.0f ? r : e * r);
 }
 
 template <int DT, int ACT>
@@ -84,9 +85,11 @@ __device__ __forceinline__ float act_mul(float g, float u) {
     float a;
     if constexpr (ACT == 0) {
         a = g * sigmoid<DT>(g);
-    } else {
+    } else if constexpr (DT == kF32) {
         const float z = 0.7978845608f * (g + 0.044715f * g * g * g);
-        a = g * sigmoid2<DT>(z);
+        a = g * sigmoid<DT>(2.0f * z);
+    } else {
+        a = gelu_tanh16(g);
     }
     return a * u;
 }
@@ -137,6 +140,81 @@ __global__ __launch_bounds__(256) void gated_vec(ActParams p) {
         if constexpr (MODE == kActDtype) {
             buf_st16_nt(ro, ch * 16u, pack<DT>(y));
         } else if constexpr (MODE == kActFp8) {
+            if constexpr (V == 8) {
+                u32x2 c;
+                c[0] = fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
+                             y[3] * p.inv_scale);
+                c[1] = fp8x4(y[4] * p.inv_scale, y[5] * p.inv_scale, y[6] * p.inv_scale,
+                             y[7] * p.inv_scale);
+                buf_st8_nt(ro, ch * 8u, c);
+            } else {
+                buf_st4_nt(ro, ch * 4u, fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale,
+                                              y[2] * p.inv_scale, y[3] * p.inv_scale));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; ++i) amax_acc = fmaxf(amax_acc, fabsf(y[i]));
+        }
+    }
+    if constexpr (MODE == kActAmax) {
+        amax_acc = seg_max<64>(amax_acc);
+        if ((threadIdx.x & 63) == 0) atomic_max_nonneg(p.amax, amax_acc);
+    }
+}
+
+// Flat-group kernel: used where a row is a whole number gpr >= 2 of
+// 256-chunk groups (d a multiple of 256 Vec) and lanes take two chunks.
+// Block b takes groups 2b and 2b + 1 of the T gpr groups in row-major order,
+// which may lie in consecutive rows, so every lane of every block has data;
+// with one block per pair of groups of a row, an odd gpr left half of each
+// row's last block without any (d = 10240 bf16: gpr = 5, a sixth of the
+// waves' arithmetic spent on zeros).  A group past the last row gets empty
+// buffer resources: its loads read zeros and its stores are dropped.
+template <int DT, int ACT, int MODE>
+__global__ __launch_bounds__(256) void gated_flat(ActParams p) {
+    constexpr int V = Vec<DT>::n;
+    constexpr int EB = EltBytes<DT>::n;
+    constexpr int U = 2;
+    asm volatile("" ::"s"(p.gate_up), "s"(p.d), "s"(p.blocks_per_row), "s"(p.T));
+    if constexpr (MODE == kActDtype) asm volatile("" ::"s"(p.out));
+    if constexpr (MODE == kActFp8) asm volatile("" ::"s"(p.out8), "s"(p.inv_scale));
+    if constexpr (MODE == kActAmax) asm volatile("" ::"s"(p.amax));
+    const uint32_t gpr = (uint32_t)p.blocks_per_row;      // groups per row
+    const uint32_t q0 = blockIdx.x * (uint32_t)U;
+    const uint32_t t0 = q0 / gpr;
+    const uint32_t c0 = q0 - t0 * gpr;
+    const uint32_t hb = (uint32_t)p.d * EB;                 // bytes of a half row
+    const int64_t ngroups = p.T * (int64_t)gpr;
+    int64_t tk[U];
+    uint32_t ck[U], live[U];
+    u32x4 gv[U], uv[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const uint32_t c = c0 + (uint32_t)k;
+        const uint32_t wrap = c >= gpr ? 1u : 0u;           // U <= gpr: one boundary at most
+        tk[k] = (int64_t)(t0 + wrap);
+        ck[k] = c - wrap * gpr;
+        live[k] = (int64_t)q0 + k < ngroups ? 1u : 0u;
+        const char* row = (const char*)p.gate_up + tk[k] * 2 * (int64_t)hb;
+        const uint32_t off = (ck[k] * 256u + threadIdx.x) * 16u;
+        gv[k] = buf_ld16_nt(buf_rsrc((void*)row, live[k] * hb), off);
+        uv[k] = buf_ld16_nt(buf_rsrc((void*)(row + hb), live[k] * hb), off);
+    }
+    asm volatile("" ::: "memory");
+    float amax_acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const uint32_t ch = ck[k] * 256u + threadIdx.x;
+        float g[V], u[V], y[V];
+        unpack<DT>(gv[k], g);
+        unpack<DT>(uv[k], u);
+#pragma unroll
+        for (int i = 0; i < V; ++i) y[i] = act_mul<DT, ACT>(g[i], u[i]);
+        if constexpr (MODE == kActDtype) {
+            buf_st16_nt(buf_rsrc((char*)p.out + tk[k] * (int64_t)hb, live[k] * hb), ch * 16u,
+                        pack<DT>(y));
+        } else if constexpr (MODE == kActFp8) {
+            const auto ro = buf_rsrc(p.out8 + tk[k] * (int64_t)p.d, live[k] * (uint32_t)p.d);
             if constexpr (V == 8) {
                 u32x2 c;
                 c[0] = fp8x4(y[0] * p.inv_scale, y[1] * p.inv_scale, y[2] * p.inv_scale,
@@ -272,6 +350,23 @@ hipError_t launch_mode(const ActArgs& a, hipStream_t s) {
         // Two chunks per lane only at prefill widths: at decode widths the
         // per-wave latency matters more than the per-wave overhead.
         const int U = (a.T * (int64_t)p.chunks >= kActU2Chunks) ? 2 : 1;
+        // Whole 256-chunk groups per row: the flat-group kernel, measured
+        // on MI355X at d = 10240 bf16 (five groups per row) against one
+        // block per pair of a row's groups, together with the GELU-tanh
+        // argument above: GELU -> FP8 T = 512 / 1024 / 2048 6.92 / 12.60 /
+        // 21.74 -> 6.14 / 10.72 / 19.83 us, SiLU -> FP8 6.10 / 11.47 / 19.84
+        // -> 5.99 / 10.35 / 19.43 us.  Three or four groups per block were
+        // slower at T = 384 - 512 (GELU -> FP8 T = 512: 6.14 -> 6.56 / 6.77
+        // us).
+        if (U == 2 && p.chunks % 256 == 0 && p.chunks >= 512) {
+            const int64_t groups = a.T * (int64_t)(p.chunks / 256);
+            if (groups < (int64_t(1) << 32)) {
+                p.blocks_per_row = p.chunks / 256;
+                hipLaunchKernelGGL((gated_flat<DT, ACT, MODE>), dim3((uint32_t)((groups + 1) / 2)),
+                                   dim3(256), 0, s, p);
+                return hipGetLastError();
+            }
+        }
         p.blocks_per_row = (p.chunks + 256 * U - 1) / (256 * U);
         const int64_t blocks = a.T * (int64_t)p.blocks_per_row;
         if (blocks <= 0x7FFFFFFFll) {

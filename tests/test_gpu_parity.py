@@ -479,6 +479,13 @@ EDGE_ACT = [
     _acell(name="full_fp8_T205", d=10240, T=205, act=W.GELU_TANH, fp8=True, cell=13),
     _acell(name="half_f16_fp8_d2056", dtype=W.F16, d=2056, T=7, act=W.GELU_TANH, fp8=True,
            cell=14),
+    # rows of whole 256-chunk groups with two chunks per lane take the
+    # flat-group kernel: an odd number of groups (the last block's second
+    # group past the last row) and blocks straddling two rows, in bf16
+    # (FP8 out and its calibration), fp16 and fp32
+    _acell(name="flat_odd_groups_fp8", d=10240, T=333, act=W.GELU_TANH, fp8=True, cell=15),
+    _acell(name="flat_f16_odd_groups", dtype=W.F16, d=10240, T=333, cell=16),
+    _acell(name="flat_f32_gpr3", dtype=W.F32, d=3072, T=521, act=W.GELU_TANH, cell=17),
 ]
 
 
@@ -493,15 +500,20 @@ def test_act_unaligned(mbt, orc, dtype):
                    offset=1)
 
 
-@pytest.mark.parametrize("rows", [1, 20, 50],
-                         ids=["half_chunk_per_lane", "one_chunk_per_lane", "two_chunks_per_lane"])
-def test_act_exhaustive_bf16_gate(mbt, orc, rows):
+@pytest.mark.parametrize("rows,pad", [(1, False), (20, False), (50, False), (50, True)],
+                         ids=["half_chunk_per_lane", "one_chunk_per_lane", "two_chunks_per_lane",
+                              "two_chunks_flat_groups"])
+def test_act_exhaustive_bf16_gate(mbt, orc, rows, pad):
     """Every finite bf16 gate value with up = 1: GPU vs oracle, <= 1 ulp.
     One row is a narrow launch (half a chunk per lane); 20 and 50 copies of
-    the row make it wide enough for one and two chunks per lane."""
+    the row make it wide enough for one and two chunks per lane.  Padded
+    with zeros to 65536 gate values, a row is 32 whole 256-chunk groups and
+    50 rows take the flat-group kernel."""
     bits = np.arange(65536, dtype=np.uint16)
     keep = np.isfinite(W.bits_to_f32(bits, W.BF16))
     bits = bits[keep]
+    if pad:
+        bits = np.concatenate([bits, np.zeros(65536 - bits.size, np.uint16)])
     gu = np.concatenate([bits, W.to_bits(np.ones(bits.size), W.BF16)])[None, :]
     gu = np.repeat(gu, rows, axis=0)
     for act in (W.SILU, W.GELU_TANH):
