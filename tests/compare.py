@@ -59,6 +59,13 @@ def check_prologue(gpu, ora, n_ora, cos_sin, pos, rot, layout, dtype, max_pos=No
     T, H, D = ora.shape
     if T * H * D == 0:
         return dict(n=0)
+    # a NaN matches any NaN and nothing else (a row holding a NaN is NaN
+    # throughout, its rotation included)
+    as_f = (lambda a: a.astype(np.float64)) if dtype == F32 else \
+        (lambda a: W.bits_to_f32(a, dtype).astype(np.float64))
+    nan_o = np.isnan(as_f(ora))
+    odd = int(np.count_nonzero(np.isnan(as_f(gpu)) != nan_o))
+    assert odd == 0, f"{label}: {odd} elements are NaN on one side only"
     mp = cos_sin.shape[0] if max_pos is None else max_pos
     pos = np.asarray(pos, np.int64)
     inr = (pos >= 0) & (pos < mp)
@@ -83,11 +90,12 @@ def check_prologue(gpu, ora, n_ora, cos_sin, pos, rot, layout, dtype, max_pos=No
         scale = np.abs(o)
         pair = np.hypot(n, n[..., part])
         scale = np.where(rotated, np.maximum(scale, pair), scale)
-        ok = np.abs(g - o) <= 1e-5 * scale + 1e-35
+        with np.errstate(invalid="ignore"):
+            ok = (g == o) | nan_o | (np.isfinite(o) & (np.abs(g - o) <= 1e-5 * scale + 1e-35))
         bad = int(np.count_nonzero(~ok))
         assert bad == 0, f"{label}: {bad} fp32 elements beyond rel 1e-5"
         return dict(n=ora.size, differ=int(np.count_nonzero(g != o)))
-    d = ulp16_dist(gpu, ora)
+    d = np.where(nan_o, 0, ulp16_dist(gpu, ora))
     ok = d <= 1
     esc_mask = (~ok) & rotated
     if np.any(esc_mask):
@@ -107,13 +115,25 @@ def check_prologue(gpu, ora, n_ora, cos_sin, pos, rot, layout, dtype, max_pos=No
 
 
 def check_values(gpu, ora, dtype, label="", max_differ_frac=0.005):
-    """Normalised / activated values: <= 1 ulp (bf16, fp16) or rel 1e-5 (fp32)."""
-    gpu, ora = np.asarray(gpu), np.asarray(ora)
+    """Normalised / activated values: <= 1 ulp (bf16, fp16) or rel 1e-5 (fp32).
+    A NaN matches any NaN (sign and payload carry nothing) and nothing else;
+    an infinity matches only the same infinity."""
+    gpu, ora = np.asarray(gpu).ravel(), np.asarray(ora).ravel()
     if ora.size == 0:
         return dict(n=0)
+    as_f = (lambda a: a.astype(np.float64)) if dtype == F32 else \
+        (lambda a: W.bits_to_f32(a, dtype).astype(np.float64))
+    gn, on = np.isnan(as_f(gpu)), np.isnan(as_f(ora))
+    odd = int(np.count_nonzero(gn != on))
+    assert odd == 0, f"{label}: {odd} elements are NaN on one side only"
+    gpu, ora = gpu[~on], ora[~on]
+    if ora.size == 0:
+        return dict(n=0, nan=int(np.count_nonzero(on)))
     if dtype == F32:
         g, o = gpu.astype(np.float64), ora.astype(np.float64)
-        bad = int(np.count_nonzero(np.abs(g - o) > 1e-5 * np.abs(o) + 1e-35))
+        with np.errstate(invalid="ignore"):
+            ok = (g == o) | (np.isfinite(o) & (np.abs(g - o) <= 1e-5 * np.abs(o) + 1e-35))
+        bad = int(np.count_nonzero(~ok))
         assert bad == 0, f"{label}: {bad} fp32 elements beyond rel 1e-5"
         return dict(n=ora.size, differ=int(np.count_nonzero(g != o)))
     d = ulp16_dist(gpu, ora)

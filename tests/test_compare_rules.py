@@ -78,6 +78,34 @@ def test_values_rule(dtype):
         C.check_values(many, ora, dtype)
 
 
+@pytest.mark.parametrize("dtype", [BF16, F16, F32])
+def test_values_rule_nan_and_inf(dtype):
+    vals = np.array([1.0, -2.5, np.inf, -np.inf, np.nan, 0.0], np.float32)
+    ora = vals if dtype == F32 else W.to_bits(vals, dtype)
+    C.check_values(ora.copy(), ora, dtype)
+    # a NaN of the other sign or another payload is still a NaN
+    other = ora.copy()
+    if dtype == F32:
+        other[4] = np.array([0xFFC00001], np.uint32).view(np.float32)[0]
+    else:
+        other[4] = 0xFF81 if dtype == BF16 else 0xFC01
+    C.check_values(other, ora, dtype)
+    # a NaN where the oracle has a number, and a number where it has a NaN
+    for i, v in ((0, np.nan), (4, 1.0)):
+        g = vals.copy()
+        g[i] = v
+        g = g if dtype == F32 else W.to_bits(g, dtype)
+        with pytest.raises(AssertionError, match="NaN on one side"):
+            C.check_values(g, ora, dtype)
+    # an infinity where the oracle has a finite value, or the other infinity
+    for i, v in ((1, np.inf), (2, -np.inf)):
+        g = vals.copy()
+        g[i] = v
+        g = g if dtype == F32 else W.to_bits(g, dtype)
+        with pytest.raises(AssertionError):
+            C.check_values(g, ora, dtype)
+
+
 def test_values_rule_fp32():
     ora = np.linspace(-3.0, 3.0, 1001, dtype=np.float32)
     near = (ora.astype(np.float64) * (1 + 0.9e-5)).astype(np.float32)
