@@ -14,6 +14,8 @@ and its calibration amax) in every dtype, at eps = 0 and eps > 0:
   x / sqrt(eps) (w + delta));
 * a random row beside them, as a control.
 
+And special gate and up values through the gated activation.
+
 The comparison rules are the parity tests' (compare.py); a NaN matches any
 NaN, since neither side's NaN payload or sign carries information.  Each row
 kind is repeated so that both the narrow (decode-width) and the wide launch
@@ -194,3 +196,34 @@ def test_prologue_degenerate_rows(mbt, orc, dtype, D, rot, layout, reps, eps):
             C.check_prologue(got, ora, n_ora, cs, pos, rot, layout, dtype, label=label)
             gf = got if dtype == W.F32 else W.bits_to_f32(got, dtype)
             expected_specials(names, gf[:n, 0, :], eps, label)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
+@pytest.mark.parametrize("d,T", [(1024, 4), (10240, 40), (1000, 3)],
+                         ids=["narrow", "wide", "scalar"])
+def test_act_degenerate_values(mbt, orc, dtype, d, T):
+    """Gate values +-inf, NaN, +-0, the largest finite magnitudes and
+    subnormals, against up values 1, +-inf, NaN, 0 and a random one: act(g) u
+    on the GPU agrees with the oracle (inf * 0 and NaN propagate as NaN on
+    both sides), to a dtype and to FP8."""
+    big = 3.0e38 if dtype != W.F16 else 65504.0
+    tiny = 2.0 ** -133 if dtype != W.F16 else 2.0 ** -24
+    gates = np.array([np.inf, -np.inf, np.nan, 0.0, -0.0, big, -big, tiny, -tiny, 1.5, -1.5,
+                      -90.0, 30.0], np.float32)
+    ups = np.array([1.0, np.inf, -np.inf, np.nan, 0.0, -2.0], np.float32)
+    gg, uu = np.meshgrid(gates, ups)
+    g_row, u_row = gg.ravel(), uu.ravel()                       # every pair once
+    rng = np.random.default_rng([5, dtype, d])
+    g = rng.standard_normal((T, d)).astype(np.float32)
+    u = rng.standard_normal((T, d)).astype(np.float32)
+    for t in range(T):                                          # the pairs in every row
+        at = (t * 97) % (d - g_row.size)
+        g[t, at:at + g_row.size] = g_row
+        u[t, at:at + u_row.size] = u_row
+    gu = W.to_bits(np.concatenate([g, u], axis=1), dtype)
+    print(f"act degenerate dtype={dtype} d={d} T={T}", flush=True)
+    for act in (W.SILU, W.GELU_TANH):
+        out = W.from_torch(mbt.gated_act(W.to_torch(gu, dtype, DEV), act), dtype)
+        C.check_values(out, orc.gated_act(gu, act, dtype), dtype, label=f"act {act}")
+        y = mbt.gated_act_fp8(W.to_torch(gu, dtype, DEV), 0.5, act).cpu().numpy()
+        C.check_fp8(y, orc.gated_act_fp8(gu, 0.5, act, dtype), label=f"act {act} fp8")
