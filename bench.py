@@ -1163,8 +1163,11 @@ def main():
     us_t1 = {k: round(v, 3) for k, v in w1.items()}
     us_t1["method"] = ("(16,2) D256 rot64 bf16, graph of 32 calls on one buffer set, 20 warm-up "
                        "replays, median / quartiles of 200 replays; stream = direct launches")
-    # the same method on the library's streaming copy of the call's bytes
+    # the same method on the library's streaming copy of the call's bytes,
+    # and on its smallest launch (one 16-byte chunk): what any kernel node
+    # in a graph costs here, whatever it moves
     us_t1["copy_floor_us"] = round(copy_warm_us(torch, mbt, t1.bytes_algorithmic()), 3)
+    us_t1["launch_floor_us"] = round(copy_warm_us(torch, mbt, 32), 3)
 
     # configuration 1: the Qwen3-style cell (head_dim 128, full rotary,
     # (16, 8) heads, T = 4, one token outside the cache), same method

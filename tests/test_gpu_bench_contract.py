@@ -52,7 +52,10 @@ def test_bench_json_contract():
     assert len(reps) == 3 and reps[0] == pytest.approx(1000 * d["ms_per_step"], abs=2e-3)
     assert d["repeat_spread"] == pytest.approx(max(reps) / min(reps) - 1, abs=2e-3)
     assert "cpu_baseline" not in d                      # --no-cpu
-    assert 0 < d["us_per_call_T1"]["median"] < 50
+    t1 = d["us_per_call_T1"]
+    assert 0 < t1["median"] < 50
+    # the smallest launch is a floor for every call, the T = 1 copy included
+    assert 0 < t1["launch_floor_us"] <= t1["copy_floor_us"] * 1.05
     assert len(d["prefill"]) == 24
     for c in d["prefill"]:
         assert c["T"] >= 256 and 0 < c["frac_peak"] < 1 and c["copy_us"] > 0
