@@ -597,8 +597,10 @@ __global__ __launch_bounds__(256) void qknorm_rope_scalar(QkParams p, QkGen<true
 // measured best on MI355X; every shape gives the same bits.
 constexpr int64_t kCWaves = 2560;
 // Interleaved pairs rotate in every chunk, so a lane's chain grows with its
-// chunks: those launches keep fewer chunks per lane, up to this many waves.
+// chunks: those launches keep fewer chunks per lane, up to this many waves
+// (one chunk per lane only up to kCWavesInterleaved1).
 constexpr int64_t kCWavesInterleaved = 8000;
+constexpr int64_t kCWavesInterleaved1 = 6000;
 constexpr int kCMax = 4;
 
 // Waves of a launch with G lanes per row.
@@ -709,13 +711,17 @@ hipError_t launch_dt(const QkArgs& a, hipStream_t s) {
         // with the 8000 bound against 2560: (24, 4) T = 256 / 512 / 1024 /
         // 2048 3.35 / 4.48 / 6.57 / 11.32 -> 3.26 / 4.37 / 6.43 / 11.14 us,
         // (16, 2) T = 512 / 1024 / 2048 3.66 / 5.28 / 7.94 -> 3.60 / 4.94 /
-        // 7.83 us.
+        // 7.83 us.  One chunk per lane only up to 6000 of those waves: (24, 4)
+        // T = 512 (7168 waves at one chunk, 3584 at two) 4.43 -> 4.26 us,
+        // every other configuration-3 cell unchanged; a single bound of
+        // 4000 also took T = 1024 to four chunks (6.44 -> 6.58 us).
         const int half = a.rot_dim / 2;
         const int rc = (a.rot_dim == 0) ? 0
                        : (a.layout == 0 ? 2 * (half / V) : (a.rot_dim + V - 1) / V);
         int C = 1;
         const int64_t cwaves = a.layout == 0 ? kCWaves : kCWavesInterleaved;
-        if (vec_waves(p, L) > cwaves) {
+        const int64_t c1waves = a.layout == 0 ? kCWaves : kCWavesInterleaved1;
+        if (vec_waves(p, L) > c1waves) {
             for (int cand : {2, 4}) {
                 const int G = L / cand;
                 if (cand > kCMax || G < 4 || (a.layout == 0 && G < rc)) continue;
