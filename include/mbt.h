@@ -21,9 +21,10 @@
  *  - Every value is decoded to fp32, all arithmetic and accumulation is fp32,
  *    and each output is rounded once to nearest-even (P1 section 3, R1).
  *  - All arguments are checked first, before the library computes an
- *    address or launches anything (P1 section 5.5); a rejected call enqueues nothing and returns the
- *    status below, with a detail string in mbt_last_error().  There is no
- *    fallback path: a configuration the kernels do not cover is an error.
+ *    address or launches anything (P1 section 5.5); a rejected call
+ *    enqueues nothing and returns the status below, with a detail string in
+ *    mbt_last_error().  There is no fallback path: a configuration the
+ *    kernels do not cover is an error.
  *  - T == 0 (no tokens / rows) is a successful no-op; NULL is an error only
  *    for a pointer the call needs when T > 0.
  *  - Any element-aligned pointer is accepted; 16-byte aligned, densely
