@@ -7,8 +7,9 @@ pairings, any head counts including zero of one kind, short and ragged token
 counts, caches of a few hundred rows with positions inside and outside them,
 both weight conventions, in place and unaligned storage; norm rows of any
 width with and without residual or weight, FP8 or dtype output; activation
-rows of any width -- so every launch-shape branch (vector or scalar kernel,
-chunks per lane, segment width) meets inputs it was not tuned on.  Each case
+rows of any width, and activation launches wide enough for two chunks per
+lane -- so every launch-shape branch (vector or scalar kernel, chunks per
+lane, segment width) meets inputs it was not tuned on.  Each case
 is fixed by its seed: `random_prologue_17` is always the same cell."""
 import numpy as np
 import pytest
@@ -69,6 +70,26 @@ def act_case(n):
     return cell, int(g.integers(0, 2))
 
 
+def prefill_act_case(n):
+    """Activation rows wide enough for two chunks per lane (at least 400k
+    chunks in the launch): half the widths whole 256-chunk groups (the
+    flat-group kernel), the others any multiple of the vector width (one
+    block per pair of a row's groups, the last one partly past d)."""
+    g = np.random.default_rng([90, n])
+    dtype = int(g.choice(DTYPES))
+    V = 4 if dtype == W.F32 else 8
+    if n % 2 == 0:
+        d = 256 * V * int(g.integers(2, 7))
+    else:
+        d = V * int(g.integers(300, 1600))
+    chunks = d // V
+    T = -(-int(g.integers(400_000, 1_200_000)) // chunks)
+    cell = W.ActCell(name=f"random_prefill_act_{n}", config=90, cell=n, T=T, d=d,
+                     act=int(g.integers(0, 2)), dtype=dtype,
+                     x_std=float(g.choice([1.5, 6.0])), fp8=bool(g.integers(0, 2)))
+    return cell, 0                              # aligned: the vector kernels
+
+
 @pytest.mark.parametrize("n", range(48), ids=lambda n: f"random_prologue_{n}")
 def test_random_prologue(mbt, orc, n):
     cell, kw = prologue_case(n)
@@ -88,6 +109,14 @@ def test_random_norm(mbt, orc, n):
 @pytest.mark.parametrize("n", range(24), ids=lambda n: f"random_act_{n}")
 def test_random_act(mbt, orc, n):
     cell, offset = act_case(n)
+    print(f"{cell.name}: T={cell.T} d={cell.d} act={cell.act} dtype={cell.dtype} "
+          f"fp8={cell.fp8} offset={offset}", flush=True)
+    check_act_cell(mbt, orc, cell, offset=offset)
+
+
+@pytest.mark.parametrize("n", range(12), ids=lambda n: f"random_prefill_act_{n}")
+def test_random_prefill_act(mbt, orc, n):
+    cell, offset = prefill_act_case(n)
     print(f"{cell.name}: T={cell.T} d={cell.d} act={cell.act} dtype={cell.dtype} "
           f"fp8={cell.fp8} offset={offset}", flush=True)
     check_act_cell(mbt, orc, cell, offset=offset)
