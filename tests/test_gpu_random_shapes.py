@@ -7,9 +7,10 @@ pairings, any head counts including zero of one kind, short and ragged token
 counts, caches of a few hundred rows with positions inside and outside them,
 both weight conventions, in place and unaligned storage; norm rows of any
 width with and without residual or weight, FP8 or dtype output; activation
-rows of any width, and activation launches wide enough for two chunks per
-lane -- so every launch-shape branch (vector or scalar kernel, chunks per
-lane, segment width) meets inputs it was not tuned on.  Each case
+rows of any width, and prologue and activation launches wide enough for
+two and four chunks per lane -- so every launch-shape branch (vector or
+scalar kernel, chunks per lane, load order, segment width) meets inputs it
+was not tuned on.  Each case
 is fixed by its seed: `random_prologue_17` is always the same cell."""
 import numpy as np
 import pytest
@@ -70,6 +71,27 @@ def act_case(n):
     return cell, int(g.integers(0, 2))
 
 
+def prefill_prologue_case(n):
+    """Prologue launches of 2k to 30k head-rows of the vector-kernel head
+    dims, so that two and four chunks per lane and every load order (by
+    wave count) meet head dims, rotary spans and head counts other than the
+    configurations'."""
+    g = np.random.default_rng([89, n])
+    D = int(g.choice([64, 128, 256, 512]))
+    rot = int(g.choice([D, D // 2, D // 4]))
+    Q, K = int(g.integers(1, 33)), int(g.integers(1, 9))
+    T = max(1, int(g.integers(2_000, 30_000)) // (Q + K))
+    mp = int(g.integers(T // 2, 2 * T))
+    delta = int(g.integers(0, 2))
+    cell = W.PrologueCell(
+        name=f"random_prefill_prologue_{n}", config=89, cell=n, T=T, Q=Q, K=K, D=D, rot=rot,
+        theta=float(10 ** g.uniform(4, 7)), layout=int(g.integers(0, 2)),
+        dtype=int(g.choice(DTYPES, p=[0.5, 0.3, 0.2])), weight_offset=delta,
+        w_mean=0.0 if delta else 1.0, w_std=0.05, x_std=2.0, eps=1e-6, max_pos=mp,
+        outside=((1, -1), (2, mp)))
+    return cell, dict(offset=0, in_place=bool(g.integers(0, 2)))
+
+
 def prefill_act_case(n):
     """Activation rows wide enough for two chunks per lane (at least 400k
     chunks in the launch): half the widths whole 256-chunk groups (the
@@ -120,3 +142,11 @@ def test_random_prefill_act(mbt, orc, n):
     print(f"{cell.name}: T={cell.T} d={cell.d} act={cell.act} dtype={cell.dtype} "
           f"fp8={cell.fp8} offset={offset}", flush=True)
     check_act_cell(mbt, orc, cell, offset=offset)
+
+
+@pytest.mark.parametrize("n", range(12), ids=lambda n: f"random_prefill_prologue_{n}")
+def test_random_prefill_prologue(mbt, orc, n):
+    cell, kw = prefill_prologue_case(n)
+    print(f"{cell.name}: T={cell.T} Q={cell.Q} K={cell.K} D={cell.D} rot={cell.rot} "
+          f"layout={cell.layout} dtype={cell.dtype} max_pos={cell.max_pos} {kw}", flush=True)
+    check_prologue_cell(mbt, orc, cell, **kw)
