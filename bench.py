@@ -907,6 +907,18 @@ def write_profiles(d):
                "| kernel | grid (work-items) | bytes moved | launches | average us | median us "
                "| bench.py events us |",
                "|---|---|---|---|---|---|---|", *rows_cp]
+    # the gated activation and the residual norm: every launch shape of them
+    # in the run (the configuration 4 and 5 sweeps, the decode-layer step,
+    # the split route's norms, the no-weight and adaptive norms)
+    for fam, title in (("gated_", "The gated activation"), ("rmsnorm_", "The residual norm")):
+        rs = sorted((r for r in groups_d.values() if fam in r["Name"]),
+                    key=lambda r: (r["Name"], int(r["Grid"].split("x")[0])))
+        if rs:
+            md += ["", f"## {title}: every launch shape in the run", "",
+                   "| kernel | grid (work-items) | launches | average us | median us |",
+                   "|---|---|---|---|---|",
+                   *[f"| `{r['Name']}` | {r['Grid'].split('x')[0]} | {r['Calls']} | "
+                     f"{us(r, 'AverageNs'):.3f} | {us(r, 'MedianNs'):.3f} |" for r in rs]]
     with open(os.path.join(P, "bench_default_kernel_trace.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     with open(os.path.join(P, "bench_default_kernel_trace.json"), "w") as f:
