@@ -20,8 +20,6 @@
 // exp2 (with a rescale that keeps results below FLT_MIN), fp32 I/O from the
 // full-accuracy expf.
 
-#include <stdlib.h>
-
 #include "mbt_device.hpp"
 #include "mbt_launch.hpp"
 

@@ -53,8 +53,6 @@
 // shape and alignment the vector kernel does not; it follows the same
 // reduction tree, so both give identical bits.
 
-#include <stdlib.h>
-
 #include "mbt_device.hpp"
 #include "mbt_launch.hpp"
 

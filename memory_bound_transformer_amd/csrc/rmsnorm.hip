@@ -38,8 +38,6 @@
 //  * Odd widths and unaligned pointers take a two-pass scalar kernel with
 //    the same tree.
 
-#include <stdlib.h>
-
 #include "mbt_device.hpp"
 #include "mbt_launch.hpp"
 
