@@ -61,8 +61,7 @@ def check_prologue(gpu, ora, n_ora, cos_sin, pos, rot, layout, dtype, max_pos=No
         return dict(n=0)
     # a NaN matches any NaN and nothing else (a row holding a NaN is NaN
     # throughout, its rotation included)
-    as_f = (lambda a: a.astype(np.float64)) if dtype == F32 else \
-        (lambda a: W.bits_to_f32(a, dtype).astype(np.float64))
+    as_f = (lambda a: a.astype(np.float64)) if dtype == F32 else _bits_f64(dtype)
     nan_o = np.isnan(as_f(ora))
     odd = int(np.count_nonzero(np.isnan(as_f(gpu)) != nan_o))
     assert odd == 0, f"{label}: {odd} elements are NaN on one side only"
@@ -114,6 +113,15 @@ def check_prologue(gpu, ora, n_ora, cos_sin, pos, rot, layout, dtype, max_pos=No
     return dict(n=d.size, differ=differ, escapes=int(np.count_nonzero(esc_mask)), max_ulp=worst)
 
 
+def _bits_f64(dtype):
+    """16-bit patterns -> float64 values; a signalling NaN pattern quietly
+    becomes a NaN (numpy flags the conversion as invalid)."""
+    def f(a):
+        with np.errstate(invalid="ignore"):
+            return W.bits_to_f32(a, dtype).astype(np.float64)
+    return f
+
+
 def check_values(gpu, ora, dtype, label="", max_differ_frac=0.005):
     """Normalised / activated values: <= 1 ulp (bf16, fp16) or rel 1e-5 (fp32).
     A NaN matches any NaN (sign and payload carry nothing) and nothing else;
@@ -121,8 +129,7 @@ def check_values(gpu, ora, dtype, label="", max_differ_frac=0.005):
     gpu, ora = np.asarray(gpu).ravel(), np.asarray(ora).ravel()
     if ora.size == 0:
         return dict(n=0)
-    as_f = (lambda a: a.astype(np.float64)) if dtype == F32 else \
-        (lambda a: W.bits_to_f32(a, dtype).astype(np.float64))
+    as_f = (lambda a: a.astype(np.float64)) if dtype == F32 else _bits_f64(dtype)
     gn, on = np.isnan(as_f(gpu)), np.isnan(as_f(ora))
     odd = int(np.count_nonzero(gn != on))
     assert odd == 0, f"{label}: {odd} elements are NaN on one side only"
