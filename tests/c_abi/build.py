@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
 SRC = os.path.join(HERE, "abi_roundtrip.c")
 EXE = os.path.join(HERE, "abi_roundtrip")
-ROCM = "/opt/rocm"
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
 def build(out=EXE):
