@@ -146,12 +146,24 @@ EDGE_PROLOGUE = [
           max_pos=4096, cell=36),
     _cell(name="c2_thr_rot96", D=256, rot=96, T=1024, Q=24, K=4, max_pos=4096, cell=37),
     _cell(name="c4_thr_f16_rot0", dtype=W.F16, D=256, rot=0, T=1024, Q=24, K=4, cell=38),
+    # a dense launch of one to one and a half resident rounds (8192 to
+    # 12288 waves) runs as two launches over the token halves: an even split
+    # with random positions, an odd one (the halves differ by a token) with
+    # in-place storage, and interleaved fp16; just past the bound, one launch
+    _cell(name="split_16x2_T4100", D=256, rot=64, T=4100, Q=16, K=2, max_pos=4096,
+          outside=((1, -1), (4099, 4096)), cell=40),
+    _cell(name="split_odd_24x4_T3001", D=256, rot=64, T=3001, Q=24, K=4, max_pos=4096,
+          positions="arange", in_place=True, cell=41),
+    _cell(name="split_inter_f16_T2500", dtype=W.F16, D=256, rot=256, layout=W.INTERLEAVED,
+          T=2500, Q=24, K=4, max_pos=4096, cell=42),
+    _cell(name="unsplit_24x4_T3512", D=256, rot=64, T=3512, Q=24, K=4, max_pos=4096,
+          positions="arange", cell=43),
 ]
 
 
 @pytest.mark.parametrize("cell", EDGE_PROLOGUE, ids=lambda c: c.name)
 def test_prologue_edges(mbt, orc, cell):
-    check_prologue_cell(mbt, orc, cell)
+    check_prologue_cell(mbt, orc, cell, in_place=cell.in_place)
 
 
 @pytest.mark.parametrize("T,layout", [(1024, W.ROTATE_HALF), (2048, W.ROTATE_HALF),
@@ -173,6 +185,28 @@ def test_prologue_width_invariant(mbt, T, layout):
     qo, ko = mbt.qknorm_rope(q, k, wq, wk, cs, pos, *args)
     qs, ks = torch.empty_like(q), torch.empty_like(k)
     for t0 in range(0, T, 16):
+        mbt.qknorm_rope(q[t0:t0 + 16], k[t0:t0 + 16], wq, wk, cs, pos[t0:t0 + 16], *args,
+                        q_out=qs[t0:t0 + 16], k_out=ks[t0:t0 + 16])
+    torch.cuda.synchronize()
+    assert torch.equal(qo.view(torch.int16), qs.view(torch.int16))
+    assert torch.equal(ko.view(torch.int16), ks.view(torch.int16))
+
+
+def test_prologue_split_invariant(mbt):
+    """A launch of one to one and a half resident rounds, run as two
+    launches over the token halves, gives the bits of the same tokens in
+    16-token launches."""
+    cell = [c for c in EDGE_PROLOGUE if c.name == "split_16x2_T4100"][0]
+    i = cell.inputs()
+    dt = cell.dtype
+    q, k = dev(i["q"], dt), dev(i["k"], dt)
+    wq, wk = dev(i["w_q"], dt), dev(i["w_k"], dt)
+    cs = torch.from_numpy(i["cos_sin"]).to(DEV)
+    pos = torch.from_numpy(i["pos"]).to(DEV)
+    args = (cell.rot, cell.eps, cell.weight_offset, cell.layout)
+    qo, ko = mbt.qknorm_rope(q, k, wq, wk, cs, pos, *args)
+    qs, ks = torch.empty_like(q), torch.empty_like(k)
+    for t0 in range(0, cell.T, 16):
         mbt.qknorm_rope(q[t0:t0 + 16], k[t0:t0 + 16], wq, wk, cs, pos[t0:t0 + 16], *args,
                         q_out=qs[t0:t0 + 16], k_out=ks[t0:t0 + 16])
     torch.cuda.synchronize()
