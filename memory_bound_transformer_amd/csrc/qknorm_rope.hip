@@ -735,44 +735,49 @@ hipError_t launch_dt(const QkArgs& a, hipStream_t s) {
         const bool gen = a.round_once || a.slot || a.v_in ||
                          (a.Q > 0 && (a.q_in_stride != qrow || a.q_out_stride != qrow)) ||
                          (a.K > 0 && (a.k_in_stride != krow || a.k_out_stride != krow));
-        if (gen)
-            return (a.layout == 0) ? launch_gc<DT, 0, true>(p, g, L, C, s)
-                                   : launch_gc<DT, 1, true>(p, g, L, C, s);
-        auto dense = [&](const QkParams& pp) {
+        auto run = [&](const QkParams& pp) {
+            if (gen)
+                return (a.layout == 0) ? launch_gc<DT, 0, true>(pp, g, L, C, s)
+                                       : launch_gc<DT, 1, true>(pp, g, L, C, s);
             return (a.layout == 0) ? launch_gc<DT, 0, false>(pp, g, L, C, s)
                                    : launch_gc<DT, 1, false>(pp, g, L, C, s);
         };
-        // A dense launch of more than one resident round but at most one and
-        // a half (8192 < waves <= 12288), whose second round would run half
-        // empty, runs as two launches over the two halves of the tokens,
-        // each within one round (the same bits: every row is computed
-        // alone).  Measured on MI355X, cold, D = 256 rot_dim 64 bf16, on
+        // A launch without a slot table or value rows, of more than one
+        // resident round but at most one and a half (8192 < waves <= 12288),
+        // whose second round would run half empty, runs as two launches over
+        // the two halves of the tokens, each within one round (the same
+        // bits: every row is computed alone).  Measured on MI355X, cold, D = 256 rot_dim 64 bf16, on
         // three machines: (16, 2) T = 4096 (9216 waves) 4.6-5.6 % faster on
         // each, (24, 4) T = 3072 (10752) 2.7-3.3 %, (16, 2) T = 5120
         // (11520) 2.5-4.6 %; from about 12500 waves the split was neither
         // reliably faster nor slower ((24, 4) T = 4096: -4.0 / +3.9 /
         // -0.9 %), and two launches of more than a round each were slower
-        // ((16, 2) T = 8192: 26.4 -> 29.6 us).
+        // ((16, 2) T = 8192: 26.4 -> 29.6 us).  q and k as strided views of a
+        // fused QKV buffer gain alike (2.0-4.0 % at the same widths); the
+        // KV-cache form, whose key waves also carry the value heads, was
+        // mixed (+11.6 % at (16, 2) T = 4096, -4.8 / -6.3 % at the others)
+        // and keeps one launch.
         const int64_t w = vec_waves(p, L / C);
-        if (w > kThrWavesHi && w <= kThrWavesHi + kThrWavesHi / 2 && a.T >= 2) {
+        if (!a.slot && !a.v_in && w > kThrWavesHi && w <= kThrWavesHi + kThrWavesHi / 2 &&
+            a.T >= 2) {
             const int64_t T1 = (a.T + 1) / 2;
             QkParams p2 = p;
             p.T = T1;
             p2.T = a.T - T1;
             if (a.Q > 0) {
-                p2.q_in = (const char*)a.q_in + T1 * qrow * EB;
-                p2.q_out = (char*)a.q_out + T1 * qrow * EB;
+                p2.q_in = (const char*)a.q_in + T1 * a.q_in_stride * EB;
+                p2.q_out = (char*)a.q_out + T1 * a.q_out_stride * EB;
             }
             if (a.K > 0) {
-                p2.k_in = (const char*)a.k_in + T1 * krow * EB;
-                p2.k_out = (char*)a.k_out + T1 * krow * EB;
+                p2.k_in = (const char*)a.k_in + T1 * a.k_in_stride * EB;
+                p2.k_out = (char*)a.k_out + T1 * a.k_out_stride * EB;
             }
             p2.pos = a.pos + T1;
-            const hipError_t e = dense(p);
+            const hipError_t e = run(p);
             if (e != hipSuccess) return e;
-            return dense(p2);
+            return run(p2);
         }
-        return dense(p);
+        return run(p);
     }
     const int64_t blocks = (a.T * (int64_t)(QK + (a.v_in ? a.K : 0)) + 3) / 4;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;

@@ -200,6 +200,10 @@ STRIDE_CELLS = [
     _cell(name="qkv_f16_inter", dtype=W.F16, rot=256, layout=W.INTERLEAVED, cell=43),
     _cell(name="qkv_bf16_mid_T999", Q=24, K=4, T=999, positions="arange", max_pos=4096,
           outside=(), cell=44),
+    # one to one and a half resident rounds (9225 waves): two launches over
+    # the token halves, at the views' own strides
+    _cell(name="qkv_bf16_split_16x2_T4100", Q=16, K=2, T=4100, positions="arange",
+          max_pos=4096, outside=((4099, 4096),), cell=45),
 ]
 
 
