@@ -4,7 +4,9 @@
  * back and checked against the CPU oracle (liboracle, test infrastructure).
  *
  * Cases: the fused QK-RMSNorm + RoPE prologue ("thox-edge-ops v2", section
- * 5.1; tokens inside and outside the cos/sin cache), the residual-add
+ * 5.1; tokens inside and outside the cos/sin cache), the same on a fused
+ * QKV buffer with the key / value cache write (FlashRT's decoder kernel
+ * list, qkv_split_rope_kvcache; a padding slot), the residual-add
  * RMSNorm to static FP8 (FlashRT "optimization details", fused kernel
  * table) with its in-place residual update, the gated SiLU activation, and
  * one rejected call.  The comparison rules are the parity suite's: <= 1 bf16
@@ -174,6 +176,94 @@ static void case_prologue(void) {
     free(nq); free(nk);
 }
 
+/* ---- the fused QKV buffer with the key / value cache write -------------- */
+static void case_qkv_cache(void) {
+    enum { T = 5, Q = 4, K = 2, D = 128, ROT = 64, MAXPOS = 64, NSLOTS = 8 };
+    const float eps = 1e-6f;
+    printf("case qkv -> q_out + K/V cache: T=%d Q=%d K=%d D=%d, slots of %d\n", T, Q, K, D,
+           NSLOTS);
+    fflush(stdout);
+    const size_t row = (size_t)(Q + 2 * K) * D;               /* elements per token */
+    uint16_t* qkv = bf16_array((size_t)T * row, 0.0, 2.0);
+    uint16_t* wq = bf16_array(D, 0.0, 0.05);
+    uint16_t* wk = bf16_array(D, 0.0, 0.05);
+    float* cs = malloc(sizeof(float) * MAXPOS * ROT);
+    for (int p = 0; p < MAXPOS; ++p)
+        for (int i = 0; i < ROT / 2; ++i) {
+            double a = p * pow(1.0e6, -2.0 * i / ROT);
+            cs[p * ROT + i] = (float)cos(a);
+            cs[p * ROT + ROT / 2 + i] = (float)sin(a);
+        }
+    const int64_t pos[T] = {3, 9, 70, 12, 40};          /* 70: outside the cache */
+    const int64_t slot[T] = {6, 0, 3, -1, 5};           /* -1: padding, no cache row */
+    const size_t cache_elems = (size_t)NSLOTS * K * D;
+    uint16_t* kc0 = malloc(sizeof(uint16_t) * cache_elems);
+    for (size_t e = 0; e < cache_elems; ++e) kc0[e] = 0x7FC0;   /* a NaN fill: rows not written */
+
+    void *dqkv = to_device(qkv, sizeof(uint16_t) * T * row);
+    void *dqo = to_device(NULL, sizeof(uint16_t) * T * Q * D);
+    void *dkc = to_device(kc0, sizeof(uint16_t) * cache_elems);
+    void *dvc = to_device(kc0, sizeof(uint16_t) * cache_elems);
+    void *dwq = to_device(wq, sizeof(uint16_t) * D), *dwk = to_device(wk, sizeof(uint16_t) * D);
+    void *dcs = to_device(cs, sizeof(float) * MAXPOS * ROT), *dpos = to_device(pos, sizeof pos);
+    void *dslot = to_device(slot, sizeof slot);
+    mbt_status st = mbt_qkv_norm_rope_cache(dqkv, dqo, dkc, dvc, dslot, NSLOTS, dwq, dwk, dcs,
+                                            MAXPOS, dpos, Q, K, T, D, ROT, eps, 1,
+                                            MBT_ROPE_ROTATE_HALF, MBT_BF16, 0, NULL);
+    check(st == MBT_OK, "mbt_qkv_norm_rope_cache returned an error");
+    uint16_t* gq = malloc(sizeof(uint16_t) * T * Q * D);
+    uint16_t* gkc = malloc(sizeof(uint16_t) * cache_elems);
+    uint16_t* gvc = malloc(sizeof(uint16_t) * cache_elems);
+    from_device(gq, dqo, sizeof(uint16_t) * T * Q * D);
+    from_device(gkc, dkc, sizeof(uint16_t) * cache_elems);
+    from_device(gvc, dvc, sizeof(uint16_t) * cache_elems);
+
+    /* the oracle's prologue on the q and k heads gathered out of qkv */
+    uint16_t* q = malloc(sizeof(uint16_t) * T * Q * D);
+    uint16_t* k = malloc(sizeof(uint16_t) * T * K * D);
+    for (int t = 0; t < T; ++t) {
+        memcpy(q + (size_t)t * Q * D, qkv + t * row, sizeof(uint16_t) * Q * D);
+        memcpy(k + (size_t)t * K * D, qkv + t * row + (size_t)Q * D, sizeof(uint16_t) * K * D);
+    }
+    uint16_t* oq = malloc(sizeof(uint16_t) * T * Q * D);
+    uint16_t* ok = malloc(sizeof(uint16_t) * T * K * D);
+    check(mbt_ref_qknorm_rope(q, k, oq, ok, wq, wk, cs, MAXPOS, pos, Q, K, T, D, ROT, eps, 1,
+                              MBT_REF_ROTATE_HALF, MBT_REF_BF16) == 0, "oracle prologue");
+    long far = 0, differ = 0, vbad = 0, untouched_bad = 0;
+    for (size_t e = 0; e < (size_t)T * Q * D; ++e) {
+        const int64_t d = ulp_dist(gq[e], oq[e]);
+        differ += d != 0;
+        far += d > 1;
+    }
+    int written[NSLOTS] = {0};
+    for (int t = 0; t < T; ++t) {
+        if (slot[t] < 0 || slot[t] >= NSLOTS) continue;
+        written[slot[t]] = 1;
+        for (size_t e = 0; e < (size_t)K * D; ++e) {
+            const size_t c = (size_t)slot[t] * K * D + e;
+            const int64_t d = ulp_dist(gkc[c], ok[(size_t)t * K * D + e]);
+            differ += d != 0;
+            far += d > 1;
+            vbad += gvc[c] != qkv[t * row + (size_t)(Q + K) * D + e];
+        }
+    }
+    for (int sl = 0; sl < NSLOTS; ++sl)
+        if (!written[sl])
+            for (size_t e = 0; e < (size_t)K * D; ++e)
+                untouched_bad += gkc[(size_t)sl * K * D + e] != 0x7FC0 ||
+                                 gvc[(size_t)sl * K * D + e] != 0x7FC0;
+    printf("  q and cached keys: %ld differ, %ld by more than one ulp; value rows not copied "
+           "bit for bit: %ld; unwritten cache elements changed: %ld\n", differ, far, vbad,
+           untouched_bad);
+    check(far == 0, "qkv cache: beyond one ulp");
+    check(vbad == 0, "value rows not copied bit for bit");
+    check(untouched_bad == 0, "a cache row without a token was written");
+    hipFree(dqkv); hipFree(dqo); hipFree(dkc); hipFree(dvc); hipFree(dwq); hipFree(dwk);
+    hipFree(dcs); hipFree(dpos); hipFree(dslot);
+    free(qkv); free(wq); free(wk); free(cs); free(kc0); free(gq); free(gkc); free(gvc);
+    free(q); free(k); free(oq); free(ok);
+}
+
 /* ---- residual-add RMSNorm to FP8 ---------------------------------------- */
 static void case_norm_fp8(void) {
     enum { T = 7, H = 1024 };
@@ -262,6 +352,7 @@ int main(void) {
     }
     case_rejected();
     case_prologue();
+    case_qkv_cache();
     case_norm_fp8();
     case_gated_act();
     printf(failures ? "c abi: %d failure(s)\n" : "c abi: every check passed\n", failures);
