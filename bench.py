@@ -107,7 +107,7 @@ def parse_args():
                          "(headline_sustained), after every other GPU figure")
     ap.add_argument("--only", default=None,
                     choices=["prologue_prefill", "prefill_cells", "norm_fp8", "prologue",
-                             "act_fp8"],
+                             "act_fp8", "act_prefill", "norm_prefill"],
                     help="profiling aid: launch one thing repeatedly and exit: "
                          "prologue_prefill (the headline launch), prefill_cells (every "
                          "prefill cell in turn), or a kernel of the decode-layer step "
@@ -956,6 +956,9 @@ def write_profiles(d):
     for k, src in (("norm_fp8", "rmsnorm"), ("prologue", "qknorm_rope"), ("act_fp8", "gated_act")):
         if k in step and os.path.exists(os.path.join(d, f"pmc_{k}_FETCH_SIZE")):
             launches[f"{k}_T128"] = (k, src, step[k]["bytes"])
+    for k, src in (("act_prefill", "gated_act"), ("norm_prefill", "rmsnorm")):
+        if os.path.exists(os.path.join(d, f"pmc_{k}_FETCH_SIZE")):
+            launches[k] = (k, src, prefill_traffic_cell(W, k).bytes_algorithmic())
     tl = []
     for key, (only, src, algo) in launches.items():
         f_, n = pmc(only, "FETCH_SIZE")
@@ -982,6 +985,8 @@ def write_profiles(d):
           "|---|---|---|---|---|---|", *tl, "",
           "`prologue_prefill` is the headline launch: the prologue at (Q, K) = (24, 4), head_dim 256,",
           "rot_dim 64, T = 2048, bf16.  `*_T128` are the kernels of the decode-layer step at T = 128.",
+          "`act_prefill` is configuration 5's SiLU-gate -> FP8 at d = 10240, T = 512; `norm_prefill`",
+          "configuration 4's bf16 residual norm in place at H = 2560, T = 512.",
           "", "Commands (from /tmp with TMPDIR=/tmp; `$REPO` is the repository root):", "", "```",
           *[cmd_p.format(ctr=c, only=o) for o in [v[0] for v in launches.values()]
             for c in ("FETCH_SIZE", "WRITE_SIZE")],
@@ -1070,6 +1075,17 @@ def cpu_baseline(W, cell, threads=1, tokens_per_call=32):
 
 # ---------------------------------------------------------------------------
 
+def prefill_traffic_cell(W, what):
+    """The bandwidth-bound cells whose HBM traffic the counter runs record
+    beside the headline's: configuration 5's SiLU-gate -> FP8 at T = 512 and
+    configuration 4's bf16 residual norm at H = 2560, T = 512."""
+    if what == "act_prefill":
+        return [c for c in W.config5_cells() if isinstance(c, W.ActCell) and c.T == 512
+                and c.act == W.SILU and c.fp8][0]
+    return [c for c in W.config4_cells() if c.dtype == W.BF16 and c.H == 2560 and c.T == 512
+            and c.weight_offset == 0][0]
+
+
 def only_mode(torch, mbt, W, what, steps):
     """Profiling aids: launch one thing repeatedly, print a JSON line, exit."""
     if what == "prologue_prefill":
@@ -1085,6 +1101,32 @@ def only_mode(torch, mbt, W, what, steps):
             prologue_cold_us(torch, mbt, W, c, launches=500)
             names.append(c.name)
         return {"only": what, "cells": names}
+    if what in ("act_prefill", "norm_prefill"):
+        # configuration 5's SiLU-gate -> FP8 at T = 512, or configuration 4's
+        # bf16 residual norm at H = 2560, T = 512, over a cold buffer ring
+        c = prefill_traffic_cell(W, what)
+        dev = "cuda:0"
+        R = ring_slots(c.bytes_algorithmic())
+        if what == "act_prefill":
+            gu0 = W.to_torch(c.inputs()["gate_up"], c.dtype, dev)
+            ring = [(gu0.clone(), torch.empty((c.T, c.d), dtype=torch.uint8, device=dev))
+                    for _ in range(R)]
+
+            def call(j):
+                mbt.gated_act_fp8(ring[j][0], 1.0 / 16, c.act, out=ring[j][1])
+        else:
+            i = c.inputs()
+            w = W.to_torch(i["w"], c.dtype, dev)
+            x0, r0 = W.to_torch(i["x"], c.dtype, dev), W.to_torch(i["residual"], c.dtype, dev)
+            ring = [(x0.clone(), r0.clone()) for _ in range(R)]
+
+            def call(j):
+                mbt.fused_add_rmsnorm(ring[j][0], ring[j][1], w, c.eps, c.weight_offset)
+        n = max(steps, R)
+        for j in range(n):
+            call(j % R)
+        torch.cuda.synchronize()
+        return {"only": what, "cell": c.name, "launches": n}
     st = DecodeStep(torch, mbt, W, 128)
     fn = st.kernels()[what][0]
     n = max(steps, st.R)
@@ -1278,6 +1320,8 @@ def main():
                 cu, ck = best_copy(x.bytes_algorithmic())
                 row.update({"copy_us": round(cu, 3), "copy_form": ck,
                             "of_copy": round(cu / us, 4)})
+            if x.name == prefill_traffic_cell(W, "norm_prefill").name:
+                row["traffic"] = traffic_for("norm_prefill", "rmsnorm")
             nsweep.append(row)
         out["norm_sweep_config4"] = nsweep
         phase("activation sweep (configuration 5)")
@@ -1287,10 +1331,13 @@ def main():
                 continue
             us, mode = act_cold_us(torch, mbt, W, x)
             gbps = x.bytes_algorithmic() / us / 1e3
-            asweep.append({"act": "silu" if x.act == W.SILU else "gelu_tanh", "T": x.T,
-                           "out": "fp8" if x.fp8 else "bf16", "d": x.d, "us": round(us, 3),
-                           "ring": mode, "rows_per_s": round(x.T / us * 1e6, 1),
-                           "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)})
+            arow = {"act": "silu" if x.act == W.SILU else "gelu_tanh", "T": x.T,
+                    "out": "fp8" if x.fp8 else "bf16", "d": x.d, "us": round(us, 3),
+                    "ring": mode, "rows_per_s": round(x.T / us * 1e6, 1),
+                    "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+            if x.name == prefill_traffic_cell(W, "act_prefill").name:
+                arow["traffic"] = traffic_for("act_prefill", "gated_act")
+            asweep.append(arow)
         out["act_sweep_config5"] = asweep
         phase("routes")
         out["routes"] = {"warm": [route_us(torch, mbt, W, x, cold=False)

@@ -66,6 +66,8 @@ def test_bench_json_contract():
     (["--only", "norm_fp8", "--steps", "30"], "launches"),
     (["--only", "prologue", "--steps", "30"], "launches"),
     (["--only", "act_fp8", "--steps", "30"], "launches"),
+    (["--only", "act_prefill", "--steps", "30"], "launches"),
+    (["--only", "norm_prefill", "--steps", "30"], "launches"),
     (["--copy-probe", "1048576"], "copy_probe_bytes_moved"),
 ])
 def test_bench_profiling_aids(args, key):
