@@ -54,8 +54,9 @@ def test_bench_json_contract():
     assert "cpu_baseline" not in d                      # --no-cpu
     t1 = d["us_per_call_T1"]
     assert 0 < t1["median"] < 50
-    # the smallest launch is a floor for every call, the T = 1 copy included
-    assert 0 < t1["launch_floor_us"] <= t1["copy_floor_us"] * 1.05
+    # the smallest launch is about the floor of every call, the T = 1 copy
+    # included (the two medians can trade places within noise)
+    assert 0 < t1["launch_floor_us"] <= t1["copy_floor_us"] * 1.15
     assert len(d["prefill"]) == 24
     for c in d["prefill"]:
         assert c["T"] >= 256 and 0 < c["frac_peak"] < 1 and c["copy_us"] > 0
