@@ -109,19 +109,38 @@ def _dtype(t):
         raise TypeError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16")
 
 
-def _dev(*tensors):
+def _on_current_gpu(tensors, current_device=None):
+    """Every tensor on the current GPU.  The kernels run on the device of
+    the stream they are given (the current device's, by default) and
+    address every pointer from there, so a tensor on another GPU would be
+    read and written from the wrong device."""
+    cur = None
     for t in tensors:
         if t is None:
             continue
         if not t.is_cuda:
             raise ValueError("libmbt operates on GPU tensors only")
-        if not t.is_contiguous():
+        if cur is None:
+            cur = (current_device or torch.cuda.current_device)()
+        if t.device.index != cur:
+            raise ValueError(f"a tensor is on {t.device} but the current device is cuda:{cur}; "
+                             f"call inside torch.cuda.device({t.device.index})")
+
+
+def _dev(*tensors):
+    _on_current_gpu(tensors)
+    for t in tensors:
+        if t is not None and not t.is_contiguous():
             raise ValueError("libmbt needs contiguous tensors")
 
 
-def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+def _stream(stream, current_device=None):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    cur = (current_device or torch.cuda.current_device)()
+    if stream.device.index != cur:
+        raise ValueError(f"stream is on {stream.device} but the current device is cuda:{cur}")
+    return stream.cuda_stream
 
 
 def _same_dtype(ref, *tensors):
@@ -261,9 +280,7 @@ def qknorm_rope_ex(q_in, k_in, w_q, w_k, cos_sin, pos, rot_dim, eps=1e-6, weight
     """mbt_qknorm_rope on strided [T, heads, D] views (e.g. q and k slices of
     a fused QKV buffer), with the single-rounding variant on request.  Pass
     q_out=q_in / k_out=k_in for the in-place form."""
-    for t in (q_in, k_in, w_q, w_k, cos_sin, pos, q_out, k_out):
-        if t is not None and not t.is_cuda:
-            raise ValueError("libmbt operates on GPU tensors only")
+    _on_current_gpu((q_in, k_in, w_q, w_k, cos_sin, pos, q_out, k_out))
     for t in (w_q, w_k, cos_sin, pos):
         if t is not None and not t.is_contiguous():
             raise ValueError("weights, cos_sin and pos must be contiguous")

@@ -96,3 +96,28 @@ def test_stream_copy_refuses_host_tensors():
     a = torch.zeros(64, dtype=torch.uint8)
     with pytest.raises(ValueError, match="GPU tensors only"):
         mbt.stream_copy(a[:32], a[32:], 1)
+
+
+class _OnDevice:
+    """Stands in for a tensor or stream on a given device (no GPU here)."""
+    def __init__(self, index):
+        self.is_cuda = True
+        self.device = torch.device("cuda", index)
+        self.cuda_stream = 1234
+
+    def is_contiguous(self):
+        return True
+
+
+def test_tensors_and_stream_on_the_current_gpu():
+    cur = lambda: 0                                     # noqa: E731
+    mbt._on_current_gpu([_OnDevice(0), None, _OnDevice(0)], cur)
+    with pytest.raises(ValueError):
+        mbt._on_current_gpu([_OnDevice(0), _OnDevice(1)], cur)   # two GPUs
+    with pytest.raises(ValueError):
+        mbt._on_current_gpu([_OnDevice(1)], cur)                 # not the current one
+    with pytest.raises(ValueError):
+        mbt._on_current_gpu([torch.zeros(2)], cur)               # host memory
+    assert mbt._stream(_OnDevice(0), cur) == 1234
+    with pytest.raises(ValueError):
+        mbt._stream(_OnDevice(1), cur)
