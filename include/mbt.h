@@ -15,6 +15,8 @@
  *    library allocates nothing, performs no I/O and never synchronises the
  *    host (P1 section 5.5): every call enqueues its kernels on `stream` (a
  *    hipStream_t passed as void*, NULL = the null stream) and returns.
+ *    Calls run on the current HIP device: `stream` must belong to it, and
+ *    every pointer must be memory that device can address (its own HBM).
  *  - Tensors are dense, row-major, one element type per call:
  *    MBT_F32 (float), MBT_F16 (IEEE binary16), MBT_BF16 (bfloat16) -- the
  *    three dtypes of P1 section 3.  FP8 outputs are OCP e4m3fn codes (uint8).
