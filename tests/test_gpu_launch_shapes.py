@@ -55,3 +55,23 @@ def _cells():
 @pytest.mark.parametrize("cell", _cells(), ids=lambda c: c.name)
 def test_prologue_launch_shape(mbt, orc, cell):
     check_prologue_cell(mbt, orc, cell, in_place=cell.in_place)
+
+
+# The general kernel (token strides, slot table and value rows, the
+# single-rounding flag) has the same launch shapes; its cells in bf16 and
+# fp32 go through the strided-view and KV-cache checks of
+# test_gpu_prologue_ex (against the oracle, and bit for bit against the
+# dense op), the single-rounding flag on every other cell.
+import test_gpu_prologue_ex as ex  # noqa: E402
+
+_GEN = [c for c in _cells() if c.dtype in (W.BF16, W.F32)]
+
+
+@pytest.mark.parametrize("cell", _GEN, ids=lambda c: c.name)
+def test_strided_launch_shape(mbt, orc, cell):
+    ex.test_strided_views(mbt, orc, cell, round_once=cell.cell % 2 == 0, pad=0)
+
+
+@pytest.mark.parametrize("cell", _GEN, ids=lambda c: c.name)
+def test_cache_launch_shape(mbt, orc, cell):
+    ex.test_qkv_cache(mbt, orc, cell, round_once=cell.cell % 2 == 1)
