@@ -365,6 +365,11 @@ __global__ __launch_bounds__(256) void qknorm_rope_vec(QkParams p, QkGen<GEN> g)
         wrow = wsh[wib];
     }
     if constexpr (THR) {                                    // both rows, block-wide
+        // Every lane loads one element of w_q, waits, then one of w_k: two
+        // dependent round trips before the barrier, as measured best on
+        // MI355X at (Q, K) = (24, 4), T = 2048.  Both loads behind one wait,
+        // 16-byte loads on the first 2 L lanes, or a third dependent load
+        // were 9-12 % / 11-12 % / 1-2 % slower (the same bits).
         for (int i = threadIdx.x; i < p.D; i += 256) {
             wsh[0][i] = (p.Q > 0) ? ld_elt<DT>(p.w_q, i) + p.delta : 0.0f;
             wsh[1][i] = (p.K > 0) ? ld_elt<DT>(p.w_k, i) + p.delta : 0.0f;
