@@ -8,8 +8,9 @@
  * QKV buffer with the key / value cache write (FlashRT's decoder kernel
  * list, qkv_split_rope_kvcache; a padding slot), the residual-add
  * RMSNorm to static FP8 (FlashRT "optimization details", fused kernel
- * table) with its in-place residual update, the gated SiLU activation, and
- * one rejected call.  The comparison rules are the parity suite's: <= 1 bf16
+ * table) with its in-place residual update, the gated SiLU activation, the
+ * standalone rotation (interleaved pairs, in place, bit for bit), and one
+ * rejected call.  The comparison rules are the parity suite's: <= 1 bf16
  * ulp for normalised, rotated and activated values (a rotated value may
  * also move by the rotation of a one-ulp difference in its inputs), FP8
  * codes within one step, residual sums bit-identical.
@@ -333,6 +334,45 @@ static void case_gated_act(void) {
     free(gu); free(g); free(o);
 }
 
+/* ---- the standalone rotation (the split route), interleaved pairs ------- */
+static void case_rope(void) {
+    enum { T = 5, Q = 3, K = 1, D = 64, ROT = 32, MAXPOS = 40 };
+    printf("case rope: T=%d Q=%d K=%d D=%d rot=%d bf16, interleaved, in place\n", T, Q, K, D,
+           ROT);
+    fflush(stdout);
+    uint16_t* q = bf16_array((size_t)T * Q * D, 0.0, 1.0);
+    uint16_t* k = bf16_array((size_t)T * K * D, 0.0, 1.0);
+    float* cs = malloc(sizeof(float) * MAXPOS * ROT);
+    for (int p = 0; p < MAXPOS; ++p)
+        for (int i = 0; i < ROT / 2; ++i) {
+            double a = p * pow(1.0e4, -2.0 * i / ROT);
+            cs[p * ROT + i] = (float)cos(a);
+            cs[p * ROT + ROT / 2 + i] = (float)sin(a);
+        }
+    const int64_t pos[T] = {3, 39, 40, -2, 0};      /* 40 and -2: untouched */
+    void *dq = to_device(q, sizeof(uint16_t) * T * Q * D);
+    void *dk = to_device(k, sizeof(uint16_t) * T * K * D);
+    void *dcs = to_device(cs, sizeof(float) * MAXPOS * ROT), *dpos = to_device(pos, sizeof pos);
+    mbt_status st = mbt_rope(dq, dk, dcs, MAXPOS, dpos, Q, K, T, D, ROT, MBT_ROPE_INTERLEAVED,
+                             MBT_BF16, NULL);
+    check(st == MBT_OK, "mbt_rope returned an error");
+    uint16_t* gq = malloc(sizeof(uint16_t) * T * Q * D);
+    uint16_t* gk = malloc(sizeof(uint16_t) * T * K * D);
+    from_device(gq, dq, sizeof(uint16_t) * T * Q * D);
+    from_device(gk, dk, sizeof(uint16_t) * T * K * D);
+    check(mbt_ref_rope(q, cs, MAXPOS, pos, T, Q, D, ROT, MBT_REF_INTERLEAVED, MBT_REF_BF16) == 0,
+          "oracle rope q");
+    check(mbt_ref_rope(k, cs, MAXPOS, pos, T, K, D, ROT, MBT_REF_INTERLEAVED, MBT_REF_BF16) == 0,
+          "oracle rope k");
+    long differ = 0;
+    for (size_t e = 0; e < (size_t)T * Q * D; ++e) differ += gq[e] != q[e];
+    for (size_t e = 0; e < (size_t)T * K * D; ++e) differ += gk[e] != k[e];
+    printf("  %ld elements differ from the oracle (the rotation is bit-exact)\n", differ);
+    check(differ == 0, "standalone rotation not bit-identical to the oracle");
+    hipFree(dq); hipFree(dk); hipFree(dcs); hipFree(dpos);
+    free(q); free(k); free(cs); free(gq); free(gk);
+}
+
 /* ---- a rejected call: nothing launched, a status and a detail string --- */
 static void case_rejected(void) {
     printf("case rejected call: an unknown dtype\n");
@@ -355,6 +395,7 @@ int main(void) {
     case_qkv_cache();
     case_norm_fp8();
     case_gated_act();
+    case_rope();
     printf(failures ? "c abi: %d failure(s)\n" : "c abi: every check passed\n", failures);
     return failures ? 1 : 0;
 }
