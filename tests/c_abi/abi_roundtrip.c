@@ -9,8 +9,8 @@
  * list, qkv_split_rope_kvcache; a padding slot), the residual-add
  * RMSNorm to static FP8 (FlashRT "optimization details", fused kernel
  * table) with its in-place residual update, the gated SiLU activation, the
- * standalone rotation (interleaved pairs, in place, bit for bit), and one
- * rejected call.  The comparison rules are the parity suite's: <= 1 bf16
+ * standalone rotation (interleaved pairs, in place, bit for bit), the
+ * adaptive norm to FP8 with its calibration pass, and one rejected call.  The comparison rules are the parity suite's: <= 1 bf16
  * ulp for normalised, rotated and activated values (a rotated value may
  * also move by the rotation of a one-ulp difference in its inputs), FP8
  * codes within one step, residual sums bit-identical.
@@ -334,6 +334,59 @@ static void case_gated_act(void) {
     free(gu); free(g); free(o);
 }
 
+/* ---- the adaptive norm to FP8, with its calibration pass ---------------- */
+static void case_adarms_fp8(void) {
+    enum { T = 4, H = 512 };
+    const float eps = 1e-6f;
+    printf("case adaptive RMSNorm -> FP8: T=%d H=%d bf16, gated residual, calibrated\n", T, H);
+    fflush(stdout);
+    uint16_t* x = bf16_array((size_t)T * H, 0.0, 1.0);
+    uint16_t* r = bf16_array((size_t)T * H, 0.0, 1.0);
+    uint16_t* gate = bf16_array(H, 1.0, 0.1);
+    uint16_t* scale = bf16_array(H, 0.0, 0.1);
+    uint16_t* shift = bf16_array(H, 0.0, 0.1);
+    void *dx = to_device(x, sizeof(uint16_t) * T * H), *dr = to_device(r, sizeof(uint16_t) * T * H);
+    void *dg = to_device(gate, sizeof(uint16_t) * H), *dsc = to_device(scale, sizeof(uint16_t) * H);
+    void *dsh = to_device(shift, sizeof(uint16_t) * H), *dy = to_device(NULL, (size_t)T * H);
+    const float zero = 0.0f;
+    void* damax = to_device(&zero, sizeof zero);      /* the caller zeroes the fold */
+    /* calibration on the GPU and in the oracle: the same maximum */
+    mbt_status st = mbt_adarms_amax(dx, dr, dg, dsc, dsh, (float*)damax, T, H, eps, MBT_BF16,
+                                    NULL);
+    check(st == MBT_OK, "mbt_adarms_amax returned an error");
+    float gamax = 0.0f;
+    from_device(&gamax, damax, sizeof gamax);
+    const float amax = mbt_ref_adarms_amax(x, r, gate, scale, shift, T, H, eps, MBT_REF_BF16);
+    check(fabs((double)gamax - (double)amax) <= 1e-5 * (double)amax, "calibration amax");
+    const float inv_scale = (float)(448.0 / (double)amax);
+    st = mbt_adarms_fp8(dx, dr, dg, dsc, dsh, (uint8_t*)dy, inv_scale, T, H, eps, MBT_BF16, NULL);
+    check(st == MBT_OK, "mbt_adarms_fp8 returned an error");
+    uint8_t* gy = malloc((size_t)T * H);
+    uint16_t* gr = malloc(sizeof(uint16_t) * T * H);
+    from_device(gy, dy, (size_t)T * H);
+    from_device(gr, dr, sizeof(uint16_t) * T * H);
+    uint8_t* oy = malloc((size_t)T * H);
+    check(mbt_ref_adarms_fp8(x, r, gate, scale, shift, oy, inv_scale, T, H, eps,
+                             MBT_REF_BF16) == 0, "oracle adaptive norm fp8");
+    long differ = 0, far = 0, res_bad = 0;
+    for (size_t e = 0; e < (size_t)T * H; ++e) {
+        const int a = (gy[e] & 0x80) ? -(gy[e] & 0x7F) : (gy[e] & 0x7F);
+        const int b = (oy[e] & 0x80) ? -(oy[e] & 0x7F) : (oy[e] & 0x7F);
+        const int d = abs(a - b);
+        if (d) ++differ;
+        if (d > 1) ++far;
+        if (gr[e] != r[e]) ++res_bad;
+    }
+    printf("  amax %.9g vs %.9g; FP8 codes: %ld of %d differ, %ld by more than one step; "
+           "residual: %ld not bit-identical\n", gamax, amax, differ, T * H, far, res_bad);
+    check(far == 0, "adaptive FP8 codes more than one step apart");
+    check(differ <= 4 || differ * 500 <= (long)T * H, "adaptive FP8: too many differences");
+    check(res_bad == 0, "gated residual sum not bit-identical");
+    hipFree(dx); hipFree(dr); hipFree(dg); hipFree(dsc); hipFree(dsh); hipFree(dy);
+    hipFree(damax);
+    free(x); free(r); free(gate); free(scale); free(shift); free(gy); free(gr); free(oy);
+}
+
 /* ---- the standalone rotation (the split route), interleaved pairs ------- */
 static void case_rope(void) {
     enum { T = 5, Q = 3, K = 1, D = 64, ROT = 32, MAXPOS = 40 };
@@ -396,6 +449,7 @@ int main(void) {
     case_norm_fp8();
     case_gated_act();
     case_rope();
+    case_adarms_fp8();
     printf(failures ? "c abi: %d failure(s)\n" : "c abi: every check passed\n", failures);
     return failures ? 1 : 0;
 }
